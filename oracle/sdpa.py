@@ -1,0 +1,329 @@
+"""Plain CPU float64 reference for attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check of the package entry
+file and the CPU-baseline leg of the benchmark use it.  It shares no code with
+the HIP library (no helpers, no tables, no pre/post-processing) and it never
+reads anything the HIP library produced.
+
+Sources (cited by page title and section; no other authority is used):
+
+* "fuel-reference-backend -- attention kernel contracts" (the kernel-contract
+  page), sections ``attention_naive``, ``attention_flash`` and
+  ``attention_paged_naive``: shapes ``[B, H, S, D]``, GQA broadcast, the order
+  of the score transforms (scale, softcap, ALiBi), the mask rules, stable
+  softmax, the zero output of a fully masked row, and paged address
+  translation with its implicit causal position.
+* "gfx942 unified attention, from the math up" (the derivation page): section 1
+  (definition), section 2 (shift invariance of softmax), section 3 (the online
+  recurrence), section 4 (bottom-right causal alignment when Sq != Sk),
+  section 5 (paged pool layout and GQA as repeat-interleave) and section 8
+  (split-KV decode combining partial results).
+
+Readings taken where the pages are silent or disagree (each is repeated in the
+design notes of the repository):
+
+* Causal and window masks are bottom-right aligned: query row ``i`` sits at
+  absolute position ``i' = i + Sk - Sq`` (derivation page section 4; the
+  kernel-contract page's paged section uses the same shift).  For Sq == Sk this
+  is exactly the kernel-contract page's literal rule.
+* Window bounds are inclusive: key ``j`` is admissible iff
+  ``i' - left <= j <= i' + right``; ``None`` means unbounded on that side.
+* ALiBi adds ``slope[h] * (j - i')``; slopes are float32 ``[Hq]``.
+* ``softcap=None`` (or 0) disables the softcap; a negative value is an error.
+* KV head of query head ``h`` is ``h // (Hq // Hkv)`` (contiguous groups).
+
+Every function computes in float64; inputs of any float dtype are upcast.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "query_positions",
+    "admissible",
+    "transform_scores",
+    "sdpa_naive_f64",
+    "sdpa_online_f64",
+    "attention_partial_f64",
+    "lse_merge_f64",
+    "paged_gather",
+    "paged_decode_f64",
+    "admissible_pair_count",
+]
+
+
+def _check_common(q, k, v, alibi, softcap):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be rank 4 [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    if Bk != B or Dk != D:
+        raise ValueError("batch and head dim of k must match q")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if alibi is not None and np.shape(alibi) != (Hq,):
+        raise ValueError("ALiBi slopes must be [Hq]")
+    if softcap is not None and softcap < 0:
+        raise ValueError("softcap must be >= 0 (0 or None disables it)")
+    return B, Hq, Hkv, Sq, Sk, D
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """KV head serving query head ``h``: each KV head is shared by a contiguous
+    group of ``Hq // Hkv`` query heads (kernel-contract page, intro; derivation
+    page section 5, where K/V are repeat-interleaved to the query heads)."""
+    return h // (Hq // Hkv)
+
+
+def query_positions(Sq: int, Sk: int) -> np.ndarray:
+    """Absolute position of each query row: ``i + Sk - Sq`` (bottom-right
+    alignment, derivation page section 4)."""
+    return np.arange(Sq, dtype=np.int64) + (Sk - Sq)
+
+
+def admissible(Sq, Sk, causal, window_left=None, window_right=None, rows=None):
+    """Boolean ``[rows, Sk]``: may query row i attend to key j?
+
+    Kernel-contract page, ``attention_naive``: causal masks keys in the future
+    of the query, a left window masks keys more than ``left`` before it, a
+    right window masks keys more than ``right`` after it.  Positions are the
+    bottom-right aligned ``i'`` of :func:`query_positions`.
+    """
+    ip = query_positions(Sq, Sk)
+    if rows is not None:
+        ip = ip[rows]
+    ip = ip[:, None]
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    ok = np.ones((ip.shape[0], Sk), dtype=bool)
+    if causal:
+        ok &= j <= ip
+    if window_left is not None:
+        ok &= j >= ip - window_left
+    if window_right is not None:
+        ok &= j <= ip + window_right
+    return ok
+
+
+def transform_scores(s, softcap=None, slope=None, rel=None):
+    """Score transforms in the order the kernel-contract page fixes for
+    ``attention_naive``: the already scaled score first goes through the
+    softcap ``c * tanh(s / c)``, then ALiBi adds ``slope * (j - i')``."""
+    if softcap:
+        s = softcap * np.tanh(s / softcap)
+    if slope is not None:
+        s = s + slope * rel
+    return s
+
+
+def _scores(qrows, kmat, scale, softcap, slope, rel, ok):
+    s = (qrows @ kmat.T) * scale
+    s = transform_scores(s, softcap, slope, rel)
+    return np.where(ok, s, -np.inf)
+
+
+def sdpa_naive_f64(q, k, v, *, scale, causal=False, window_left=None,
+                   window_right=None, softcap=None, alibi=None, row_block=512):
+    """Materialised-score attention, the definition itself.
+
+    Derivation page section 1 (output row = softmax-weighted convex combination
+    of V rows), section 2 (subtract the row max before exponentiating) and the
+    kernel-contract page's ``attention_naive`` (mask, softcap, ALiBi, GQA, and a
+    row with no admissible key gives an all-zero output row).  Score rows are
+    computed ``row_block`` queries at a time only to bound memory.
+
+    Returns float64 ``[B, Hq, Sq, D]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Sq, Sk, D = _check_common(q, k, v, alibi, softcap)
+    slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
+    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    if Sq == 0 or Sk == 0:
+        return out
+    ip_all = query_positions(Sq, Sk)
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    ones = np.ones((Sk, 1), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            # V with a trailing column of ones: the same products give the
+            # unnormalised output and its denominator, so the one division at
+            # the end sees sums taken in the same order.
+            v1 = np.concatenate([v[b, g], ones], axis=1)
+            for r0 in range(0, Sq, row_block):
+                rows = slice(r0, min(Sq, r0 + row_block))
+                ok = admissible(Sq, Sk, causal, window_left, window_right, rows)
+                rel = j - ip_all[rows][:, None]
+                slope = None if slopes is None else slopes[h]
+                s = _scores(q[b, h, rows], k[b, g], scale, softcap, slope, rel, ok)
+                has_key = ok.any(axis=1)
+                m = np.where(has_key, s.max(axis=1), 0.0)[:, None]
+                p = np.exp(s - m)                      # exp(-inf) == 0
+                acc = p @ v1
+                den = acc[:, D:D + 1]
+                o = np.divide(acc[:, :D], den, out=np.zeros_like(acc[:, :D]),
+                              where=has_key[:, None])
+                out[b, h, rows] = o
+    return out
+
+
+def sdpa_online_f64(q, k, v, *, scale, tile=16, causal=False, window_left=None,
+                    window_right=None, softcap=None, alibi=None):
+    """Streaming (online) softmax over key tiles of width ``tile``.
+
+    Derivation page section 3: running max ``m``, denominator ``l`` and
+    unnormalised output ``o`` start at ``-inf, 0, 0``; each tile raises the max,
+    rescales the old state by ``alpha = exp(m_old - m_new)`` and adds the tile's
+    weights ``exp(s - m_new)``; the result is ``o / l``.  The kernel-contract
+    page's ``attention_flash`` states the same recurrence and that a row whose
+    ``l`` stays 0 outputs zero.  While no admissible key has been seen the max
+    is still ``-inf``; then ``alpha`` is taken as 1 and the weights as 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Sq, Sk, D = _check_common(q, k, v, alibi, softcap)
+    if tile < 1:
+        raise ValueError("tile must be >= 1")
+    slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
+    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    if Sq == 0 or Sk == 0:
+        return out
+    ip = query_positions(Sq, Sk)[:, None]
+    ok_all = admissible(Sq, Sk, causal, window_left, window_right)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            m = np.full((Sq,), -np.inf)
+            l = np.zeros((Sq,))
+            o = np.zeros((Sq, D))
+            for t0 in range(0, Sk, tile):
+                t1 = min(Sk, t0 + tile)
+                jt = np.arange(t0, t1, dtype=np.int64)[None, :]
+                slope = None if slopes is None else slopes[h]
+                s = _scores(q[b, h], k[b, g, t0:t1], scale, softcap, slope,
+                            jt - ip, ok_all[:, t0:t1])
+                m_new = np.maximum(m, s.max(axis=1))
+                live = np.isfinite(m_new)
+                safe = np.where(live, m_new, 0.0)
+                alpha = np.where(live, np.exp(m - safe), 1.0)
+                p = np.where(live[:, None], np.exp(s - safe[:, None]), 0.0)
+                l = alpha * l + p.sum(axis=1)
+                o = alpha[:, None] * o + p @ v[b, g, t0:t1]
+                m = m_new
+            out[b, h] = np.divide(o, l[:, None], out=np.zeros_like(o),
+                                  where=(l > 0)[:, None])
+    return out
+
+
+def attention_partial_f64(q_rows, k_rows, v_rows, *, scale, softcap=None,
+                          slope=None, rel=None, ok=None):
+    """One partial result over a subset of keys, for split-KV decode.
+
+    Returns ``(o, lse)`` for a ``[R, D]`` block of queries against the given
+    ``[N, D]`` keys: ``o`` is the softmax-normalised output over that subset
+    and ``lse = m + log(l)`` its log-sum-exp (``-inf`` and a zero row when the
+    subset holds no admissible key).  Together they carry exactly the state of
+    the derivation page's section-3 recurrence, which is what section 8 needs
+    to combine partial outputs of the split key dimension.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k_rows = np.asarray(k_rows, dtype=np.float64)
+    v_rows = np.asarray(v_rows, dtype=np.float64)
+    R, D = q_rows.shape
+    N = k_rows.shape[0]
+    if ok is None:
+        ok = np.ones((R, N), dtype=bool)
+    if rel is None:
+        rel = np.zeros((R, N))
+    if N == 0:
+        return np.zeros((R, D)), np.full((R,), -np.inf)
+    s = _scores(q_rows, k_rows, scale, softcap, slope, rel, ok)
+    has_key = ok.any(axis=1)
+    m = np.where(has_key, s.max(axis=1), 0.0)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    o = np.divide(p @ v_rows, l[:, None], out=np.zeros((R, D)),
+                  where=has_key[:, None])
+    lse = np.where(has_key, m + np.log(np.where(has_key, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def lse_merge_f64(o_parts, lse_parts):
+    """Combine partial results ``o_parts [P, R, D]`` / ``lse_parts [P, R]``.
+
+    Re-basing each part to the common max ``M = max_s lse_s`` with weight
+    ``exp(lse_s - M)`` is the section-3 rescale of the derivation page applied
+    across parts instead of tiles; parts with ``lse = -inf`` weigh 0 and a row
+    with no live part is zero.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    M = lse_parts.max(axis=0)
+    live = np.isfinite(M)
+    w = np.where(live[None, :], np.exp(lse_parts - np.where(live, M, 0.0)[None, :]), 0.0)
+    num = (w[:, :, None] * o_parts).sum(axis=0)
+    den = w.sum(axis=0)
+    return np.divide(num, den[:, None], out=np.zeros_like(num), where=live[:, None])
+
+
+def paged_gather(pool, block_table, seq_len, b, block_size):
+    """Dense ``[seq_len, Hkv, D]`` rows of sequence ``b`` from a paged pool.
+
+    Kernel-contract page, ``attention_paged_naive``: logical key position ``t``
+    lives in physical block ``block_table[b, t // block_size]`` at slot
+    ``t % block_size`` of a ``[num_blocks, block_size, Hkv, D]`` pool.  Indices
+    outside ``[0, num_blocks)`` are rejected (the page bounds-checks them).
+    """
+    pool = np.asarray(pool)
+    t = np.arange(int(seq_len), dtype=np.int64)
+    phys = np.asarray(block_table)[b, t // block_size].astype(np.int64)
+    if phys.size and (phys.min() < 0 or phys.max() >= pool.shape[0]):
+        raise IndexError("block_table entry outside the pool")
+    return pool[phys, t % block_size]
+
+
+def paged_decode_f64(q, k_pool, v_pool, block_table, seq_lens, *, scale,
+                     softcap=None, alibi=None):
+    """Paged-cache attention (kernel-contract page, ``attention_paged_naive``).
+
+    For each sequence the live keys ``0 .. seq_lens[b]-1`` are gathered with
+    :func:`paged_gather` and the dense definition is applied with the implicit
+    causal mask: query slot ``i`` sits at ``seq_lens[b] - Sq + i``, which is the
+    bottom-right alignment of :func:`query_positions` with ``Sk = seq_lens[b]``.
+    At ``Sq = 1`` every live key is admissible (derivation page section 4:
+    a single decode query sees all keys).  ``q`` is ``[B, Hq, Sq, D]``, pools are
+    ``[num_blocks, block_size, Hkv, D]``; returns float64 ``[B, Hq, Sq, D]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_pool = np.asarray(k_pool)
+    v_pool = np.asarray(v_pool)
+    if k_pool.shape != v_pool.shape or k_pool.ndim != 4:
+        raise ValueError("k_pool and v_pool must both be [num_blocks, block_size, Hkv, D]")
+    B, Hq, Sq, D = q.shape
+    block_size = k_pool.shape[1]
+    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    for b in range(B):
+        ctx = int(seq_lens[b])
+        kb = paged_gather(k_pool, block_table, ctx, b, block_size)
+        vb = paged_gather(v_pool, block_table, ctx, b, block_size)
+        kb = np.transpose(kb, (1, 0, 2))[None]          # [1, Hkv, ctx, D]
+        vb = np.transpose(vb, (1, 0, 2))[None]
+        out[b:b + 1] = sdpa_naive_f64(q[b:b + 1], kb, vb, scale=scale,
+                                      causal=True, softcap=softcap, alibi=alibi)
+    return out
+
+
+def admissible_pair_count(Sq, Sk, causal, window_left=None, window_right=None):
+    """Number of admissible (query, key) pairs of one head, counted from the
+    mask of :func:`admissible` row by row."""
+    total = 0
+    for r0 in range(0, Sq, 1024):
+        rows = slice(r0, min(Sq, r0 + 1024))
+        total += int(admissible(Sq, Sk, causal, window_left, window_right, rows).sum())
+    return total
