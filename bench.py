@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill: attn_fwd, bf16, B=2, Hq=32, Hkv=8, Sq=Sk=2048, D=128, causal,
+    scale 1/sqrt(128) -- causal-effective TFLOP/s (4 * D * admissible pairs);
+  * decode: attn_paged_decode, bf16, B=64, Hq=32, Hkv=8, D=128, context
+    lengths uniform on [512, 8192], 64-token blocks randomly permuted in one
+    pool, 8 key splits -- HBM GB/s over the live K/V bytes plus Q, out and the
+    block-table entries read.
+
+Inputs are generated (seeded) and resident in device memory before the timed
+region.  Kernel durations come from HIP events recorded on the stream the
+kernels run on, around each launch inside the timed steps.  ``value`` is the
+prefill TFLOP/s; the decode figures ride along under ``decode``.  The CPU
+oracle is timed on a bounded sample of the same prefill workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --mode profile           # fixed launches for rocprofv3
+    python bench.py --summarize DIR          # text summary of rocprofv3 output
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOPS (bf16 causal prefill) + paged-decode HBM GB/s, % of roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = ["scaled_dot_product_amd/csrc/fwd_mfma.hip",
+                  "scaled_dot_product_amd/csrc/decode.hip",
+                  "scaled_dot_product_amd/csrc/device_common.h"]
+
+
+# ---------------------------------------------------------------- work counts
+
+def admissible_pairs(Sq, Sk, causal, window_left=None, window_right=None) -> int:
+    """(query, key) pairs one head may attend to, counted per row from the
+    admissible interval [max(0, i'-left), min(Sk-1, i', i'+right)], with the
+    bottom-right aligned position i' = i + Sk - Sq."""
+    ip = np.arange(Sq, dtype=np.int64) + (Sk - Sq)
+    lo = np.zeros(Sq, dtype=np.int64) if window_left is None else np.maximum(0, ip - window_left)
+    hi = np.full(Sq, Sk - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, ip)
+    if window_right is not None:
+        hi = np.minimum(hi, ip + window_right)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def prefill_flops(w) -> int:
+    return 4 * w.D * w.B * w.Hq * admissible_pairs(w.Sq, w.Sk, w.causal, w.window_left,
+                                                   w.window_right)
+
+
+def decode_bytes(w, lens) -> int:
+    """Algorithmic HBM bytes of one decode: live K and V rows once, Q and the
+    output once, each live block-table entry once per KV head, the lengths."""
+    lens = np.asarray(lens, dtype=np.int64)
+    es = 2
+    kv = int(lens.sum()) * w.Hkv * w.D * es * 2
+    qo = 2 * w.B * w.Hq * w.D * es
+    pages = int(((lens + w.block_size - 1) // w.block_size).sum())
+    return kv + qo + pages * 4 * w.Hkv + w.B * 4
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-launch HBM bytes measured with rocprofv3 counters, if they were
+    taken on the current kernel sources; {} otherwise."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("sources_sha256_16") != sources_digest():
+        return {}
+    out = {}
+    for key in ("prefill_bytes", "decode_bytes"):
+        if key in vals:
+            out[key] = float(vals[key])
+    return out
+
+
+# ---------------------------------------------------------------- GPU setup
+
+def setup(torch, sdpa, W, dev):
+    wp, wd = W.GQA_CAUSAL_2K, W.PAGED_DECODE
+    q, k, v, _ = W.dense_inputs(wp)
+    pre = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
+    pre["out"] = torch.empty_like(pre["q"])
+    dq, kp, vp, table, lens, _ = W.paged_inputs(wd)
+    dec = dict(q=dq.to(dev), k_pool=kp.to(dev), v_pool=vp.to(dev), block_table=table.to(dev),
+               seq_lens=lens.to(dev))
+    dec["out"] = torch.empty_like(dec["q"])
+    p = sdpa.attn_paged_params(tuple(dq.shape), tuple(kp.shape), table.shape[1], dq.dtype,
+                               num_splits=wd.num_splits)
+    dec["workspace"] = torch.empty(sdpa.attn_paged_decode_workspace_size(p), dtype=torch.uint8,
+                                   device=dev)
+    del kp, vp
+    return wp, wd, pre, dec, lens.numpy()
+
+
+def run_prefill(sdpa, wp, pre, stream):
+    sdpa.attn_fwd(pre["q"], pre["k"], pre["v"], None, pre["out"], softmax_scale=wp.scale,
+                  causal=wp.causal, stream=stream)
+
+
+def run_decode(sdpa, wd, dec, stream):
+    sdpa.attn_paged_decode(dec["q"], dec["k_pool"], dec["v_pool"], dec["block_table"],
+                           dec["seq_lens"], None, dec["out"], softmax_scale=wd.scale,
+                           num_splits=wd.num_splits, workspace=dec["workspace"], stream=stream)
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(W, budget_s: float):
+    """The oracle, as it stands, on whole heads of the prefill workload until
+    about ``budget_s`` seconds of CPU work have been spent (at least one)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    w = W.GQA_CAUSAL_2K
+    q, k, v, _ = W.dense_inputs(w)
+    q64, k64, v64 = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    pairs = admissible_pairs(w.Sq, w.Sk, w.causal)
+    heads, t0 = 0, time.perf_counter()
+    order = [(b, h) for h in range(w.Hq) for b in range(w.B)]
+    while heads < len(order):
+        b, h = order[heads]
+        g = oracle.kv_head_of(h, w.Hq, w.Hkv)
+        oracle.sdpa_naive_f64(q64[b:b + 1, h:h + 1], k64[b:b + 1, g:g + 1], v64[b:b + 1, g:g + 1],
+                              scale=w.scale, causal=True)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * w.D * pairs * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of the prefill workload "
+                      f"(all 2048 rows each), float64 NumPy, {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------- modes
+
+def bench(args):
+    import torch
+    import scaled_dot_product_amd as sdpa
+    import workloads as W
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU (cuda:0)")
+    dev = torch.device("cuda:0")
+    sdpa.library()
+    wp, wd, pre, dec, lens = setup(torch, sdpa, W, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        run_prefill(sdpa, wp, pre, stream)
+        run_decode(sdpa, wd, dec, stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run_prefill(sdpa, wp, pre, stream)
+        ev[i][1].record(stream)
+        run_decode(sdpa, wd, dec, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+
+    flops = prefill_flops(wp)
+    nbytes = decode_bytes(wd, lens)
+    tflops = flops / t_pre / 1e12
+    gbs = nbytes / t_dec / 1e9
+    traffic = read_traffic()
+    roof_pre = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic.get("prefill_bytes"),
+                "kernel": "fwd_mfma_kernel<bf16, D=128, causal>",
+                "work_per_launch": flops, "ms_per_launch": t_pre * 1e3}
+    roof_dec = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic.get("decode_bytes"),
+                "kernel": "decode_partial_kernel<bf16, D=128, 4 heads> + decode_merge_kernel",
+                "work_per_launch": nbytes, "ms_per_launch": t_dec * 1e3}
+    dominant = roof_pre if t_pre >= t_dec else roof_dec
+    result = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs; uniform context lengths)",
+        "config": {"workload": f"{wp.name} + {wd.name}",
+                   "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
+                               "D": wp.D, "causal": wp.causal},
+                   "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D,
+                              "block_size": wd.block_size, "ctx": [wd.ctx_lo, wd.ctx_hi],
+                              "num_splits": wd.num_splits, "live_tokens": int(lens.sum())}},
+        "decode": {"value": gbs, "unit": "GB/s", "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+                   "ms": t_dec * 1e3},
+        "roofline": dominant,
+        "rooflines": {"prefill": roof_pre, "decode": roof_dec},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def profile(args):
+    """Fixed launches for rocprofv3: 10 prefills, 10 decodes, and a plain
+    256 MiB float32 copy kernel (read N, write N) that calibrates the HBM
+    byte counters."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    wp, wd, pre, dec, lens = setup(torch, sdpa, W, dev)
+    stream = torch.cuda.current_stream(dev)
+    src = torch.randn(64 * 1024 * 1024, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        run_prefill(sdpa, wp, pre, stream)
+        run_decode(sdpa, wd, dec, stream)
+    torch.cuda.synchronize()
+    for _ in range(args.launches):
+        run_prefill(sdpa, wp, pre, stream)
+    for _ in range(args.launches):
+        run_decode(sdpa, wd, dec, stream)
+    for _ in range(args.launches):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_launches": args.launches, "prefill_flops": prefill_flops(wp),
+                      "decode_bytes": decode_bytes(wd, lens), "copy_bytes_each_way": src.numel() * 4,
+                      "sources_sha256_16": sources_digest()}), flush=True)
+
+
+def summarize(path):
+    """Print the per-kernel duration table of a rocprofv3 --stats run."""
+    files = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {path}")
+    for fn in files:
+        print(f"# {os.path.relpath(fn, path)}")
+        with open(fn) as f:
+            rows = list(csv.DictReader(f))
+        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+        for r in rows:
+            name = r.get("Name", "?")
+            print(f"{int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
+                  f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} {float(r.get('MaxNs', 0)) / 1e3:>10.2f} "
+                  f"{float(r.get('Percentage', 0)):>6.2f}  {name[:150]}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
+    ap.add_argument("--launches", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--summarize", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize:
+        return summarize(args.summarize)
+    if args.gpus != 1:
+        sys.exit(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the attention "
+                 "kernels here are single-GPU, and multi-GPU sharding is not part of this build")
+    if args.mode == "profile":
+        return profile(args)
+    return bench(args)
+
+
+if __name__ == "__main__":
+    main()

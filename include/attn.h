@@ -1,0 +1,177 @@
+/*
+ * attn.h -- C ABI of libattn: attention forward on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, each with a host-only argument check that makes no HIP call:
+ *
+ *   attn_fwd            multi-head scaled dot-product attention forward over
+ *                       dense [B, H, S, D] tensors, computed as a tiled
+ *                       online-softmax recurrence.
+ *   attn_paged_decode   one decode query per sequence against a paged KV
+ *                       pool, split over the key dimension, with the partial
+ *                       results merged through their log-sum-exp.
+ *
+ * What is computed follows two pages: the kernel-contract page
+ * ("fuel-reference-backend -- attention kernel contracts", sections
+ * attention_naive, attention_flash and attention_paged_naive) and the
+ * derivation page ("gfx942 unified attention, from the math up", sections 1-5
+ * and 8).  For query row i of head h (KV head g = h / (Hq / Hkv)):
+ *
+ *   i'  = i + Sk - Sq                        bottom-right aligned position
+ *   s_j = softmax_scale * (q_i . k_j)
+ *   s_j = softcap * tanh(s_j / softcap)      if softcap > 0
+ *   s_j = s_j + alibi[h] * (j - i')          if alibi != NULL
+ *   key j is admissible iff 0 <= j < Sk, (!causal || j <= i'),
+ *         (window_left  < 0 || j >= i' - window_left),
+ *         (window_right < 0 || j <= i' + window_right)
+ *   out_i = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m) over admissible j
+ *           (m = max admissible s_j), and out_i = 0 if no key is admissible.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller and borrowed
+ *     only for the work enqueued by the call.  The library allocates nothing,
+ *     frees nothing and keeps no state between calls.
+ *   - Tensors are contiguous, row-major, zero-offset, 16-byte aligned.  Views
+ *     with other strides must be materialised by the caller.
+ *   - q, k, v (or the pools) and out share one element type (dtype); out has
+ *     the shape and dtype of q.  ALiBi slopes are always float32 [Hq].
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  A non-OK status means nothing was enqueued, except
+ *     ATTN_ERR_HIP, which reports a launch failure.
+ *   - Results are bitwise reproducible for identical inputs and parameters
+ *     (no atomics in any reduction, fixed reduction orders).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_dtype {
+  ATTN_F32 = 0,
+  ATTN_F16 = 1,
+  ATTN_BF16 = 2
+} attn_dtype_t;
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  ATTN_ERR_DTYPE = 2,        /* dtype is not an attn_dtype_t value                  */
+  ATTN_ERR_SHAPE = 3,        /* a size is negative, inconsistent or too large       */
+  ATTN_ERR_GQA = 4,          /* Hkv == 0 or Hq is not a multiple of Hkv             */
+  ATTN_ERR_HEAD_DIM = 5,     /* D is not 64 or 128                                  */
+  ATTN_ERR_PARAM = 6,        /* scale/softcap/window/split parameter out of range   */
+  ATTN_ERR_ALIGN = 7,        /* a pointer is not 16-byte aligned                    */
+  ATTN_ERR_ALIAS = 8,        /* out overlaps an input or the workspace              */
+  ATTN_ERR_WORKSPACE = 9,    /* workspace missing or smaller than required          */
+  ATTN_ERR_UNSUPPORTED = 10, /* allowed by the contract but not built here          */
+  ATTN_ERR_HIP = 11          /* the HIP runtime reported an error at launch         */
+} attn_status_t;
+
+/* Parameters of attn_fwd (kernel-contract page, attention_naive: the
+ * FlashAttn parameter set -- scale, causal flag, optional left/right window,
+ * optional softcap). */
+typedef struct attn_fwd_params {
+  int64_t B;             /* batch                                               */
+  int64_t Hq;            /* query heads; a multiple of Hkv                      */
+  int64_t Hkv;           /* key/value heads                                     */
+  int64_t Sq;            /* query length (0 allowed: nothing to do)             */
+  int64_t Sk;            /* key length (0 allowed: output is all zero)          */
+  int64_t D;             /* head dim: 64 or 128                                 */
+  int32_t dtype;         /* attn_dtype_t of q, k, v and out                     */
+  int32_t causal;        /* nonzero: bottom-right causal mask                   */
+  int64_t window_left;   /* -1: unbounded; else keys j >= i' - window_left      */
+  int64_t window_right;  /* -1: unbounded; else keys j <= i' + window_right     */
+  float softmax_scale;   /* finite, >= 0 (1/sqrt(D) is the usual value)         */
+  float softcap;         /* 0: off; > 0: s <- softcap * tanh(s / softcap)       */
+} attn_fwd_params_t;
+
+/* Host-only validation of an attn_fwd call (no HIP call is made).
+ *   q     [B, Hq, Sq, D]   dtype
+ *   k, v  [B, Hkv, Sk, D]  dtype
+ *   alibi [Hq] float32 or NULL
+ *   out   [B, Hq, Sq, D]   dtype; must not overlap q, k, v or alibi.
+ * A pointer may be NULL only when its tensor has no elements. */
+attn_status_t attn_fwd_check(const void* q, const void* k, const void* v,
+                             const float* alibi, const void* out,
+                             const attn_fwd_params_t* p);
+
+/* Attention forward: validates as attn_fwd_check, then enqueues the kernel
+ * for p->dtype and p->D on `stream` and returns.  F16/BF16 compute both
+ * matmuls on the matrix cores with float32 accumulation (the softmax weights
+ * enter the second matmul rounded to the input dtype); F32 computes in
+ * float32 throughout. */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v,
+                       const float* alibi, void* out,
+                       const attn_fwd_params_t* p, void* stream);
+
+/* Parameters of attn_paged_decode (kernel-contract page, attention_paged_naive:
+ * the PagedAttn parameter set -- scale, block size, optional softcap -- plus
+ * the number of key-dimension splits of the decode path, derivation page
+ * section 8). */
+typedef struct attn_paged_params {
+  int64_t B;                   /* sequences                                      */
+  int64_t Hq;                  /* query heads; a multiple of Hkv                 */
+  int64_t Hkv;                 /* key/value heads                                */
+  int64_t D;                   /* head dim: 64 or 128                            */
+  int64_t num_blocks;          /* physical blocks in each pool                   */
+  int64_t block_size;          /* tokens per block (>= 1)                        */
+  int64_t max_blocks_per_seq;  /* columns of block_table                         */
+  int32_t dtype;               /* attn_dtype_t of q, pools and out (F16, BF16)   */
+  int32_t num_splits;          /* key-dimension splits per sequence, 1..256      */
+  float softmax_scale;         /* finite, >= 0                                   */
+  float softcap;               /* 0: off; > 0: softcap * tanh(s / softcap)       */
+} attn_paged_params_t;
+
+/* Bytes of device workspace attn_paged_decode needs for these parameters
+ * (0 if the parameters are invalid).  The workspace holds, per (sequence,
+ * query head, split), a float32 partial output [D] and its log-sum-exp. */
+size_t attn_paged_decode_workspace_size(const attn_paged_params_t* p);
+
+/* Host-only validation of an attn_paged_decode call (no HIP call is made).
+ *   q            [B, Hq, 1, D]                         dtype
+ *   k_pool,v_pool[num_blocks, block_size, Hkv, D]       dtype
+ *   block_table  [B, max_blocks_per_seq] int32: physical block of logical
+ *                block n of sequence b; entries past the last live block are
+ *                never read.
+ *   seq_lens     [B] int32: live keys of sequence b (the query sits at
+ *                position seq_lens[b] - 1 and sees every live key).
+ *   alibi        [Hq] float32 or NULL (ALiBi distance is k_pos - (seq_len-1))
+ *   out          [B, Hq, 1, D] dtype
+ *   workspace    >= attn_paged_decode_workspace_size(p) bytes
+ *   error_flag   NULL or one device int32. */
+attn_status_t attn_paged_decode_check(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      const float* alibi, const void* out,
+                                      const void* workspace, size_t workspace_bytes,
+                                      const int32_t* error_flag,
+                                      const attn_paged_params_t* p);
+
+/* Paged split-KV decode: validates as attn_paged_decode_check, then enqueues
+ * the partial kernel (one workgroup per sequence, KV head and split) and the
+ * merge kernel on `stream` and returns.  Device-side errors do not fault:
+ * a seq_len outside [0, max_blocks_per_seq * block_size] is clamped into that
+ * range and a block_table entry outside [0, num_blocks) masks its keys; both
+ * store 1 to *error_flag when error_flag is not NULL (the flag is never
+ * cleared by the library).  A sequence with no live key outputs zeros. */
+attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const float* alibi, void* out,
+                                void* workspace, size_t workspace_bytes,
+                                int32_t* error_flag,
+                                const attn_paged_params_t* p, void* stream);
+
+/* Static string naming a status code. */
+const char* attn_status_str(attn_status_t status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

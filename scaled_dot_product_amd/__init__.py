@@ -1,0 +1,246 @@
+"""Attention forward on AMD Instinct MI355X (gfx950): Python binding of libattn.
+
+The entry points mirror the C ABI of ``include/attn.h`` one to one and only
+marshal arguments: tensor pointers, sizes and the caller's stream go to the
+HIP library, where every step of the computation runs.  PyTorch supplies the
+device memory (and allocates ``out`` / the decode workspace when the caller
+does not pass them).  There is no fallback: if ``libattn.so`` is missing or
+fails to load, every call raises.
+
+    attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
+             window_left=None, window_right=None, softcap=None, stream=None)
+    attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
+                      out=None, *, softmax_scale=None, softcap=None,
+                      num_splits=8, workspace=None, error_flag=None, stream=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "AttnError", "library", "LIB_PATH",
+    "attn_fwd", "attn_fwd_check", "attn_fwd_params",
+    "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
+    "attn_paged_params", "attn_status_str", "attn_version",
+    "ATTN_F32", "ATTN_F16", "ATTN_BF16",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DTYPE", 3: "ATTN_ERR_SHAPE",
+    4: "ATTN_ERR_GQA", 5: "ATTN_ERR_HEAD_DIM", 6: "ATTN_ERR_PARAM", 7: "ATTN_ERR_ALIGN",
+    8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_WORKSPACE", 10: "ATTN_ERR_UNSUPPORTED", 11: "ATTN_ERR_HIP",
+}
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from libattn (``status`` holds the code)."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({attn_status_str(status)})")
+
+
+class attn_fwd_params_t(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("Sq", ctypes.c_int64), ("Sk", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("window_left", ctypes.c_int64), ("window_right", ctypes.c_int64),
+                ("softmax_scale", ctypes.c_float), ("softcap", ctypes.c_float)]
+
+
+class attn_paged_params_t(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("num_blocks", ctypes.c_int64),
+                ("block_size", ctypes.c_int64), ("max_blocks_per_seq", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("softcap", ctypes.c_float)]
+
+
+_lib = None
+_VP = ctypes.c_void_p
+
+
+def library():
+    """Load ``libattn.so`` (raises ImportError when it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m scaled_dot_product_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    fwd_p = ctypes.POINTER(attn_fwd_params_t)
+    pag_p = ctypes.POINTER(attn_paged_params_t)
+    lib.attn_fwd_check.argtypes = [_VP, _VP, _VP, _VP, _VP, fwd_p]
+    lib.attn_fwd_check.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP, fwd_p, _VP]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_paged_decode_workspace_size.argtypes = [pag_p]
+    lib.attn_paged_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_paged_decode_check.argtypes = [_VP] * 8 + [ctypes.c_size_t, _VP, pag_p]
+    lib.attn_paged_decode_check.restype = ctypes.c_int
+    lib.attn_paged_decode.argtypes = [_VP] * 8 + [ctypes.c_size_t, _VP, pag_p, _VP]
+    lib.attn_paged_decode.restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def attn_status_str(status: int) -> str:
+    return library().attn_status_str(int(status)).decode()
+
+
+def attn_version() -> int:
+    return int(library().attn_version())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else (t.data_ptr() or None)
+
+
+def _need_device(name, t, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (materialise the view first)")
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def attn_fwd_params(q_shape, k_shape, dtype, *, softmax_scale=None, causal=False,
+                    window_left=None, window_right=None, softcap=None) -> attn_fwd_params_t:
+    B, Hq, Sq, D = q_shape
+    _, Hkv, Sk, _ = k_shape
+    return attn_fwd_params_t(
+        B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, D=D,
+        dtype=_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+        causal=1 if causal else 0,
+        window_left=-1 if window_left is None else int(window_left),
+        window_right=-1 if window_right is None else int(window_right),
+        softmax_scale=(1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale),
+        softcap=0.0 if not softcap else float(softcap))
+
+
+def attn_fwd_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr, params: attn_fwd_params_t) -> int:
+    """Host-only argument check (no HIP call): returns the status code."""
+    return int(library().attn_fwd_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr,
+                                        None if params is None else ctypes.byref(params)))
+
+
+def attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
+             window_left=None, window_right=None, softcap=None, stream=None):
+    """Attention forward over ``[B, H, S, D]`` device tensors (see attn.h)."""
+    lib = library()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("alibi", alibi), ("out", out)):
+        _need_device(name, t, dev)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, Hq, Sq, D]; k and v the same [B, Hkv, Sk, D]")
+    if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("batch and head dim of k/v must match q")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must share one dtype of float32 / float16 / bfloat16")
+    if alibi is not None and (alibi.dtype != torch.float32 or alibi.shape != (q.shape[1],)):
+        raise ValueError("alibi slopes must be float32 [Hq]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    p = attn_fwd_params(tuple(q.shape), tuple(k.shape), q.dtype, softmax_scale=softmax_scale,
+                        causal=causal, window_left=window_left, window_right=window_right,
+                        softcap=softcap)
+    st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alibi), _ptr(out), ctypes.byref(p),
+                      _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out
+
+
+def attn_paged_params(q_shape, pool_shape, max_blocks_per_seq, dtype, *, softmax_scale=None,
+                      softcap=None, num_splits=8) -> attn_paged_params_t:
+    B, Hq, _, D = q_shape
+    num_blocks, block_size, Hkv, _ = pool_shape
+    return attn_paged_params_t(
+        B=B, Hq=Hq, Hkv=Hkv, D=D, num_blocks=num_blocks, block_size=block_size,
+        max_blocks_per_seq=max_blocks_per_seq,
+        dtype=_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+        num_splits=int(num_splits),
+        softmax_scale=(1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale),
+        softcap=0.0 if not softcap else float(softcap))
+
+
+def attn_paged_decode_workspace_size(params: attn_paged_params_t) -> int:
+    return int(library().attn_paged_decode_workspace_size(ctypes.byref(params)))
+
+
+def attn_paged_decode_check(q_ptr, k_ptr, v_ptr, table_ptr, lens_ptr, alibi_ptr, out_ptr,
+                            ws_ptr, ws_bytes, err_ptr, params: attn_paged_params_t) -> int:
+    """Host-only argument check (no HIP call): returns the status code."""
+    return int(library().attn_paged_decode_check(q_ptr, k_ptr, v_ptr, table_ptr, lens_ptr,
+                                                 alibi_ptr, out_ptr, ws_ptr, ws_bytes, err_ptr,
+                                                 None if params is None else ctypes.byref(params)))
+
+
+def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
+                      softmax_scale=None, softcap=None, num_splits=8, workspace=None,
+                      error_flag=None, stream=None):
+    """Paged split-KV decode, one query per sequence (see attn.h)."""
+    lib = library()
+    dev = q.device
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("alibi", alibi),
+                    ("out", out), ("workspace", workspace), ("error_flag", error_flag)):
+        _need_device(name, t, dev)
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [B, Hq, 1, D]")
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must both be [num_blocks, block_size, Hkv, D]")
+    if k_pool.shape[3] != q.shape[3]:
+        raise ValueError("pool head dim must match q")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q and the pools must share one dtype")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != q.shape[0]:
+        raise ValueError("block_table must be int32 [B, max_blocks_per_seq]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("seq_lens must be int32 [B]")
+    if alibi is not None and (alibi.dtype != torch.float32 or alibi.shape != (q.shape[1],)):
+        raise ValueError("alibi slopes must be float32 [Hq]")
+    if error_flag is not None and (error_flag.dtype != torch.int32 or error_flag.numel() != 1):
+        raise ValueError("error_flag must be one int32")
+    p = attn_paged_params(tuple(q.shape), tuple(k_pool.shape), block_table.shape[1], q.dtype,
+                          softmax_scale=softmax_scale, softcap=softcap, num_splits=num_splits)
+    need = attn_paged_decode_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                               _ptr(seq_lens), _ptr(alibi), _ptr(out), _ptr(workspace), ws_bytes,
+                               _ptr(error_flag), ctypes.byref(p), _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_paged_decode")
+    return out

@@ -1,0 +1,260 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h.
+//
+// Argument validation is pure host code (no HIP call), so the *_check entry
+// points work on machines without a GPU.  The compute entry points validate,
+// narrow the sizes, pick the kernel for (dtype, head dim) and enqueue it on the
+// caller's stream.  Nothing is allocated and no state is kept.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "attn.h"
+#include "launch.h"
+
+namespace attn {
+hipError_t launch_fwd_mfma_bf16_d128(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_mfma_bf16_d64(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_mfma_f16_d128(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_mfma_f16_d64(const FwdProblem& p, hipStream_t stream);
+
+hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream) {
+  if (dtype == ATTN_BF16)
+    return p.D == 128 ? launch_fwd_mfma_bf16_d128(p, stream) : launch_fwd_mfma_bf16_d64(p, stream);
+  return p.D == 128 ? launch_fwd_mfma_f16_d128(p, stream) : launch_fwd_mfma_f16_d64(p, stream);
+}
+}  // namespace attn
+
+namespace {
+
+constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions stay far inside int32
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+bool valid_dtype(int32_t d) { return d == ATTN_F32 || d == ATTN_F16 || d == ATTN_BF16; }
+int64_t elem_bytes(int32_t d) { return d == ATTN_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b * ... without overflow (all factors >= 0); false on overflow.
+bool mul(int64_t a, int64_t b, int64_t* r) {
+  if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
+  *r = a * b;
+  return true;
+}
+bool mul4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* r) {
+  int64_t x, y;
+  return mul(a, b, &x) && mul(x, c, &y) && mul(y, d, r);
+}
+
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+bool overlaps(Span a, Span b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+bool bad_scale(float s) { return !std::isfinite(s) || s < 0.f; }
+bool bad_softcap(float c) { return !std::isfinite(c) || c < 0.f; }
+
+// Byte sizes of the dense operands; fills q/kv/out byte counts.
+attn_status_t fwd_shape(const attn_fwd_params_t* p, int64_t* q_bytes, int64_t* kv_bytes) {
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->Sq < 0 || p->Sk < 0 || p->D < 0)
+    return ATTN_ERR_SHAPE;
+  if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
+  if (p->D != 64 && p->D != 128) return ATTN_ERR_HEAD_DIM;
+  if (p->Sq > kMaxLen || p->Sk > kMaxLen) return ATTN_ERR_SHAPE;
+  int64_t bh;
+  if (!mul(p->B, p->Hq, &bh) || bh > kMaxLen) return ATTN_ERR_SHAPE;
+  const int64_t qblocks = (p->Sq + 63) / 64;
+  int64_t grid;
+  if (!mul(bh, qblocks, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
+  const int64_t es = elem_bytes(p->dtype);
+  if (!mul4(p->B, p->Hq, p->Sq, p->D * es, q_bytes)) return ATTN_ERR_SHAPE;
+  if (!mul4(p->B, p->Hkv, p->Sk, p->D * es, kv_bytes)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status_t check_fwd(const void* q, const void* k, const void* v, const float* alibi,
+                        const void* out, const attn_fwd_params_t* p) {
+  if (!p) return ATTN_ERR_NULL;
+  if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
+  int64_t qb, kvb;
+  const attn_status_t st = fwd_shape(p, &qb, &kvb);
+  if (st != ATTN_OK) return st;
+  if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
+  if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_PARAM;
+  if (qb > 0 && (!q || !out)) return ATTN_ERR_NULL;
+  if (qb > 0 && kvb > 0 && (!k || !v)) return ATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, alibi, out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return ATTN_ERR_ALIGN;
+  const Span o{out, qb};
+  if (overlaps(o, Span{q, qb}) || overlaps(o, Span{k, kvb}) || overlaps(o, Span{v, kvb}) ||
+      overlaps(o, Span{alibi, p->Hq * 4}))
+    return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+int64_t paged_ws_lse_offset(const attn_paged_params_t* p) {
+  const int64_t o_bytes = p->B * p->Hq * (int64_t)p->num_splits * p->D * 4;
+  return (o_bytes + 255) / 256 * 256;
+}
+
+attn_status_t paged_shape(const attn_paged_params_t* p) {
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->D < 0 || p->num_blocks < 0 ||
+      p->max_blocks_per_seq < 0)
+    return ATTN_ERR_SHAPE;
+  if (p->block_size < 1) return ATTN_ERR_SHAPE;
+  if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
+  if (p->D != 64 && p->D != 128) return ATTN_ERR_HEAD_DIM;
+  if (p->num_splits < 1 || p->num_splits > 256) return ATTN_ERR_PARAM;
+  if (p->B > 65535 || p->Hq > 65535) return ATTN_ERR_SHAPE;
+  const int64_t hchunks = (p->Hq / p->Hkv + 15) / 16;
+  if (p->Hkv * hchunks > 65535) return ATTN_ERR_SHAPE;
+  int64_t cap, pool_tokens;
+  if (!mul(p->max_blocks_per_seq, p->block_size, &cap) || cap > kMaxLen) return ATTN_ERR_SHAPE;
+  if (!mul(p->num_blocks, p->block_size, &pool_tokens) || pool_tokens > (int64_t(1) << 40))
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const float* alibi,
+                             const void* out, const attn_fwd_params_t* p) {
+  return check_fwd(q, k, v, alibi, out, p);
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, const float* alibi, void* out,
+                       const attn_fwd_params_t* p, void* stream) {
+  const attn_status_t st = check_fwd(q, k, v, alibi, out, p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Hq == 0 || p->Sq == 0) return ATTN_OK;
+  attn::FwdProblem fp;
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.alibi = alibi;
+  fp.out = out;
+  fp.B = (int)p->B;
+  fp.Hq = (int)p->Hq;
+  fp.Hkv = (int)p->Hkv;
+  fp.Sq = (int)p->Sq;
+  fp.Sk = (int)p->Sk;
+  fp.D = (int)p->D;
+  fp.causal = p->causal != 0;
+  // Windows wider than every possible distance are the same as no window.
+  fp.wl = (p->window_left < 0 || p->window_left >= p->Sk) ? -1 : (int)p->window_left;
+  fp.wr = (p->window_right < 0 || p->window_right >= p->Sq) ? -1 : (int)p->window_right;
+  fp.scale = p->softmax_scale;
+  fp.softcap = p->softcap;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      p->dtype == ATTN_F32 ? attn::launch_fwd_f32(fp, s) : attn::launch_fwd_mfma(fp, p->dtype, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_paged_decode_workspace_size(const attn_paged_params_t* p) {
+  if (!p || paged_shape(p) != ATTN_OK) return 0;
+  const int64_t lse_bytes = p->B * p->Hq * (int64_t)p->num_splits * 4;
+  return (size_t)(paged_ws_lse_offset(p) + lse_bytes);
+}
+
+attn_status_t attn_paged_decode_check(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      const float* alibi, const void* out, const void* workspace,
+                                      size_t workspace_bytes, const int32_t* error_flag,
+                                      const attn_paged_params_t* p) {
+  if (!p) return ATTN_ERR_NULL;
+  if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
+  if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  const attn_status_t st = paged_shape(p);
+  if (st != ATTN_OK) return st;
+  if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
+  const int64_t es = elem_bytes(p->dtype);
+  const int64_t q_bytes = p->B * p->Hq * p->D * es;
+  int64_t pool_bytes;
+  if (!mul4(p->num_blocks, p->block_size, p->Hkv, p->D * es, &pool_bytes)) return ATTN_ERR_SHAPE;
+  const int64_t table_bytes = p->B * p->max_blocks_per_seq * 4;
+  const int64_t lens_bytes = p->B * 4;
+  if (q_bytes > 0) {
+    if (!q || !out || !seq_lens) return ATTN_ERR_NULL;
+    if (table_bytes > 0 && !block_table) return ATTN_ERR_NULL;
+    if (pool_bytes > 0 && (!k_pool || !v_pool)) return ATTN_ERR_NULL;
+  }
+  const size_t need = attn_paged_decode_workspace_size(p);
+  if (q_bytes > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k_pool, v_pool, block_table, seq_lens, alibi, out, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return ATTN_ERR_ALIGN;
+  if (error_flag && (reinterpret_cast<uintptr_t>(error_flag) & 3u)) return ATTN_ERR_ALIGN;
+  const Span o{out, q_bytes}, ws{workspace, (int64_t)need};
+  const Span inputs[] = {{q, q_bytes},          {k_pool, pool_bytes},    {v_pool, pool_bytes},
+                         {block_table, table_bytes}, {seq_lens, lens_bytes}, {alibi, p->Hq * 4},
+                         {error_flag, 4}};
+  for (const Span& in : inputs)
+    if (overlaps(o, in) || overlaps(ws, in)) return ATTN_ERR_ALIAS;
+  if (overlaps(o, ws)) return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const float* alibi, void* out, void* workspace,
+                                size_t workspace_bytes, int32_t* error_flag,
+                                const attn_paged_params_t* p, void* stream) {
+  const attn_status_t st = attn_paged_decode_check(q, k_pool, v_pool, block_table, seq_lens, alibi,
+                                                   out, workspace, workspace_bytes, error_flag, p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Hq == 0) return ATTN_OK;
+  attn::DecodeProblem dp;
+  dp.q = q;
+  dp.k_pool = k_pool;
+  dp.v_pool = v_pool;
+  dp.block_table = block_table;
+  dp.seq_lens = seq_lens;
+  dp.alibi = alibi;
+  dp.out = out;
+  dp.ws_o = static_cast<float*>(workspace);
+  dp.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + paged_ws_lse_offset(p));
+  dp.error_flag = error_flag;
+  dp.B = (int)p->B;
+  dp.Hq = (int)p->Hq;
+  dp.Hkv = (int)p->Hkv;
+  dp.D = (int)p->D;
+  dp.num_blocks = p->num_blocks > INT32_MAX ? INT32_MAX : (int)p->num_blocks;
+  dp.block_size = (int)p->block_size;
+  dp.max_blocks = (int)p->max_blocks_per_seq;
+  dp.splits = p->num_splits;
+  dp.scale = p->softmax_scale;
+  dp.softcap = p->softcap;
+  const hipError_t e = attn::launch_paged_decode(dp, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_status_str(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "required pointer is NULL";
+    case ATTN_ERR_DTYPE: return "invalid dtype";
+    case ATTN_ERR_SHAPE: return "invalid or too large shape";
+    case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
+    case ATTN_ERR_HEAD_DIM: return "head dim must be 64 or 128";
+    case ATTN_ERR_PARAM: return "parameter out of range";
+    case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ATTN_ERR_ALIAS: return "output overlaps an input";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_UNSUPPORTED: return "supported by the contract but not built";
+    case ATTN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int32_t attn_version(void) { return 100; }
+
+}  // extern "C"

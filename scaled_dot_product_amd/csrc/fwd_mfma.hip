@@ -1,0 +1,378 @@
+// fwd_mfma.hip -- attention forward for bf16 / f16 on the gfx950 matrix cores.
+//
+// Computes what the kernel-contract page ("fuel-reference-backend -- attention
+// kernel contracts", attention_naive / attention_flash) defines, with the
+// streaming softmax of the derivation page ("gfx942 unified attention, from the
+// math up", section 3) and its causal tile early exit (section 4).
+//
+// Compiled once per (element type, head dim): ATTN_ELEM is __bf16 or _Float16,
+// ATTN_D is 64 or 128, ATTN_TAG names the exported launcher.
+//
+// Mapping onto CDNA4 (designed for gfx950, not taken from the gfx942 design):
+//   * A workgroup of 4 waves owns 128 query rows of one (batch, head); each
+//     wave owns 32 rows.  Key/value tiles of 64 keys are staged in LDS
+//     (double-buffered, one barrier per tile) and shared by the 4 waves.
+//   * Scores are computed transposed, S^T = K Q^T, on the 32x32x16 matrix
+//     instruction: K (LDS, row-major, XOR-swizzled 16-byte chunks) is the A
+//     operand, this wave's Q rows (registers, loaded once) are the B operand.
+//     In the 32x32 accumulator layout a lane then holds 16 keys of ONE query,
+//     so row reductions are in-lane plus a single cross-half swap.
+//   * Softmax runs in log2 units (exp2); the running max is raised only when a
+//     tile's max exceeds it by more than 2^8, which keeps every weight <= 256
+//     and skips the rescale of the output in almost every tile.  The final
+//     o / l is independent of the reference value, so the result is the same
+//     recurrence (the derivation page notes the streaming form is exact).
+//   * The weights, rounded to the input type, are already laid out as the B
+//     operand of O^T = V^T P^T; V^T comes from row-major V in LDS through the
+//     gfx950 LDS transpose read.  The output accumulator therefore also has
+//     one query per lane, matching the softmax state.
+//   * Tiles wholly outside a wave's admissible key range are skipped (causal
+//     and window early exit, per wave); masks are evaluated only on tiles that
+//     straddle a mask boundary.
+//   * Workgroups are issued heaviest-first under a causal mask, and the heads
+//     of one dispatch round are dealt to the 8 XCDs in contiguous runs so that
+//     the query heads sharing a KV head run on the same L2.
+#include <limits.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+#ifndef ATTN_ELEM
+#define ATTN_ELEM __bf16
+#define ATTN_D 128
+#define ATTN_TAG bf16_d128
+#endif
+
+#define ATTN_CAT2(a, b) a##b
+#define ATTN_CAT(a, b) ATTN_CAT2(a, b)
+
+namespace attn {
+namespace {
+
+constexpr int kBN = 64;            // keys per tile
+constexpr int kNW = 4;             // waves per workgroup
+constexpr int kQW = 32;            // query rows per wave
+constexpr int kBM = kNW * kQW;     // query rows per workgroup
+constexpr int kThreads = kNW * 64;
+constexpr float kRescaleGap = 8.0f;  // log2 units: weights stay <= 2^8
+
+enum : int { F_MASK = 1, F_SOFTCAP = 2, F_ALIBI = 4 };
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alibi;
+  void* out;
+  int Sq, Sk, Hq, Hkv, group, nbh, nqb;
+  int heavy_first;
+  int wl;       // left window, -1 = unbounded
+  int has_hi;   // is j - i' bounded above?
+  int dmax;     // that bound (causal and/or right window)
+  float c_score;  // log2(e) * scale; with softcap 2 * log2(e) * scale / cap
+  float c_cap;    // log2(e) * cap
+};
+
+// XOR swizzles of the 16-byte chunk index, chosen so that the matrix-operand
+// reads of K (16 rows, one chunk each) and the transpose reads of V (4 rows x
+// 2-4 chunks per 16/32 lanes) hit distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// Key offset (within a 64-key tile, without the lane-half term 4*g) of
+// accumulator element r of score block kb, from the 32x32 accumulator layout:
+// element r of lane l is row 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ constexpr int key_of(int kb, int r) {
+  return 32 * kb + 8 * (r >> 2) + (r & 3);
+}
+
+template <typename T, int D, int FLAGS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(FwdArgs a) {
+  using E = Elem<T>;
+  constexpr bool MASK = (FLAGS & F_MASK) != 0;
+  constexpr bool SOFTCAP = (FLAGS & F_SOFTCAP) != 0;
+  constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
+  constexpr int NC = D / 8;              // 16-byte chunks per K/V row
+  constexpr int TC = kBN * NC;           // chunks per K (or V) tile
+  constexpr int CPT = TC / kThreads;     // chunks per thread per tile and tensor
+  constexpr int KS = D / 16;             // contraction steps of K Q^T
+  constexpr int DB = D / 32;             // 32-row blocks of O^T
+  static_assert(CPT * kThreads == TC, "tile must split evenly over the workgroup");
+
+  __shared__ u32x4 smem[2][2][TC];       // [buffer][K, V][chunk]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;               // lane half
+  const int ln = lane & 31;
+
+  // ---- work item: (query block, head, batch)
+  const int id = blockIdx.x;
+  const int round = id / a.nbh;
+  const int u = id - round * a.nbh;
+  const int bh = (a.nbh & 7) == 0 ? ((u & 7) * (a.nbh >> 3) + (u >> 3)) : u;
+  const int qb = a.heavy_first ? (a.nqb - 1 - round) : round;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int kvh = h / a.group;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const int m0 = qb * kBM;
+
+  const T* Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * Sq * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * Sk * D;
+  const T* V = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * Sk * D;
+  T* O = reinterpret_cast<T*>(a.out) + (size_t)bh * Sq * D;
+
+  // ---- admissible key ranges: [lo(i'_first), hi(i'_last))
+  auto key_lo = [&](int ipa) { return a.wl >= 0 ? max(0, ipa - a.wl) : 0; };
+  auto key_hi = [&](int ipb) { return a.has_hi ? min(Sk, max(0, ipb + a.dmax + 1)) : Sk; };
+  const int wg_last = min(m0 + kBM, Sq) - 1;
+  const int n_lo = key_lo(m0 + off);
+  const int n_hi = key_hi(wg_last + off);
+  const int t_begin = n_lo / kBN;
+  const int t_end = n_hi > n_lo ? (n_hi + kBN - 1) / kBN : t_begin;
+
+  const int wq0 = m0 + wave * kQW;
+  const bool wave_live = wq0 < Sq;
+  const int wq_last = min(wq0 + kQW, Sq) - 1;
+  const int ipa_w = wq0 + off, ipb_w = wq_last + off;
+  const int w_lo = key_lo(ipa_w);
+  const int w_hi = key_hi(ipb_w);
+
+  const int qi = wq0 + ln;  // this lane's query row
+  const int ip = qi + off;  // its bottom-right aligned position
+
+  // ---- this wave's Q rows as the B operand: lane -> (row ln, d = 16 s + 8 g .. +7)
+  u32x4 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = qi < Sq ? load16(Q + (size_t)qi * D + 16 * s + 8 * g) : zero_u32x4();
+
+  float slope_l2 = 0.f;
+  if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
+
+  floatx16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = floatx16{};
+  float m_run = kNegInf;  // running reference max (log2 units)
+  float l_part = 0.f;     // running denominator over this lane's keys
+
+  // ---- K/V staging: global -> registers -> LDS
+  u32x4 kr[CPT], vr[CPT];
+  auto gload = [&](int t) {
+    const int n0 = t * kBN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads * i;
+      const int key = n0 + c / NC;
+      const int cc = c % NC;
+      if (key < Sk) {
+        kr[i] = load16(K + (size_t)key * D + cc * 8);
+        vr[i] = load16(V + (size_t)key * D + cc * 8);
+      } else {
+        kr[i] = zero_u32x4();
+        vr[i] = zero_u32x4();
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / NC, cc = c % NC;
+      smem[buf][0][r * NC + (cc ^ swz_k<D>(r))] = kr[i];
+      smem[buf][1][r * NC + (cc ^ swz_v<D>(r))] = vr[i];
+    }
+  };
+
+  if (t_begin < t_end) gload(t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    lstore(buf);
+    __syncthreads();
+    if (t + 1 < t_end) gload(t + 1);
+    const int n0 = t * kBN;
+    if (!(wave_live && n0 < w_hi && n0 + kBN > w_lo)) continue;  // wave-uniform
+
+    const u32x4* Ks = smem[buf][0];
+    const T* Vs = reinterpret_cast<const T*>(smem[buf][1]);
+
+    // ---- S^T = K Q^T for keys [n0, n0+32) and [n0+32, n0+64)
+    floatx16 sc[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = 2 * s + g;
+      sc[0] = E::mma32(Ks[ln * NC + (c ^ swz_k<D>(ln))], qf[s], sc[0]);
+      sc[1] = E::mma32(Ks[(32 + ln) * NC + (c ^ swz_k<D>(32 + ln))], qf[s], sc[1]);
+    }
+
+    // ---- score transform (log2 units) and mask
+    constexpr bool kRaw = !SOFTCAP && !ALIBI;  // max on raw scores, scale folded into exp
+    const int rb = n0 + 4 * g - ip;            // j - i' of element offset 0
+    if constexpr (!kRaw) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sc[kb][r];
+          if constexpr (SOFTCAP) {
+            const float e = fast_exp2(x * a.c_score);
+            x = a.c_cap - 2.f * a.c_cap * fast_rcp(1.f + e);
+          } else {
+            x *= a.c_score;
+          }
+          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(rb + key_of(kb, r)), x);
+          sc[kb][r] = x;
+        }
+    }
+    if constexpr (MASK) {
+      const bool full = n0 + kBN <= Sk && (!a.has_hi || n0 + kBN - 1 - ipa_w <= a.dmax) &&
+                        (a.wl < 0 || ipb_w - n0 <= a.wl);
+      if (!full) {
+        // admissible iff lo <= j - i' <= hi, with j < Sk folded into hi
+        int hi = Sk - 1 - ip;
+        if (a.has_hi) hi = min(hi, a.dmax);
+        int lo = -ip;  // j >= 0
+        if (a.wl >= 0) lo = max(lo, -a.wl);
+        int klo = max(lo - rb, 0), khi = min(hi - rb, kBN - 1);
+        if (khi < klo) klo = khi = kBN;
+        const uint32_t span = (uint32_t)(khi - klo);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((uint32_t)(key_of(kb, r) - klo) > span) sc[kb][r] = kNegInf;
+      }
+    }
+
+    // ---- row max: 32 values in-lane, then the other half of the keys
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[kb][r], sc[kb][r + 1]));
+    float mt = mx;
+    if constexpr (kRaw) mt = mx == kNegInf ? kNegInf : mx * a.c_score;
+    mt = halves_max(mt);
+
+    // ---- raise the reference max only when the tile exceeds it by > 2^8
+    const bool need = mt > m_run + kRescaleGap;
+    if (wave_any(need)) {
+      const float alpha = need ? fast_exp2(m_run - mt) : 1.f;
+      m_run = need ? mt : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+
+    // ---- weights, rounded to the input type, packed as the PV B operand
+    uint32_t pp[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0, p1;
+        if constexpr (kRaw) {
+          p0 = fast_exp2(__builtin_fmaf(sc[kb][r], a.c_score, -m_use));
+          p1 = fast_exp2(__builtin_fmaf(sc[kb][r + 1], a.c_score, -m_use));
+        } else {
+          p0 = fast_exp2(sc[kb][r] - m_use);
+          p1 = fast_exp2(sc[kb][r + 1] - m_use);
+        }
+        const uint32_t pk = E::pack2(p0, p1);
+        pp[kb * 8 + r / 2] = pk;
+        l_part = E::dot2(pk, E::kOnePair, l_part);
+      }
+
+    // ---- O^T += V^T P^T, 16 keys per step
+    const int trow = 4 * g + ((lane & 15) >> 2);         // key row within a 16-key step
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d within a 32-row block
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 pf = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
+      const int r0 = 16 * ks + trow;
+      const int sw = swz_v<D>(r0);  // same for r0 + 8
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = 32 * db + tcol;
+        const int cidx = ((col >> 3) ^ sw) * 8 + (col & 7);
+        const u32x2 lo = lds_read_tr16(Vs + r0 * D + cidx);
+        const u32x2 hi = lds_read_tr16(Vs + (r0 + 8) * D + cidx);
+        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+        o[db] = E::mma32(va, pf, o[db]);
+      }
+    }
+  }
+
+  // ---- epilogue: O = o / l (0 when no key was admissible)
+  const float l = halves_sum(l_part);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (qi < Sq) {
+    T* orow = O + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = E::pack2(o[db][4 * j] * inv, o[db][4 * j + 1] * inv);
+        w[1] = E::pack2(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * j + 4 * g) = w;
+      }
+  }
+}
+
+template <int FLAGS>
+hipError_t launch_flags(const FwdArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_mfma_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t stream) {
+  FwdArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.alibi = p.alibi;
+  a.out = p.out;
+  a.Sq = p.Sq;
+  a.Sk = p.Sk;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.group = p.Hq / p.Hkv;
+  a.nbh = p.B * p.Hq;
+  a.nqb = (p.Sq + kBM - 1) / kBM;
+  a.heavy_first = p.causal;
+  a.wl = p.wl;
+  a.has_hi = p.causal || p.wr >= 0;
+  a.dmax = p.causal ? (p.wr >= 0 ? min(p.wr, 0) : 0) : p.wr;
+  const bool softcap = p.softcap > 0.f;
+  a.c_score = softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
+  a.c_cap = kLog2e * p.softcap;
+  const int grid = a.nqb * a.nbh;
+  const bool mask = p.causal || p.wl >= 0 || p.wr >= 0 || (p.Sk % kBN) != 0;
+  const int flags = (mask ? F_MASK : 0) | (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0);
+  switch (flags) {
+    case 0: return launch_flags<0>(a, grid, stream);
+    case 1: return launch_flags<1>(a, grid, stream);
+    case 2: return launch_flags<2>(a, grid, stream);
+    case 3: return launch_flags<3>(a, grid, stream);
+    case 4: return launch_flags<4>(a, grid, stream);
+    case 5: return launch_flags<5>(a, grid, stream);
+    case 6: return launch_flags<6>(a, grid, stream);
+    default: return launch_flags<7>(a, grid, stream);
+  }
+}
+
+}  // namespace attn

@@ -1,0 +1,48 @@
+// launch.h -- internal interface between the C ABI (attn_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Dense forward problem, sizes narrowed to int after validation.
+struct FwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alibi;  // [Hq] float32 or nullptr
+  void* out;
+  int B, Hq, Hkv, Sq, Sk, D;
+  int causal;
+  int wl, wr;     // window; -1 = unbounded (already clamped to the useful range)
+  float scale;    // softmax scale
+  float softcap;  // 0 = off
+};
+
+// Paged decode problem.
+struct DecodeProblem {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* alibi;
+  void* out;
+  float* ws_o;    // [B, Hq, splits, D] float32 partial outputs
+  float* ws_lse;  // [B, Hq, splits] float32 log-sum-exp (natural log)
+  int32_t* error_flag;
+  int B, Hq, Hkv, D;
+  int num_blocks, block_size, max_blocks;
+  int splits;
+  float scale;
+  float softcap;
+};
+
+// 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
+hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,175 @@
+"""The C ABI without a GPU: library load, exported symbols, host-only checks.
+
+Only the ``*_check`` validators, the workspace-size query and the status
+strings are called here; they make no HIP call.  Pointers are fake aligned
+addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_amd as sdpa
+from scaled_dot_product_amd import attn_fwd_params_t, attn_paged_params_t
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK = 0
+NULL, DTYPE, SHAPE, GQA, HEAD_DIM, PARAM, ALIGN, ALIAS, WORKSPACE, UNSUPPORTED = range(1, 11)
+
+# Fake, 16-byte aligned, well separated device addresses.
+Q, K, V, AL, OUT, KP, VP, TAB, LEN, WS, ERR = (0x100000000 * (i + 1) for i in range(11))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = sdpa.library()
+    names = declared_functions()
+    assert {"attn_fwd", "attn_fwd_check", "attn_paged_decode", "attn_paged_decode_check",
+            "attn_paged_decode_workspace_size", "attn_status_str", "attn_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libattn.so does not export {n}"
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_binding_names_match_the_header():
+    for n in declared_functions():
+        assert callable(getattr(sdpa, n)), n
+
+
+def test_status_strings_and_version():
+    assert sdpa.attn_status_str(0) == "ok"
+    for code in range(1, 12):
+        assert sdpa.attn_status_str(code) not in ("ok", "unknown status")
+    assert sdpa.attn_status_str(99) == "unknown status"
+    assert sdpa.attn_version() >= 100
+
+
+def fwd(**kw):
+    base = dict(B=2, Hq=8, Hkv=2, Sq=100, Sk=130, D=128, dtype=sdpa.ATTN_BF16, causal=1,
+                window_left=-1, window_right=-1, softmax_scale=0.125, softcap=0.0)
+    base.update(kw)
+    return attn_fwd_params_t(**base)
+
+
+def check_fwd(p, q=Q, k=K, v=V, al=None, out=OUT):
+    return sdpa.attn_fwd_check(q, k, v, al, out, p)
+
+
+def test_fwd_check_accepts_valid_calls():
+    assert check_fwd(fwd()) == OK
+    assert check_fwd(fwd(D=64, dtype=sdpa.ATTN_F16, causal=0, window_left=5, window_right=0,
+                         softcap=30.0), al=AL) == OK
+    assert check_fwd(fwd(dtype=sdpa.ATTN_F32)) == OK
+    assert check_fwd(fwd(Hkv=8)) == OK
+
+
+def test_fwd_check_empty_tensors_may_be_null():
+    assert check_fwd(fwd(Sq=0), q=None, out=None) == OK
+    assert check_fwd(fwd(Sk=0), k=None, v=None) == OK
+    assert check_fwd(fwd(B=0), q=None, k=None, v=None, out=None) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), DTYPE),
+    (dict(B=-1), SHAPE), (dict(Sq=-2), SHAPE), (dict(Sk=-1), SHAPE),
+    (dict(Sq=(1 << 30) + 1), SHAPE),
+    (dict(Hkv=3), GQA), (dict(Hkv=0), GQA),
+    (dict(D=96), HEAD_DIM), (dict(D=256), HEAD_DIM),
+    (dict(softmax_scale=float("nan")), PARAM), (dict(softmax_scale=-1.0), PARAM),
+    (dict(softcap=-0.5), PARAM), (dict(softcap=float("inf")), PARAM),
+    (dict(window_left=-2), PARAM), (dict(window_right=-5), PARAM),
+])
+def test_fwd_check_rejects(kw, code):
+    assert check_fwd(fwd(**kw)) == code
+
+
+def test_fwd_check_pointers():
+    assert check_fwd(fwd(), q=None) == NULL
+    assert check_fwd(fwd(), out=None) == NULL
+    assert check_fwd(fwd(), v=None) == NULL
+    assert sdpa.attn_fwd_check(Q, K, V, None, OUT, None) == NULL
+    assert check_fwd(fwd(), k=K + 8) == ALIGN
+    assert check_fwd(fwd(), al=AL + 4) == ALIGN
+    assert check_fwd(fwd(), out=Q) == ALIAS                # out == q
+    assert check_fwd(fwd(), out=K + 4096) == ALIAS         # out inside k
+    assert check_fwd(fwd(), al=OUT + 16) == ALIAS          # slopes inside out
+
+
+def test_fwd_invalid_call_returns_before_any_launch():
+    # attn_fwd validates first; on this GPU-less host nothing must be launched.
+    lib = sdpa.library()
+    p = fwd(D=80)
+    assert lib.attn_fwd(Q, K, V, None, OUT, ctypes.byref(p), None) == HEAD_DIM
+    p = fwd(Sq=0)
+    assert lib.attn_fwd(None, K, V, None, None, ctypes.byref(p), None) == OK  # nothing to do
+
+
+def paged(**kw):
+    base = dict(B=4, Hq=32, Hkv=8, D=128, num_blocks=40, block_size=64, max_blocks_per_seq=10,
+                dtype=sdpa.ATTN_BF16, num_splits=8, softmax_scale=0.088, softcap=0.0)
+    base.update(kw)
+    return attn_paged_params_t(**base)
+
+
+def check_paged(p, ws_bytes=None, **ptrs):
+    args = dict(q=Q, k=KP, v=VP, tab=TAB, lens=LEN, al=None, out=OUT, ws=WS, err=None)
+    args.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = sdpa.attn_paged_decode_workspace_size(p)
+    return sdpa.attn_paged_decode_check(args["q"], args["k"], args["v"], args["tab"],
+                                        args["lens"], args["al"], args["out"], args["ws"],
+                                        ws_bytes, args["err"], p)
+
+
+def test_workspace_size():
+    p = paged()
+    o_bytes = 4 * 32 * 8 * 128 * 4
+    lse_off = (o_bytes + 255) // 256 * 256
+    assert sdpa.attn_paged_decode_workspace_size(p) == lse_off + 4 * 32 * 8 * 4
+    assert sdpa.attn_paged_decode_workspace_size(paged(num_splits=0)) == 0
+    assert sdpa.attn_paged_decode_workspace_size(paged(D=100)) == 0
+
+
+def test_paged_check_accepts_valid_calls():
+    assert check_paged(paged()) == OK
+    assert check_paged(paged(D=64, dtype=sdpa.ATTN_F16, block_size=16, num_splits=1,
+                             softcap=20.0), al=AL, err=ERR) == OK
+    assert check_paged(paged(Hkv=32, num_splits=256)) == OK
+    assert check_paged(paged(B=0), q=None, out=None, tab=None, lens=None, ws=None) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), DTYPE), (dict(dtype=sdpa.ATTN_F32), UNSUPPORTED),
+    (dict(B=-1), SHAPE), (dict(block_size=0), SHAPE), (dict(B=70000), SHAPE),
+    (dict(max_blocks_per_seq=1 << 30), SHAPE),
+    (dict(Hkv=5), GQA), (dict(D=32), HEAD_DIM),
+    (dict(num_splits=0), PARAM), (dict(num_splits=257), PARAM),
+    (dict(softmax_scale=float("inf")), PARAM), (dict(softcap=-1.0), PARAM),
+])
+def test_paged_check_rejects(kw, code):
+    assert check_paged(paged(**kw)) == code
+
+
+def test_paged_check_pointers_and_workspace():
+    p = paged()
+    need = sdpa.attn_paged_decode_workspace_size(p)
+    assert check_paged(p, q=None) == NULL
+    assert check_paged(p, tab=None) == NULL
+    assert check_paged(p, lens=None) == NULL
+    assert check_paged(p, k=None) == NULL
+    assert check_paged(p, ws=None) == WORKSPACE
+    assert check_paged(p, ws_bytes=need - 1) == WORKSPACE
+    assert check_paged(p, tab=TAB + 4) == ALIGN
+    assert check_paged(p, err=ERR + 2) == ALIGN
+    assert check_paged(p, out=KP + 256) == ALIAS
+    assert check_paged(p, ws=LEN) == ALIAS
+    assert check_paged(p, err=WS + 64) == ALIAS
+    assert check_paged(p, out=WS + 1024) == ALIAS

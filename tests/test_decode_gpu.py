@@ -1,0 +1,179 @@
+"""Parity of attn_paged_decode (HIP, through the C ABI) with the paged oracle.
+
+Includes a bit-exact check of the integer paging (one-hot scores make the
+output the V row of a single logical token, which encodes its (sequence,
+position) in bf16-exact integers), the device-side error flag, and bitwise
+rerun determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import announce, compare
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+DEV = torch.device("cuda:0")
+
+
+def gpu_decode(sdpa, q, kp, vp, table, lens, alibi=None, **kw):
+    out = sdpa.attn_paged_decode(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens.to(DEV),
+                                 None if alibi is None else alibi.to(DEV), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(q, kp, vp, table, lens, alibi=None, **kw):
+    return oracle.paged_decode_f64(W.to_f64(q), W.to_f64(kp), W.to_f64(vp), table.numpy(),
+                                   lens.numpy(), alibi=None if alibi is None else W.to_f64(alibi),
+                                   **kw)
+
+
+CASES = [
+    # dtype, B, Hq, Hkv, D, block_size, lens, splits, softcap, alibi
+    ("bf16", 5, 8, 2, 128, 16, [0, 1, 17, 64, 300], 3, None, False),
+    ("bf16", 3, 32, 8, 128, 64, [512, 1000, 77], 8, None, False),
+    ("f16", 4, 4, 4, 64, 7, [5, 50, 123, 13], 2, None, False),
+    ("bf16", 2, 16, 1, 64, 1, [9, 40], 1, None, False),
+    ("f16", 3, 6, 2, 128, 32, [200, 31, 97], 5, 10.0, True),
+    ("bf16", 2, 32, 1, 128, 16, [333, 129], 4, None, True),
+    ("bf16", 2, 24, 8, 64, 64, [700, 64], 8, 30.0, False),
+    ("bf16", 3, 10, 5, 128, 48, [1, 480, 481], 16, None, False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_paged_parity(gpu_lib, case):
+    dtype, B, Hq, Hkv, D, bs, lens, splits, cap, use_alibi = CASES[case]
+    maxb = max((max(lens) + bs - 1) // bs, 1) + 1
+    w = W.Paged("t", dtype, B, Hq, Hkv, D, bs, 0, 0, splits, maxb, seed=200 + case)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    alibi = torch.from_numpy(W.alibi_slopes(Hq)) if use_alibi else None
+    scale = D ** -0.5
+    announce(f"paged decode case {case}: {CASES[case]}")
+    out = gpu_decode(gpu_lib, q, kp, vp, table, sl, alibi, softmax_scale=scale, softcap=cap,
+                     num_splits=splits)
+    ref = oracle_decode(q, kp, vp, table, sl, alibi, scale=scale, softcap=cap)
+    compare(out, ref, DT[dtype], f"paged case {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
+def test_paged_decode_workload(gpu_lib):
+    w = W.PAGED_DECODE
+    q, kp, vp, table, lens, _ = W.paged_inputs(w)
+    announce(w.name)
+    out = gpu_decode(gpu_lib, q, kp, vp, table, lens, softmax_scale=w.scale,
+                     num_splits=w.num_splits)
+    ref = oracle_decode(q, kp, vp, table, lens, scale=w.scale)
+    compare(out, ref, torch.bfloat16, w.name)
+
+
+@pytest.mark.parametrize("bs,splits", [(64, 8), (16, 3), (5, 1)])
+def test_paging_is_bit_exact(gpu_lib, bs, splits):
+    """One-hot scores: q = 1024 e0 in every head and a single key row equal to
+    8 e0 give that key a score of 1024 * 8 / sqrt(128) ~ 724 and every other
+    key 0, so exp underflows to exactly 0 elsewhere and the output is exactly
+    the V row of that logical token.  V rows hold (sequence, position % 128,
+    position // 128, kv head) as bf16-exact integers; slots no table entry
+    points at hold a finite sentinel so that a stray read is visible."""
+    B, Hq, Hkv, D = 4, 8, 2, 128
+    lens = [130, 64, 7, 200]
+    rng = np.random.default_rng(5)
+    maxb = (max(lens) + bs - 1) // bs + 1
+    table_np, nb = W.paged_layout(np.array(lens), bs, maxb, rng)
+    nb_pool = nb + 3                        # three blocks nobody references
+    kp = torch.zeros(nb_pool, bs, Hkv, D, dtype=torch.bfloat16)
+    vp = torch.full((nb_pool, bs, Hkv, D), 1e4, dtype=torch.bfloat16)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            blk, slot = table_np[b, t // bs], t % bs
+            for g in range(Hkv):
+                vp[blk, slot, g, :4] = torch.tensor([b, t % 128, t // 128, g], dtype=torch.bfloat16)
+                vp[blk, slot, g, 4:] = 0
+    q = torch.zeros(B, Hq, 1, D, dtype=torch.bfloat16)
+    q[..., 0] = 1024.0
+    table = torch.from_numpy(table_np)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    dq, dt, dsl = q.to(DEV), table.to(DEV), sl.to(DEV)
+    dvp = vp.to(DEV)
+    for frac in (0.0, 0.3, 0.5, 0.99, 1.0):
+        kp.zero_()
+        targets = []
+        for b, n in enumerate(lens):
+            t = min(n - 1, int(frac * n))
+            targets.append(t)
+            kp[table_np[b, t // bs], t % bs, :, 0] = 8.0
+        announce(f"one-hot paging bs={bs} splits={splits} frac={frac}")
+        out = gpu_lib.attn_paged_decode(dq, kp.to(DEV), dvp, dt, dsl, num_splits=splits)
+        torch.cuda.synchronize()
+        out = out.cpu()
+        for b, t in enumerate(targets):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                want = torch.tensor([b, t % 128, t // 128, g] + [0] * (D - 4), dtype=torch.bfloat16)
+                assert torch.equal(out[b, h, 0], want), (b, h, t)
+
+
+def test_error_flag_and_masking(gpu_lib):
+    w = W.Paged("e", "bf16", 3, 8, 2, 128, 16, 0, 0, 4, 8, seed=9)
+    lens = [40, 100, 33]
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce("error flag: valid call")
+    gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
+    assert flag.item() == 0
+    bad = table.clone()
+    bad[1, 2] = 10 ** 6                      # keys 32..47 of sequence 1 are masked
+    announce("error flag: block id out of range")
+    out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag, num_splits=4)
+    assert flag.item() == 1
+    assert torch.isfinite(out.float()).all()
+    # The other sequences are unaffected; sequence 1 equals attention without keys 32..47.
+    ref = oracle_decode(q, kp, vp, table, sl, scale=128 ** -0.5)
+    compare(out[[0, 2]], ref[[0, 2]], torch.bfloat16, "unaffected sequences")
+    keep = [t for t in range(100) if not 32 <= t < 48]
+    kb = oracle.paged_gather(W.to_f64(kp), table.numpy(), 100, 1, 16)[keep]
+    vb = oracle.paged_gather(W.to_f64(vp), table.numpy(), 100, 1, 16)[keep]
+    r1 = oracle.sdpa_naive_f64(W.to_f64(q[1:2]), kb.transpose(1, 0, 2)[None],
+                               vb.transpose(1, 0, 2)[None], scale=128 ** -0.5)
+    compare(out[1:2], r1, torch.bfloat16, "masked keys")
+    flag.zero_()
+    long = sl.clone()
+    long[2] = 8 * 16 + 5                     # beyond the table's capacity: clamped
+    announce("error flag: seq_len beyond capacity")
+    gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag, num_splits=4)
+    assert flag.item() == 1
+
+
+def test_decode_rerun_is_bitwise_identical(gpu_lib):
+    w = W.Paged("d", "bf16", 8, 32, 8, 128, 64, 100, 3000, 8, 48, seed=10)
+    q, kp, vp, table, lens, _ = W.paged_inputs(w)
+    q, kp, vp, table, lens = (x.to(DEV) for x in (q, kp, vp, table, lens))
+    announce("decode determinism")
+    a = gpu_lib.attn_paged_decode(q, kp, vp, table, lens)
+    b = gpu_lib.attn_paged_decode(q, kp, vp, table, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_equals_dense_prefill_path(gpu_lib):
+    """A contiguous, identity-paged cache decodes to what attn_fwd gives for
+    the same single query (both HIP paths, checked against the oracle)."""
+    B, Hq, Hkv, D, S, bs = 2, 8, 2, 128, 256, 64
+    q, k, v = W.random_dense("bf16", B, Hq, Hkv, 1, S, D, 21)
+    kp = k.permute(0, 2, 1, 3).reshape(B * S // bs, bs, Hkv, D).contiguous()
+    vp = v.permute(0, 2, 1, 3).reshape(B * S // bs, bs, Hkv, D).contiguous()
+    table = torch.arange(B * S // bs, dtype=torch.int32).reshape(B, S // bs)
+    lens = torch.full((B,), S, dtype=torch.int32)
+    announce("decode vs dense")
+    dec = gpu_decode(gpu_lib, q, kp, vp, table, lens)
+    dense = gpu_lib.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_naive_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale=D ** -0.5)
+    compare(dec, ref, torch.bfloat16, "decode")
+    compare(dense, ref, torch.bfloat16, "dense")

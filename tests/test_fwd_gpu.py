@@ -1,0 +1,206 @@
+"""Parity of attn_fwd (HIP, through the C ABI) with the float64 oracle.
+
+Small cases span several 128-row / 64-key tiles with ragged tails and every
+mask combination; the full-size workloads are checked on sampled heads (all
+rows of each sampled head), in the launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import announce, compare
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def gpu_fwd(sdpa, q, k, v, alibi, **kw):
+    dev = torch.device("cuda:0")
+    out = sdpa.attn_fwd(q.to(dev), k.to(dev), v.to(dev),
+                        None if alibi is None else alibi.to(dev), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_heads(q, k, v, alibi, heads, **kw):
+    """Oracle output for the sampled (b, h) pairs, stacked [n, Sq, D]."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    res = []
+    for b, h in heads:
+        g = oracle.kv_head_of(h, Hq, Hkv)
+        sl = None if alibi is None else W.to_f64(alibi)[h:h + 1]
+        res.append(oracle.sdpa_naive_f64(W.to_f64(q[b:b + 1, h:h + 1]), W.to_f64(k[b:b + 1, g:g + 1]),
+                                         W.to_f64(v[b:b + 1, g:g + 1]), alibi=sl, **kw)[0, 0])
+    return np.stack(res)
+
+
+def run_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None,
+             softcap=None, alibi=False, amp=1.0, seed=0, heads=None):
+    name = (f"attn_fwd {dtype} B{B} H{Hq}/{Hkv} Sq{Sq} Sk{Sk} D{D} causal={causal} "
+            f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
+    q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
+    sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
+    kw = dict(scale=1.0 / math.sqrt(D), causal=causal, window_left=wl, window_right=wr,
+              softcap=softcap)
+    announce(name)
+    out = gpu_fwd(sdpa, q, k, v, sl, softmax_scale=kw["scale"], causal=causal,
+                  window_left=wl, window_right=wr, softcap=softcap)
+    if heads is None:
+        ref = oracle.sdpa_naive_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v),
+                                    alibi=None if sl is None else W.to_f64(sl), **kw)
+        compare(out, ref, DT[dtype], name)
+    else:
+        ref = oracle_heads(q, k, v, sl, heads, **kw)
+        got = torch.stack([out[b, h] for b, h in heads])
+        compare(got, ref, DT[dtype], name)
+    return out
+
+
+SMALL = [
+    # (B, Hq, Hkv, Sq, Sk, kwargs)
+    (1, 2, 2, 256, 256, dict()),
+    (2, 2, 1, 300, 333, dict()),
+    (1, 4, 2, 300, 300, dict(causal=True)),
+    (2, 4, 1, 200, 517, dict(causal=True)),
+    (1, 2, 2, 517, 200, dict(causal=True)),
+    (1, 4, 4, 333, 333, dict(causal=True, wl=37, wr=0)),
+    (1, 2, 1, 270, 290, dict(wl=50, wr=20)),
+    (1, 2, 2, 190, 190, dict(softcap=5.0, amp=3.0)),
+    (1, 4, 2, 300, 300, dict(causal=True, alibi=True)),
+    (2, 8, 2, 257, 385, dict(causal=True, wl=100, wr=0, softcap=20.0, alibi=True, amp=1.5)),
+    (1, 16, 2, 129, 129, dict(causal=True)),
+    (1, 2, 2, 64, 1000, dict(wl=10, wr=3, alibi=True)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_parity(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = SMALL[case]
+    run_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=100 + case, **kw)
+
+
+@pytest.mark.parametrize("case", [
+    (1, 4, 4, 128, 128, 64, dict()),
+    (1, 4, 2, 200, 250, 128, dict(causal=True)),
+    (2, 2, 1, 150, 150, 64, dict(causal=True, wl=30, wr=0, softcap=8.0, alibi=True)),
+    (1, 2, 2, 100, 70, 128, dict(wl=5, wr=9)),
+])
+def test_f32_parity(gpu_lib, case):
+    B, Hq, Hkv, Sq, Sk, D, kw = case
+    run_case(gpu_lib, "f32", B, Hq, Hkv, Sq, Sk, D, seed=7, **kw)
+
+
+def test_tiny_f32_workload(gpu_lib):
+    w = W.TINY_F32
+    q, k, v, _ = W.dense_inputs(w)
+    announce(w.name)
+    out = gpu_fwd(gpu_lib, q, k, v, None, softmax_scale=w.scale)
+    ref = oracle.sdpa_naive_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale=w.scale)
+    compare(out, ref, torch.float32, w.name)
+
+
+def _workload_heads(sdpa, w, sample):
+    q, k, v, sl = W.dense_inputs(w)
+    announce(w.name)
+    out = gpu_fwd(sdpa, q, k, v, sl, softmax_scale=w.scale, causal=w.causal,
+                  window_left=w.window_left, window_right=w.window_right, softcap=w.softcap)
+    ref = oracle_heads(q, k, v, sl, sample, scale=w.scale, causal=w.causal,
+                       window_left=w.window_left, window_right=w.window_right, softcap=w.softcap)
+    compare(torch.stack([out[b, h] for b, h in sample]), ref, DT[w.dtype], w.name)
+    return out
+
+
+def test_gqa_causal_2k_workload(gpu_lib):
+    _workload_heads(gpu_lib, W.GQA_CAUSAL_2K, [(0, 0), (0, 5), (0, 31), (1, 12), (1, 27)])
+
+
+def test_masked_rows_workload(gpu_lib):
+    w = W.GQA_MASKED_ROWS
+    out = _workload_heads(gpu_lib, w, [(0, 0), (1, 30)])
+    # Rows 0..63 have no admissible key in every head: exactly zero.
+    assert torch.count_nonzero(out[:, :, :64]).item() == 0
+    assert torch.count_nonzero(out[:, :, 64:].float().abs().sum(-1) == 0).item() == 0
+
+
+def test_long_masked_8k_workload(gpu_lib):
+    _workload_heads(gpu_lib, W.LONG_MASKED_8K, [(0, 0), (0, 17), (0, 31)])
+
+
+def test_chunked_prefill_workload(gpu_lib):
+    w = W.CHUNKED_PREFILL
+    _workload_heads(gpu_lib, w, [(b, h) for b in range(w.B) for h in (0, 7, 15)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_single_admissible_key_is_exact(gpu_lib, dtype):
+    """Window (0, 0): weight exactly 1 on key i', so out == V row bit for bit."""
+    q, k, v = W.random_dense(dtype, 1, 4, 2, 200, 200, 128, 11)
+    announce(f"single key {dtype}")
+    out = gpu_fwd(gpu_lib, q, k, v, None, window_left=0, window_right=0)
+    ref = torch.repeat_interleave(v, 2, dim=1)
+    assert torch.equal(out.cpu(), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_constant_v_is_exact(gpu_lib, dtype):
+    q, k, _ = W.random_dense(dtype, 1, 4, 2, 300, 300, 64, 12, amp=2.0)
+    v = torch.full((1, 2, 300, 64), 0.25, dtype=DT[dtype])
+    sl = torch.from_numpy(W.alibi_slopes(4))
+    announce(f"constant v {dtype}")
+    out = gpu_fwd(gpu_lib, q, k, v, sl, causal=True, window_left=40, softcap=10.0)
+    assert torch.all(out.cpu() == 0.25)
+
+
+def test_empty_extents(gpu_lib):
+    q, k, v = W.random_dense("bf16", 1, 2, 2, 70, 0, 128, 13)
+    announce("Sk = 0")
+    out = gpu_fwd(gpu_lib, q, k, v, None, causal=True)
+    assert torch.count_nonzero(out).item() == 0
+    q, k, v = W.random_dense("bf16", 1, 2, 2, 0, 50, 128, 13)
+    announce("Sq = 0")
+    out = gpu_fwd(gpu_lib, q, k, v, None)
+    assert out.shape == (1, 2, 0, 128)
+
+
+def test_gqa_equals_repeated_mha_bitwise(gpu_lib):
+    q, k, v = W.random_dense("bf16", 1, 8, 2, 260, 260, 128, 14)
+    announce("gqa vs mha")
+    a = gpu_fwd(gpu_lib, q, k, v, None, causal=True)
+    b = gpu_fwd(gpu_lib, q, torch.repeat_interleave(k, 4, 1), torch.repeat_interleave(v, 4, 1),
+                None, causal=True)
+    assert torch.equal(a, b)
+
+
+def test_rerun_is_bitwise_identical(gpu_lib):
+    w = W.GQA_CAUSAL_2K
+    q, k, v, _ = W.dense_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    announce("rerun determinism")
+    a = gpu_lib.attn_fwd(q, k, v, causal=True)
+    b = gpu_lib.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_binding_rejects_bad_arguments(gpu_lib):
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 3, 8, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(gpu_lib.AttnError) as e:
+        gpu_lib.attn_fwd(q, k, k)
+    assert e.value.status == 4
+    with pytest.raises(ValueError):
+        gpu_lib.attn_fwd(q, q.half(), q)
+    with pytest.raises(ValueError):
+        gpu_lib.attn_fwd(q, q.transpose(2, 3).contiguous().transpose(2, 3), q)
+    with pytest.raises(gpu_lib.AttnError) as e:
+        gpu_lib.attn_fwd(q[..., :96].contiguous(), q[..., :96].contiguous(), q[..., :96].contiguous())
+    assert e.value.status == 5
