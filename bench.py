@@ -261,20 +261,26 @@ def profile(args):
 
 
 def summarize(path):
-    """Print the per-kernel duration table of a rocprofv3 --stats run."""
-    files = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        sys.exit(f"no kernel_stats.csv under {path}")
-    for fn in files:
-        print(f"# {os.path.relpath(fn, path)}")
+    """Print the per-kernel duration table of a rocprofv3 kernel-trace run
+    (its SQLite database, or the CSV stats when it wrote those)."""
+    dbs = glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
+    csvs = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    if not dbs and not csvs:
+        sys.exit(f"no rocprofv3 output under {path}")
+    print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel")
+    for fn in dbs:
+        import sqlite3
+        con = sqlite3.connect(fn)
+        rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration) "
+                           "from kernels group by name order by sum(duration) desc").fetchall()
+        for name, n, avg, lo, hi in rows:
+            print(f"{n:>6} {avg / 1e3:>10.2f} {lo / 1e3:>10.2f} {hi / 1e3:>10.2f}  {name[:160]}")
+    for fn in csvs:
         with open(fn) as f:
-            rows = list(csv.DictReader(f))
-        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
-        for r in rows:
-            name = r.get("Name", "?")
-            print(f"{int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
-                  f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} {float(r.get('MaxNs', 0)) / 1e3:>10.2f} "
-                  f"{float(r.get('Percentage', 0)):>6.2f}  {name[:150]}")
+            for r in csv.DictReader(f):
+                print(f"{int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
+                      f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} "
+                      f"{float(r.get('MaxNs', 0)) / 1e3:>10.2f}  {r.get('Name', '?')[:160]}")
 
 
 def main():
