@@ -28,14 +28,19 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
-# (source, extra defines, object)
+# Kernels may assume NaN-free scores (lets max() skip NaN canonicalisation);
+# the host-side argument checks must not, so attn_api.cpp is built without it.
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+# (source, extra flags, object)
 UNITS = [("attn_api.cpp", [], "attn_api.o"),
-         ("fwd_f32.hip", [], "fwd_f32.o"),
-         ("decode.hip", [], "decode.o")]
+         ("fwd_f32.hip", KERNEL_FLAGS, "fwd_f32.o"),
+         ("decode.hip", KERNEL_FLAGS, "decode.o")]
 for _elem, _tag in (("__bf16", "bf16"), ("_Float16", "f16")):
     for _d in (128, 64):
         UNITS.append(("fwd_mfma.hip",
-                      [f"-DATTN_ELEM={_elem}", f"-DATTN_D={_d}", f"-DATTN_TAG={_tag}_d{_d}"],
+                      KERNEL_FLAGS + [f"-DATTN_ELEM={_elem}", f"-DATTN_D={_d}",
+                                      f"-DATTN_TAG={_tag}_d{_d}"],
                       f"fwd_mfma_{_tag}_d{_d}.o"))
 
 

@@ -14,13 +14,22 @@
 //   * The split's tokens are cut into 16-token blocks dealt round-robin to the
 //     4 waves; every wave keeps its own online-softmax state, so there is no
 //     barrier until the final 4-way merge through LDS.
-//   * Scores for all query heads of the KV head at once on the 16x16x32
-//     matrix instruction: Q (up to 16 heads, padded) is the A operand, 16
-//     gathered key rows the B operand, loaded straight from the pool (each
-//     token row is 16 B per lane, 64 contiguous bytes per 4 lanes).
-//   * P V on the vector ALU: each lane owns one 16-byte d-chunk of a few
-//     tokens (V rows loaded whole and coalesced), the weights reach it through
-//     a small per-wave LDS slab.
+//   * Both products run on the matrix cores with the query heads of the KV
+//     head as the N dimension (up to 16 per workgroup, padded):
+//       S^T = K Q^T    16x16x32, gathered key rows as the A operand straight
+//                      from the pool (64 contiguous bytes per 4 lanes);
+//       O^T += V^T P^T 16x16x16, where the S^T accumulator (4 tokens of one
+//                      head per lane) is already the P^T operand and V^T comes
+//                      from a per-wave LDS block through the transpose read.
+//     Every lane therefore owns one head: softmax state, rescale and output
+//     need no cross-lane reduction except the block max over 4 lane groups.
+//   * Loads run PF blocks ahead in a register ring.  When every 16-token block
+//     lies inside one KV block (block_size % 16 == 0) the physical block of a
+//     whole block is one wave-uniform value: a wave reads the page ids of its
+//     next 64 blocks in one load and broadcasts them with readlane, and the
+//     loads go through a buffer descriptor whose size ends at the split's last
+//     live token (later rows read as zero, no branches).  Other block sizes
+//     translate every token separately.
 //   * Output per (sequence, head, split): normalised partial o[D] and its
 //     natural-log LSE, into the caller's workspace.
 // Merge kernel: one workgroup per (sequence, head), splits combined in fixed
@@ -33,9 +42,8 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kTB = 16;  // tokens per block
+constexpr int kTB = 16;         // tokens per block
+constexpr int kPageWindow = 63; // blocks per page-id window: <= 64 lanes, a multiple of the ring size
 constexpr float kRescaleGap = 8.0f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -55,47 +63,89 @@ struct DecArgs {
   float c_cap;    // log2(e) * cap
 };
 
-// All-reduce over each row of 16 lanes (rotations by 8, 4, 2, 1).
-template <int N>
-__device__ __forceinline__ float ror16(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               0x120 + N, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = __builtin_fmaxf(x, ror16<8>(x));
-  x = __builtin_fmaxf(x, ror16<4>(x));
-  x = __builtin_fmaxf(x, ror16<2>(x));
-  return __builtin_fmaxf(x, ror16<1>(x));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += ror16<8>(x);
-  x += ror16<4>(x);
-  x += ror16<2>(x);
-  return x + ror16<1>(x);
-}
-// x[l] + x[l ^ 16] in every lane.
-__device__ __forceinline__ float xor16_sum(float x) {
+// max / sum of x over lanes l, l^16, l^32, l^48 (the four lane groups).
+__device__ __forceinline__ float groups_max(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
   auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  x = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  return halves_max(x);
 }
-// Completes this wave's LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ float groups_sum(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  return halves_sum(x);
+}
 
-template <typename T, int D, int HT>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
+template <typename T>
+__device__ __forceinline__ floatx4 mma16x16x16(u32x2 a, u32x2 b, floatx4 c);
+template <>
+__device__ __forceinline__ floatx4 mma16x16x16<__bf16>(u32x2 a, u32x2 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ floatx4 mma16x16x16<_Float16>(u32x2 a, u32x2 b, floatx4 c) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                               __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunk of V row r in the per-wave LDS block, so
+// that the transpose reads (4 rows x 2 chunks per 16 lanes) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
+}
+
+// Block copies are issued as global -> LDS copies in inline asm, so that the
+// compiler neither counts them nor inserts waits of its own (they have no
+// register result): the loop below keeps a fixed number of copies in flight
+// and waits, with wait_vmem_le, for exactly the ones it is about to read.
+__device__ __forceinline__ void asm_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, int voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+}
+// Waits until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// XOR swizzle of the 16-byte chunk of K row r in the per-wave LDS block, so
+// that the operand reads (16 rows, one chunk each, per 16 lanes) hit distinct
+// banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <typename T, int D, int PF, bool UNIFORM, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_partial_kernel(DecArgs a) {
+  constexpr int kWaves = NW;
+  constexpr int kThreads = 64 * NW;
   using E = Elem<T>;
-  constexpr int NCH = D / 8;      // 16-byte chunks per token row
-  constexpr int TG = 64 / NCH;    // token groups of the PV layout
-  constexpr int TPL = kTB / TG;   // V tokens per lane per block
-  constexpr int KS = D / 32;      // steps of the 16x16x32 score product
-  __shared__ floatx4 p_lds[kWaves][kTB][4];   // weights [token][head/4]
-  __shared__ float al_lds[kWaves][16];         // rescale factors per head
-  __shared__ float o_lds[kWaves][HT][D];
+  constexpr int KS = D / 32;          // 16x16x32 steps of S^T over d
+  constexpr int NCH = D / 8;          // 16-byte chunks per row
+  constexpr int ROWS = 64 / NCH;      // rows per copy instruction (1 KiB each)
+  constexpr int CPB = kTB / ROWS;     // copy instructions per block and tensor
+  constexpr int DB = D / 16;          // 16-row blocks of O^T
+  constexpr int NS = PF + 1;          // blocks in the prefetch ring
+  constexpr int SLOT = kTB * NCH;     // 16-byte chunks of one K (or V) block
+  constexpr int LOADS = 2 * CPB;      // vector-memory operations per block
+  static_assert(NS == 3 && kPageWindow % NS == 0, "ring slots must follow the unroll index");
+  static_assert(2 * SLOT * 16 >= 16 * D * 4, "two K slots hold the wave totals");
+  // Per wave: rings of NS K blocks and NS V blocks (row-major, swizzled
+  // chunks), one LDS object per slot so that the slot being filled is never
+  // confused with the one being read.  Afterwards K slots 0 and 1 hold the
+  // wave's totals (heads 0-7 and 8-15).
+  __shared__ u32x4 kring0[kWaves][SLOT], kring1[kWaves][SLOT], kring2[kWaves][SLOT];
+  __shared__ u32x4 vring0[kWaves][SLOT], vring1[kWaves][SLOT], vring2[kWaves][SLOT];
   __shared__ float m_lds[kWaves][16];
   __shared__ float l_lds[kWaves][16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int g = lane >> 4, hl = lane & 15;
   const int split = blockIdx.x, b = blockIdx.z;
   const int kvh = blockIdx.y / a.hchunks, hc = blockIdx.y - kvh * a.hchunks;
   const int h0 = kvh * a.group + hc * 16;
@@ -103,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
 
   // live length, clamped into the table's capacity (flagged when outside)
   const int cap = a.maxb * a.bs;
-  int ctx = a.lens[b];
+  int ctx = __builtin_amdgcn_readfirstlane(a.lens[b]);  // one value per workgroup
   if (ctx < 0 || ctx > cap) {
     if (a.err && tid == 0) *a.err = 1;
     ctx = ctx < 0 ? 0 : cap;
@@ -113,87 +163,105 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
   const int t0 = min(ctx, split * chunk);
   const int t1 = min(ctx, t0 + chunk);
   const int nblk = (t1 - t0 + kTB - 1) / kTB;
+  const int nj = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;  // this wave's blocks
 
-  // Q as the A operand: lane -> head row (lane & 15), d = 32 ks + 8 (lane >> 4) .. +7
-  const int hgrp = lane >> 4;
-  const int tl = lane & 15;
+  // Q^T as the B operand: lane -> head hl, d = 32 ks + 8 g .. +7
   const T* Qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + h0) * D;
   u32x4 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = tl < nh ? load16(Qb + tl * D + 32 * ks + 8 * hgrp) : zero_u32x4();
+    qf[ks] = hl < nh ? load16(Qb + hl * D + 32 * ks + 8 * g) : zero_u32x4();
+  const float slope_l2 = (a.alibi && hl < nh) ? a.alibi[h0 + hl] * kLog2e : 0.f;
+  const float qpos = (float)(ctx - 1);
 
-  // score layout: lane holds token tl of the block for heads 4*hgrp + r
-  float slope_l2[4], m_run[4], l_part[4];
+  floatx4 o[DB];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int hh = 4 * hgrp + r;
-    slope_l2[r] = (a.alibi && hh < nh) ? a.alibi[h0 + hh] * kLog2e : 0.f;
-    m_run[r] = kNegInf;
-    l_part[r] = 0.f;
-  }
+  for (int db = 0; db < DB; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_part = 0.f;
 
-  // PV layout: lane owns chunk c of tokens tg + TG * i of each block
-  const int c = lane % NCH, tg = lane / NCH;
-  float o[HT][8];
-#pragma unroll
-  for (int hh = 0; hh < HT; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-
-  const size_t tok_stride = (size_t)a.Hkv * D;
+  const size_t tok_stride = (size_t)a.Hkv * D;  // elements between consecutive slots
   const T* Kp = reinterpret_cast<const T*>(a.kp) + (size_t)kvh * D;
   const T* Vp = reinterpret_cast<const T*>(a.vp) + (size_t)kvh * D;
   const int32_t* trow = a.table + (size_t)b * a.maxb;
-  const float qpos = (float)(ctx - 1);
+  const int crow = lane / NCH, cch = lane % NCH;  // copy layout: chunk cch of rows crow + ROWS i
 
-  // Physical row offset of logical token t, or -1 if its block id is invalid.
-  auto row_of = [&](int t) -> long long {
-    const int page = t / a.bs;
-    const int phys = trow[page];
-    if ((unsigned)phys >= (unsigned)a.num_blocks) {
-      if (a.err) *a.err = 1;
-      return -1;
+  int page_reg = 0;  // lane j: physical block of this wave's block (window + j)
+  auto load_pages = [&](int j0) {
+    const int j = j0 + lane;
+    page_reg = j < nj ? trow[(t0 + kTB * (wave + kWaves * j)) / a.bs] : 0;
+  };
+  auto kslot = [&](int u) -> u32x4* { return u == 0 ? kring0[wave] : (u == 1 ? kring1[wave] : kring2[wave]); };
+  auto vslot = [&](int u) -> u32x4* { return u == 0 ? vring0[wave] : (u == 1 ? vring1[wave] : vring2[wave]); };
+  // 32-bit LDS address of a slot chunk (folds to scalar arithmetic)
+  auto lds_addr = [](const u32x4* p) { return (uint32_t)(uintptr_t)(const ATTN_LDS void*)p; };
+
+  bool bad_page = false;  // a table entry outside the pool was met (wave-uniform)
+  uint32_t valid[NS];     // per ring slot: bit t = token t of the block is live
+  // Issues the copies of block j (window-relative index jw for its page id)
+  // into ring slot u.  A block that is not `live` (past this window) is
+  // padding: it keeps the ring rotating, but its copies read nothing.
+  auto fetch = [&](int u, int j, int jw, bool live) {
+    const int tb = __builtin_amdgcn_readfirstlane(t0 + kTB * (wave + kWaves * j));
+    const int nvalid = live ? min(kTB, t1 - tb) : 0;
+    u32x4* ks_ = kslot(u);
+    u32x4* vs_ = vslot(u);
+    if constexpr (UNIFORM) {
+      const int phys = __builtin_amdgcn_readlane(page_reg, live ? jw : 0);
+      const bool ok = nvalid > 0 && (unsigned)phys < (unsigned)a.num_blocks;
+      bad_page |= nvalid > 0 && !ok;
+      const long long row0 = ok ? ((long long)phys * a.bs + (tb % a.bs)) * (long long)tok_stride : 0;
+      const long long bytes = ok ? (long long)nvalid * tok_stride * sizeof(T) : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp + row0, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp + row0, bytes);
+#pragma unroll
+      for (int i = 0; i < CPB; ++i) {
+        const int r = crow + ROWS * i;
+        asm_dma16(rk, lds_addr(ks_ + i * 64), (int)((r * tok_stride + 8 * (cch ^ swz_k<D>(r))) * sizeof(T)));
+        asm_dma16(rv, lds_addr(vs_ + i * 64), (int)((r * tok_stride + 8 * (cch ^ swz_v<D>(r))) * sizeof(T)));
+      }
+      valid[u] = ok ? (nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u)) : 0u;
+    } else {
+      // per-token translation: any block size (synchronous staging)
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < CPB; ++i) {
+        const int r = crow + ROWS * i;
+        const int t = tb + r;
+        long long row = -1;
+        if (live && t < t1) {
+          const int page = t / a.bs;
+          const int phys = trow[page];
+          if ((unsigned)phys < (unsigned)a.num_blocks)
+            row = ((long long)phys * a.bs + (t - page * a.bs)) * (long long)tok_stride;
+          else if (a.err)
+            *a.err = 1;
+        }
+        ks_[r * NCH + (cch ^ swz_k<D>(r))] = row >= 0 ? load16(Kp + row + 8 * cch) : zero_u32x4();
+        vs_[r * NCH + (cch ^ swz_v<D>(r))] = row >= 0 ? load16(Vp + row + 8 * cch) : zero_u32x4();
+        // row crow + ROWS i is live iff its chunk-0 lane (lane crow * NCH) found it
+        const uint64_t m = __builtin_amdgcn_ballot_w64(row >= 0 && cch == 0);
+#pragma unroll
+        for (int rr = 0; rr < ROWS; ++rr)
+          bits |= ((m >> (rr * NCH)) & 1ull) ? (1u << (rr + ROWS * i)) : 0u;
+      }
+      valid[u] = bits;
     }
-    return ((long long)phys * a.bs + (t - page * a.bs)) * (long long)tok_stride;
   };
 
-  for (int bi = wave; bi < nblk; bi += kWaves) {
-    const int tb = t0 + bi * kTB;
-    // gather: 16 key rows (score layout), TPL value rows per lane (PV layout)
-    const int tk = tb + tl;
-    u32x4 kf[KS];
-    bool kok = false;
-    if (tk < t1) {
-      const long long row = row_of(tk);
-      if (row >= 0) {
-        kok = true;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = load16(Kp + row + 32 * ks + 8 * hgrp);
-      }
-    }
-    if (!kok) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = zero_u32x4();
-    }
-    u32x4 vf[TPL];
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const int tv = tb + tg + TG * i;
-      vf[i] = zero_u32x4();
-      if (tv < t1) {
-        const long long row = row_of(tv);
-        if (row >= 0) vf[i] = load16(Vp + row + 8 * c);
-      }
-    }
-
-    // scores: 16 heads x 16 tokens
+  auto compute = [&](int u, int j) {
+    const int tb = t0 + kTB * (wave + kWaves * j);
+    // Every block is followed by exactly PF fetches (padding included), so this
+    // block's copies have landed once at most PF * LOADS operations remain.
+    if constexpr (UNIFORM) wait_vmem_le<PF * LOADS>();
+    const u32x4* ks_ = kslot(u);
+    const T* vs = reinterpret_cast<const T*>(vslot(u));
+    // S^T = K Q^T: A operand lane (g, hl) = K row hl, d = 32 ks + 8 g .. +7
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = E::mma16(qf[ks], kf[ks], s);
-
-    float mx[4];
-    bool need = false;
+    for (int ks = 0; ks < KS; ++ks)
+      s = E::mma16(ks_[hl * NCH + ((4 * ks + g) ^ swz_k<D>(hl))], qf[ks], s);
+    // s[r]: head hl, token 4 g + r
+    float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = s[r];
@@ -203,90 +271,65 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
       } else {
         x *= a.c_score;
       }
-      x = __builtin_fmaf(slope_l2[r], (float)tk - qpos, x);
-      s[r] = kok ? x : kNegInf;
-      mx[r] = row16_max(s[r]);
-      need |= mx[r] > m_run[r] + kRescaleGap;
+      const int tok = 4 * g + r;
+      x = __builtin_fmaf(slope_l2, (float)(tb + tok) - qpos, x);
+      s[r] = ((valid[u] >> tok) & 1u) ? x : kNegInf;
+      mx = __builtin_fmaxf(mx, s[r]);
     }
-    const bool rescale = wave_any(need);
-    float alpha[4];
-    floatx4 pw;
+    mx = groups_max(mx);
+    const bool need = mx > m_run + kRescaleGap;
+    if (wave_any(need)) {
+      const float alpha = need ? fast_exp2(m_run - mx) : 1.f;
+      m_run = need ? mx : m_run;
+      l_part *= alpha;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      alpha[r] = 1.f;
-      if (rescale && mx[r] > m_run[r] + kRescaleGap) {
-        alpha[r] = fast_exp2(m_run[r] - mx[r]);
-        m_run[r] = mx[r];
-      }
-      l_part[r] *= alpha[r];
-      const float m_use = m_run[r] == kNegInf ? 0.f : m_run[r];
-      pw[r] = fast_exp2(s[r] - m_use);
-      l_part[r] += pw[r];
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
-    p_lds[wave][tl][hgrp] = pw;
-    if (rescale && tl == 0) {
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    const uint32_t p01 = E::pack2(fast_exp2(s[0] - m_use), fast_exp2(s[1] - m_use));
+    const uint32_t p23 = E::pack2(fast_exp2(s[2] - m_use), fast_exp2(s[3] - m_use));
+    l_part = E::dot2(p01, E::kOnePair, l_part);
+    l_part = E::dot2(p23, E::kOnePair, l_part);
+    const u32x2 pf = {p01, p23};
+    // O^T += V^T P^T: A operand lane (g, hl) = V[4 g + 0..3][16 db + hl]
+    const int tr_row = 4 * g + (hl >> 2);
+    const int sw = swz_v<D>(tr_row);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al_lds[wave][4 * hgrp + r] = alpha[r];
+    for (int db = 0; db < DB; ++db) {
+      const int col = 16 * db + 4 * (hl & 3);
+      const u32x2 va = lds_read_tr16(vs + tr_row * D + ((col >> 3) ^ sw) * 8 + (col & 7));
+      o[db] = mma16x16x16<T>(va, pf, o[db]);
     }
-    wave_lds_sync();
+  };
 
-    if (rescale) {
+  // ---- main loop: PF blocks in flight ahead of the one being computed, in
+  // windows of kPageWindow blocks (one page-id load per window).
+  for (int c0 = 0; c0 < nj; c0 += kPageWindow) {
+    const int cn = min(kPageWindow, nj - c0);
+    if constexpr (UNIFORM) load_pages(c0);
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh) {
-        const float al = al_lds[wave][hh];
+    for (int p = 0; p < PF; ++p) fetch(p, c0 + p, p, p < cn);
+    for (int j0 = 0; j0 < cn; j0 += NS) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] *= al;
+      for (int u = 0; u < NS; ++u) {
+        const int jw = j0 + u;  // window-relative
+        const int jf = jw + PF;
+        fetch((u + PF) % NS, c0 + jf, jf, jf < cn);
+        if (jw < cn) compute(u, c0 + jw);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const int tt = tg + TG * i;
-      float pv[HT];
-#pragma unroll
-      for (int q4 = 0; q4 < (HT + 3) / 4; ++q4) {
-        const floatx4 w4 = p_lds[wave][tt][q4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * q4 + r < HT) pv[4 * q4 + r] = w4[r];
-      }
-      float vv[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vv[2 * e] = E::lo(vf[i][e]);
-        vv[2 * e + 1] = E::hi(vf[i][e]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < HT; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pv[hh], vv[e], o[hh][e]);
     }
   }
+  wait_vmem_le<0>();  // padding copies into the slots reused below have landed
+  if (bad_page && a.err && lane == 0) *a.err = 1;
 
-  // ---- wave totals: l over the 16 token lanes, o over the token groups
+  // ---- wave totals: l over the 4 lane groups; o is already complete per lane
+  const float l = groups_sum(l_part);
+  float* ow = reinterpret_cast<float*>(hl < 8 ? kring0[wave] : kring1[wave]) + (hl & 7) * D;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) l_part[r] = row16_sum(l_part[r]);
-#pragma unroll
-  for (int hh = 0; hh < HT; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = o[hh][e];
-      if constexpr (D == 64) x += ror16<8>(x);
-      x = xor16_sum(x);
-      x = halves_sum(x);
-      o[hh][e] = x;
-    }
-  if (tg == 0) {
-#pragma unroll
-    for (int hh = 0; hh < HT; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o_lds[wave][hh][c * 8 + e] = o[hh][e];
-  }
-  if (tl == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m_lds[wave][4 * hgrp + r] = m_run[r];
-      l_lds[wave][4 * hgrp + r] = l_part[r];
-    }
+  for (int db = 0; db < DB; ++db) *reinterpret_cast<floatx4*>(ow + 16 * db + 4 * g) = o[db];
+  if (g == 0) {
+    m_lds[wave][hl] = m_run;
+    l_lds[wave][hl] = l;
   }
   __syncthreads();
 
@@ -302,7 +345,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wt = fast_exp2(m_lds[w][hh] - M);
-        num = __builtin_fmaf(wt, o_lds[w][hh][d], num);
+        const float* tw = reinterpret_cast<const float*>(hh < 8 ? kring0[w] : kring1[w]);
+        num = __builtin_fmaf(wt, tw[(hh & 7) * D + d], num);
         den = __builtin_fmaf(wt, l_lds[w][hh], den);
       }
       if (den > 0.f) {
@@ -343,23 +387,19 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(MergeArgs a) {
   reinterpret_cast<T*>(a.out)[bh * D + d] = (T)r;
 }
 
-template <typename T, int D, int HT>
-hipError_t launch_partial(const DecArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, HT>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
+#ifndef ATTN_DECODE_WAVES
+#define ATTN_DECODE_WAVES 2
+#endif
 
 template <typename T, int D>
-hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, int ht, hipStream_t stream) {
+hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t stream) {
+  constexpr int NW = ATTN_DECODE_WAVES;
   const dim3 grid(p.splits, p.Hkv * a.hchunks, p.B);
-  hipError_t e;
-  switch (ht) {
-    case 1: e = launch_partial<T, D, 1>(a, grid, stream); break;
-    case 2: e = launch_partial<T, D, 2>(a, grid, stream); break;
-    case 4: e = launch_partial<T, D, 4>(a, grid, stream); break;
-    case 8: e = launch_partial<T, D, 8>(a, grid, stream); break;
-    default: e = launch_partial<T, D, 16>(a, grid, stream); break;
-  }
+  if (p.block_size % kTB == 0)
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, true, NW>), grid, dim3(64 * NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, false, NW>), grid, dim3(64 * NW), 0, stream, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs m{p.ws_o, p.ws_lse, p.out, p.splits};
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(p.B * p.Hq), dim3(D), 0, stream, m);
@@ -390,14 +430,10 @@ hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t st
   a.softcap = p.softcap > 0.f;
   a.c_score = a.softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
   a.c_cap = kLog2e * p.softcap;
-  const int g = a.group < 16 ? a.group : 16;
-  const int ht = g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 16;
-  if (dtype == 2) {
-    return p.D == 128 ? launch_typed<__bf16, 128>(p, a, ht, stream)
-                      : launch_typed<__bf16, 64>(p, a, ht, stream);
-  }
-  return p.D == 128 ? launch_typed<_Float16, 128>(p, a, ht, stream)
-                    : launch_typed<_Float16, 64>(p, a, ht, stream);
+  if (dtype == 2)
+    return p.D == 128 ? launch_typed<__bf16, 128>(p, a, stream) : launch_typed<__bf16, 64>(p, a, stream);
+  return p.D == 128 ? launch_typed<_Float16, 128>(p, a, stream)
+                    : launch_typed<_Float16, 64>(p, a, stream);
 }
 
 }  // namespace attn

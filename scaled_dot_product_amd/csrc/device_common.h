@@ -125,4 +125,20 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Asynchronous copy of 16 bytes per lane from a buffer to LDS: lane l's bytes
+// land at lds_base + 16 * l (lds_base must be the same in every lane).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_base, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)lds_base, 16, byte_off, 0, 0, 0);
+}
+
+// Waits until this wave's outstanding vector-memory loads (including the
+// buffer-to-LDS copies above) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace attn

@@ -92,12 +92,144 @@ __device__ __forceinline__ constexpr int key_of(int kb, int r) {
   return 32 * kb + 8 * (r >> 2) + (r & 3);
 }
 
+// Per-wave state of the streaming softmax: output accumulator O^T (one query
+// per lane), running reference max and this lane's share of the denominator.
+template <int DB>
+struct RowState {
+  floatx16 o[DB];
+  float m_run;
+  float l_part;
+};
+
+// S^T = K Q^T for the 64 keys of one LDS tile: sc[0] keys 0..31, sc[1] 32..63.
+template <typename T, int D>
+__device__ __forceinline__ void qk_tile(const u32x4* Ks, const u32x4* qf, int ln, int g,
+                                        floatx16 (&sc)[2]) {
+  using E = Elem<T>;
+  constexpr int NC = D / 8;
+  sc[0] = floatx16{};
+  sc[1] = floatx16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int c = 2 * s + g;
+    sc[0] = E::mma32(Ks[ln * NC + (c ^ swz_k<D>(ln))], qf[s], sc[0]);
+    sc[1] = E::mma32(Ks[(32 + ln) * NC + (c ^ swz_k<D>(32 + ln))], qf[s], sc[1]);
+  }
+}
+
+// Transform + mask + online update of one tile's scores, then O += P V.
 template <typename T, int D, int FLAGS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_mfma_kernel(FwdArgs a) {
+__device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowState<D / 32>& st,
+                                           const FwdArgs& a, int n0, int ip, int ipa_w, int ipb_w,
+                                           float slope_l2, int lane, int g) {
   using E = Elem<T>;
   constexpr bool MASK = (FLAGS & F_MASK) != 0;
   constexpr bool SOFTCAP = (FLAGS & F_SOFTCAP) != 0;
+  constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
+  constexpr bool kRaw = !SOFTCAP && !ALIBI;  // max on raw scores, scale folded into exp
+  constexpr int DB = D / 32;
+  const int Sk = a.Sk;
+  const int rb = n0 + 4 * g - ip;            // j - i' of element offset 0
+
+  if constexpr (!kRaw) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sc[kb][r];
+        if constexpr (SOFTCAP) {
+          const float e = fast_exp2(x * a.c_score);
+          x = a.c_cap - 2.f * a.c_cap * fast_rcp(1.f + e);
+        } else {
+          x *= a.c_score;
+        }
+        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(rb + key_of(kb, r)), x);
+        sc[kb][r] = x;
+      }
+  }
+  if constexpr (MASK) {
+    const bool full = n0 + kBN <= Sk && (!a.has_hi || n0 + kBN - 1 - ipa_w <= a.dmax) &&
+                      (a.wl < 0 || ipb_w - n0 <= a.wl);
+    if (!full) {
+      // admissible iff lo <= j - i' <= hi, with 0 <= j < Sk folded in
+      int hi = Sk - 1 - ip;
+      if (a.has_hi) hi = min(hi, a.dmax);
+      int lo = -ip;
+      if (a.wl >= 0) lo = max(lo, -a.wl);
+      int klo = max(lo - rb, 0), khi = min(hi - rb, kBN - 1);
+      if (khi < klo) klo = khi = kBN;
+      const uint32_t span = (uint32_t)(khi - klo);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((uint32_t)(key_of(kb, r) - klo) > span) sc[kb][r] = kNegInf;
+    }
+  }
+
+  // row max: 32 values in-lane, then the other half of the keys
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[kb][r], sc[kb][r + 1]));
+  float mt = mx;
+  if constexpr (kRaw) mt = mx == kNegInf ? kNegInf : mx * a.c_score;
+  mt = halves_max(mt);
+
+  // raise the reference max only when the tile exceeds it by > 2^8
+  const bool need = mt > st.m_run + kRescaleGap;
+  if (wave_any(need)) {
+    const float alpha = need ? fast_exp2(st.m_run - mt) : 1.f;
+    st.m_run = need ? mt : st.m_run;
+    st.l_part *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
+  }
+  const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
+
+  // weights, rounded to the input type, packed as the PV B operand
+  uint32_t pp[16];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0, p1;
+      if constexpr (kRaw) {
+        p0 = fast_exp2(__builtin_fmaf(sc[kb][r], a.c_score, -m_use));
+        p1 = fast_exp2(__builtin_fmaf(sc[kb][r + 1], a.c_score, -m_use));
+      } else {
+        p0 = fast_exp2(sc[kb][r] - m_use);
+        p1 = fast_exp2(sc[kb][r + 1] - m_use);
+      }
+      const uint32_t pk = E::pack2(p0, p1);
+      pp[kb * 8 + r / 2] = pk;
+      st.l_part = E::dot2(pk, E::kOnePair, st.l_part);
+    }
+
+  // O^T += V^T P^T, 16 keys per step; V^T through the LDS transpose read
+  const int trow = 4 * g + ((lane & 15) >> 2);                // key row within a 16-key step
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // d within a 32-row block
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 pf = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
+    const int r0 = 16 * ks + trow;
+    const int sw = swz_v<D>(r0);  // same for r0 + 8
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + tcol;
+      const int cidx = ((col >> 3) ^ sw) * 8 + (col & 7);
+      const u32x2 lo = lds_read_tr16(Vs + r0 * D + cidx);
+      const u32x2 hi = lds_read_tr16(Vs + (r0 + 8) * D + cidx);
+      const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+      st.o[db] = E::mma32(va, pf, st.o[db]);
+    }
+  }
+}
+
+template <typename T, int D, int FLAGS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(FwdArgs a) {
   constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
   constexpr int NC = D / 8;              // 16-byte chunks per K/V row
   constexpr int TC = kBN * NC;           // chunks per K (or V) tile
@@ -106,11 +238,13 @@ void fwd_mfma_kernel(FwdArgs a) {
   constexpr int DB = D / 32;             // 32-row blocks of O^T
   static_assert(CPT * kThreads == TC, "tile must split evenly over the workgroup");
 
-  __shared__ u32x4 smem[2][2][TC];       // [buffer][K, V][chunk]
+  // Four separate LDS objects so that the compiler can tell the buffer being
+  // filled by the asynchronous copy from the buffers being read.
+  __shared__ u32x4 kbuf0[TC], kbuf1[TC], vbuf0[TC], vbuf1[TC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5;               // lane half
   const int ln = lane & 31;
 
@@ -146,6 +280,7 @@ void fwd_mfma_kernel(FwdArgs a) {
   const int ipa_w = wq0 + off, ipb_w = wq_last + off;
   const int w_lo = key_lo(ipa_w);
   const int w_hi = key_hi(ipb_w);
+  auto live = [&](int t) { return wave_live && t < t_end && t * kBN < w_hi && (t + 1) * kBN > w_lo; };
 
   const int qi = wq0 + ln;  // this lane's query row
   const int ip = qi + off;  // its bottom-right aligned position
@@ -159,172 +294,81 @@ void fwd_mfma_kernel(FwdArgs a) {
   float slope_l2 = 0.f;
   if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
 
-  floatx16 o[DB];
+  RowState<DB> st;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = floatx16{};
-  float m_run = kNegInf;  // running reference max (log2 units)
-  float l_part = 0.f;     // running denominator over this lane's keys
+  for (int db = 0; db < DB; ++db) st.o[db] = floatx16{};
+  st.m_run = kNegInf;
+  st.l_part = 0.f;
 
-  // ---- K/V staging: global -> registers -> LDS
-  u32x4 kr[CPT], vr[CPT];
-  auto gload = [&](int t) {
-    const int n0 = t * kBN;
+  // ---- asynchronous tile copies global -> LDS.  Chunk c of a tile sits at
+  // LDS slot c, i.e. row c / NC, swizzled chunk c % NC; keys past Sk read 0.
+  const long long kv_bytes = (long long)Sk * D * sizeof(T);
+  auto dma_k = [&](u32x4* dst, int t) {
+    const long long base = (long long)t * kBN * D * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(K) + base, kv_bytes - base);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = n0 + c / NC;
-      const int cc = c % NC;
-      if (key < Sk) {
-        kr[i] = load16(K + (size_t)key * D + cc * 8);
-        vr[i] = load16(V + (size_t)key * D + cc * 8);
-      } else {
-        kr[i] = zero_u32x4();
-        vr[i] = zero_u32x4();
-      }
+      const int c = i * kThreads + tid;
+      const int r = c / NC, pc = c % NC;
+      dma16(rs, dst + i * kThreads + wave * 64, (r * D + (pc ^ swz_k<D>(r)) * 8) * (int)sizeof(T));
     }
   };
-  auto lstore = [&](int buf) {
+  auto dma_v = [&](u32x4* dst, int t) {
+    const long long base = (long long)t * kBN * D * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(V) + base, kv_bytes - base);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / NC, cc = c % NC;
-      smem[buf][0][r * NC + (cc ^ swz_k<D>(r))] = kr[i];
-      smem[buf][1][r * NC + (cc ^ swz_v<D>(r))] = vr[i];
+      const int c = i * kThreads + tid;
+      const int r = c / NC, pc = c % NC;
+      dma16(rs, dst + i * kThreads + wave * 64, (r * D + (pc ^ swz_v<D>(r)) * 8) * (int)sizeof(T));
     }
   };
 
-  if (t_begin < t_end) gload(t_begin);
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    lstore(buf);
+  // ---- software pipeline over the tiles t_begin + i:
+  //   step i:  S(i+1) = K(i+1) Q^T   (matrix cores)
+  //            softmax(S(i)), O += P(i) V(i)
+  //   while K(i+2) and V(i+1) stream into the buffers freed by step i-1.
+  // K(i) lives in kbuf[i % 2], V(i) in vbuf[i % 2].
+  const int n = t_end - t_begin;
+  floatx16 sa[2], sb[2];
+  if (n > 0) {
+    dma_k(kbuf0, t_begin);
+    dma_v(vbuf0, t_begin);
+    if (n > 1) dma_k(kbuf1, t_begin + 1);
+    wait_vmem();
     __syncthreads();
-    if (t + 1 < t_end) gload(t + 1);
-    const int n0 = t * kBN;
-    if (!(wave_live && n0 < w_hi && n0 + kBN > w_lo)) continue;  // wave-uniform
-
-    const u32x4* Ks = smem[buf][0];
-    const T* Vs = reinterpret_cast<const T*>(smem[buf][1]);
-
-    // ---- S^T = K Q^T for keys [n0, n0+32) and [n0+32, n0+64)
-    floatx16 sc[2] = {floatx16{}, floatx16{}};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int c = 2 * s + g;
-      sc[0] = E::mma32(Ks[ln * NC + (c ^ swz_k<D>(ln))], qf[s], sc[0]);
-      sc[1] = E::mma32(Ks[(32 + ln) * NC + (c ^ swz_k<D>(32 + ln))], qf[s], sc[1]);
-    }
-
-    // ---- score transform (log2 units) and mask
-    constexpr bool kRaw = !SOFTCAP && !ALIBI;  // max on raw scores, scale folded into exp
-    const int rb = n0 + 4 * g - ip;            // j - i' of element offset 0
-    if constexpr (!kRaw) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sc[kb][r];
-          if constexpr (SOFTCAP) {
-            const float e = fast_exp2(x * a.c_score);
-            x = a.c_cap - 2.f * a.c_cap * fast_rcp(1.f + e);
-          } else {
-            x *= a.c_score;
-          }
-          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(rb + key_of(kb, r)), x);
-          sc[kb][r] = x;
-        }
-    }
-    if constexpr (MASK) {
-      const bool full = n0 + kBN <= Sk && (!a.has_hi || n0 + kBN - 1 - ipa_w <= a.dmax) &&
-                        (a.wl < 0 || ipb_w - n0 <= a.wl);
-      if (!full) {
-        // admissible iff lo <= j - i' <= hi, with j < Sk folded into hi
-        int hi = Sk - 1 - ip;
-        if (a.has_hi) hi = min(hi, a.dmax);
-        int lo = -ip;  // j >= 0
-        if (a.wl >= 0) lo = max(lo, -a.wl);
-        int klo = max(lo - rb, 0), khi = min(hi - rb, kBN - 1);
-        if (khi < klo) klo = khi = kBN;
-        const uint32_t span = (uint32_t)(khi - klo);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if ((uint32_t)(key_of(kb, r) - klo) > span) sc[kb][r] = kNegInf;
-      }
-    }
-
-    // ---- row max: 32 values in-lane, then the other half of the keys
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[kb][r], sc[kb][r + 1]));
-    float mt = mx;
-    if constexpr (kRaw) mt = mx == kNegInf ? kNegInf : mx * a.c_score;
-    mt = halves_max(mt);
-
-    // ---- raise the reference max only when the tile exceeds it by > 2^8
-    const bool need = mt > m_run + kRescaleGap;
-    if (wave_any(need)) {
-      const float alpha = need ? fast_exp2(m_run - mt) : 1.f;
-      m_run = need ? mt : m_run;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-
-    // ---- weights, rounded to the input type, packed as the PV B operand
-    uint32_t pp[16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0, p1;
-        if constexpr (kRaw) {
-          p0 = fast_exp2(__builtin_fmaf(sc[kb][r], a.c_score, -m_use));
-          p1 = fast_exp2(__builtin_fmaf(sc[kb][r + 1], a.c_score, -m_use));
-        } else {
-          p0 = fast_exp2(sc[kb][r] - m_use);
-          p1 = fast_exp2(sc[kb][r + 1] - m_use);
-        }
-        const uint32_t pk = E::pack2(p0, p1);
-        pp[kb * 8 + r / 2] = pk;
-        l_part = E::dot2(pk, E::kOnePair, l_part);
-      }
-
-    // ---- O^T += V^T P^T, 16 keys per step
-    const int trow = 4 * g + ((lane & 15) >> 2);         // key row within a 16-key step
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d within a 32-row block
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 pf = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
-      const int r0 = 16 * ks + trow;
-      const int sw = swz_v<D>(r0);  // same for r0 + 8
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + tcol;
-        const int cidx = ((col >> 3) ^ sw) * 8 + (col & 7);
-        const u32x2 lo = lds_read_tr16(Vs + r0 * D + cidx);
-        const u32x2 hi = lds_read_tr16(Vs + (r0 + 8) * D + cidx);
-        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-        o[db] = E::mma32(va, pf, o[db]);
-      }
-    }
+    if (live(t_begin)) qk_tile<T, D>(kbuf0, qf, ln, g, sa);
+  }
+  auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload,
+                  floatx16 (&s_cur)[2], floatx16 (&s_nxt)[2]) {
+    const int t = t_begin + i;
+    wait_vmem();
+    __syncthreads();  // K(i+1), V(i) landed; everyone is done with step i-1's buffers
+    if (i + 2 < n) dma_k(kload, t + 2);
+    if (i + 1 < n) dma_v(vload, t + 1);
+    if (i + 1 < n && live(t + 1)) qk_tile<T, D>(kread, qf, ln, g, s_nxt);
+    if (live(t))
+      softmax_pv<T, D, FLAGS>(s_cur, reinterpret_cast<const T*>(vread), st, a, t * kBN, ip, ipa_w,
+                              ipb_w, slope_l2, lane, g);
+  };
+  for (int i = 0; i < n; i += 2) {
+    step(i, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+    if (i + 1 < n) step(i + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
   }
 
   // ---- epilogue: O = o / l (0 when no key was admissible)
-  const float l = halves_sum(l_part);
+  const float l = halves_sum(st.l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (qi < Sq) {
+    using E = Elem<T>;
     T* orow = O + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 w;
-        w[0] = E::pack2(o[db][4 * j] * inv, o[db][4 * j + 1] * inv);
-        w[1] = E::pack2(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
+        w[0] = E::pack2(st.o[db][4 * j] * inv, st.o[db][4 * j + 1] * inv);
+        w[1] = E::pack2(st.o[db][4 * j + 2] * inv, st.o[db][4 * j + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * j + 4 * g) = w;
       }
   }
