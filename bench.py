@@ -286,8 +286,8 @@ def summarize(path):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")

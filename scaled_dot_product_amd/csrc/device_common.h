@@ -138,7 +138,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_base,
 }
 
 // Waits until this wave's outstanding vector-memory loads (including the
-// buffer-to-LDS copies above) have completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// buffer-to-LDS copies above) have completed.  Issued through the builtin so
+// that the compiler's own wait insertion knows every earlier load is done
+// (GFX9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15 = no wait on the other two).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace attn

@@ -346,7 +346,13 @@ void fwd_mfma_kernel(FwdArgs a) {
     __syncthreads();  // K(i+1), V(i) landed; everyone is done with step i-1's buffers
     if (i + 2 < n) dma_k(kload, t + 2);
     if (i + 1 < n) dma_v(vload, t + 1);
+    // The matrix phase runs at raised wave priority so that, of the two waves
+    // sharing a SIMD, the one with matrix work ready wins instruction issue
+    // over the one in its softmax (vector) phase.
+    __builtin_amdgcn_s_setprio(1);
     if (i + 1 < n && live(t + 1)) qk_tile<T, D>(kread, qf, ln, g, s_nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     if (live(t))
       softmax_pv<T, D, FLAGS>(s_cur, reinterpret_cast<const T*>(vread), st, a, t * kBN, ip, ipa_w,
                               ipb_w, slope_l2, lane, g);
