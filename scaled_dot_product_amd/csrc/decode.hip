@@ -10,7 +10,8 @@
 // re-bases each part to a common max exactly as the section-3 recurrence
 // re-bases tiles.
 //
-// Partial kernel: one workgroup per (split, KV head [x 16-head chunk], sequence).
+// Partial kernel: one workgroup per (split, KV head [x 16-head chunk], sequence),
+// sequences taken longest first (each workgroup ranks the lengths itself).
 //   * The split's tokens are cut into 16-token blocks dealt round-robin to the
 //     4 waves; every wave keeps its own online-softmax state, so there is no
 //     barrier until the final 4-way merge through LDS.
@@ -43,6 +44,7 @@ namespace attn {
 namespace {
 
 constexpr int kTB = 16;         // tokens per block
+constexpr int kRankMax = 2048;  // batches up to this size (and the LDS it fits) go longest-first
 constexpr int kPageWindow = 63; // blocks per page-id window: <= 64 lanes, a multiple of the ring size
 constexpr float kRescaleGap = 8.0f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -57,7 +59,7 @@ struct DecArgs {
   float* ws_o;
   float* ws_lse;
   int32_t* err;
-  int Hq, Hkv, group, hchunks, num_blocks, bs, maxb, splits;
+  int B, Hq, Hkv, group, hchunks, num_blocks, bs, maxb, splits;
   int softcap;
   float c_score;  // log2(e) * scale; with softcap 2 * log2(e) * scale / cap
   float c_cap;    // log2(e) * cap
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(DecArgs a) {
   constexpr int LOADS = 2 * CPB;      // vector-memory operations per block
   static_assert(NS == 3 && kPageWindow % NS == 0, "ring slots must follow the unroll index");
   static_assert(2 * SLOT * 16 >= 16 * D * 4, "two K slots hold the wave totals");
+  constexpr int RANK_MAX = kWaves * SLOT * 4 < kRankMax ? kWaves * SLOT * 4 : kRankMax;  // ints in kring2
   // Per wave: rings of NS K blocks and NS V blocks (row-major, swizzled
   // chunks), one LDS object per slot so that the slot being filled is never
   // confused with the one being read.  Afterwards K slots 0 and 1 hold the
@@ -146,7 +149,29 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, hl = lane & 15;
-  const int split = blockIdx.x, b = blockIdx.z;
+  const int split = blockIdx.x;
+
+  // ---- sequence of this workgroup: the blockIdx.z-th longest (ties by index),
+  // so that the dispatcher issues the longest splits first and the short ones
+  // fill the tail.  The ranks are a permutation of 0..B-1.
+  int b = blockIdx.z;
+  if (a.B <= RANK_MAX) {
+    int* lens_lds = reinterpret_cast<int*>(kring2);  // free until the main loop
+    __shared__ int s_seq;
+    for (int i = tid; i < a.B; i += kThreads) lens_lds[i] = a.lens[i];
+    __syncthreads();
+    for (int i = tid; i < a.B; i += kThreads) {
+      const int li = lens_lds[i];
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int lj = lens_lds[j];
+        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      if (r == (int)blockIdx.z) s_seq = i;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(s_seq);
+  }
   const int kvh = blockIdx.y / a.hchunks, hc = blockIdx.y - kvh * a.hchunks;
   const int h0 = kvh * a.group + hc * 16;
   const int nh = min(16, a.group - hc * 16);
@@ -419,6 +444,7 @@ hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t st
   a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse;
   a.err = p.error_flag;
+  a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.group = p.Hq / p.Hkv;
