@@ -18,6 +18,7 @@ oracle is timed on a bounded sample of the same prefill workload.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --mode profile           # fixed launches for rocprofv3
     python bench.py --summarize DIR          # text summary of rocprofv3 output
+    python bench.py --traffic FETCH WRITE    # HBM bytes per launch from two counter runs
 """
 from __future__ import annotations
 
@@ -138,8 +139,9 @@ def run_decode(sdpa, wd, dec, stream):
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(W, budget_s: float):
-    """The oracle, as it stands, on whole heads of the prefill workload until
-    about ``budget_s`` seconds of CPU work have been spent (at least one)."""
+    """The oracle, as it stands, on whole (batch, head) slices of the prefill
+    workload, cycling over them until about ``budget_s`` seconds of CPU work
+    have been spent (at least one slice)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -152,8 +154,8 @@ def cpu_baseline(W, budget_s: float):
     pairs = admissible_pairs(w.Sq, w.Sk, w.causal)
     heads, t0 = 0, time.perf_counter()
     order = [(b, h) for h in range(w.Hq) for b in range(w.B)]
-    while heads < len(order):
-        b, h = order[heads]
+    while True:
+        b, h = order[heads % len(order)]
         g = oracle.kv_head_of(h, w.Hq, w.Hkv)
         oracle.sdpa_naive_f64(q64[b:b + 1, h:h + 1], k64[b:b + 1, g:g + 1], v64[b:b + 1, g:g + 1],
                               scale=w.scale, causal=True)
@@ -164,8 +166,8 @@ def cpu_baseline(W, budget_s: float):
     flops = 4 * w.D * pairs * heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of the prefill workload "
-                      f"(all 2048 rows each), float64 NumPy, {dt:.1f} s"}
+            "sample": f"{heads} (batch, head) slices of the prefill workload, cycling over its "
+                      f"{len(order)} (all {w.Sq} rows each), float64 NumPy, {dt:.1f} s"}
 
 
 # ---------------------------------------------------------------- modes
@@ -283,6 +285,53 @@ def summarize(path):
                       f"{float(r.get('MaxNs', 0)) / 1e3:>10.2f}  {r.get('Name', '?')[:160]}")
 
 
+def _counter_means(path, counter):
+    """Mean per-dispatch value of one rocprofv3 counter, by kernel class."""
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no rocprofv3 counter output under {path}")
+    vals = {"prefill": [], "decode_partial": [], "decode_merge": [], "copy": []}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                n = r["Kernel_Name"]
+                key = ("prefill" if "fwd_mfma_kernel" in n else "decode_partial" if "decode_partial" in n
+                       else "decode_merge" if "decode_merge" in n else "copy" if "neg_kernel" in n else None)
+                if key:
+                    vals[key].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v) if v else float("nan")) for k, v in vals.items()}
+
+
+def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):
+    """Per-launch HBM bytes from a FETCH_SIZE run and a WRITE_SIZE run of
+    ``--mode profile`` (KiB per dispatch), each scaled by what the same
+    counter reads for the copy kernel of known size; prints the traffic file."""
+    fe, wr = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    f_fac = copy_bytes / 1024.0 / fe["copy"]
+    w_fac = copy_bytes / 1024.0 / wr["copy"]
+    pre = (fe["prefill"] * f_fac + wr["prefill"] * w_fac) * 1024.0
+    dec_f = (fe["decode_partial"] + fe["decode_merge"]) * f_fac * 1024.0
+    dec_w = (wr["decode_partial"] + wr["decode_merge"]) * w_fac * 1024.0
+    print("# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),")
+    print("# each scaled by the factor that makes the copy kernel (torch.neg over 256 MiB float32,")
+    print("# 256 MiB read + 256 MiB written) read its known size.")
+    print(f"fetch_calibration = {f_fac:.4f}")
+    print(f"write_calibration = {w_fac:.4f}")
+    print(f"copy_fetch_kib_raw = {fe['copy']:.1f}")
+    print(f"copy_write_kib_raw = {wr['copy']:.1f}")
+    print(f"prefill_fetch_kib_raw = {fe['prefill']:.1f}")
+    print(f"prefill_write_kib_raw = {wr['prefill']:.1f}")
+    print(f"decode_fetch_kib_raw = {fe['decode_partial']:.1f} + {fe['decode_merge']:.1f} (partial + merge)")
+    print(f"decode_write_kib_raw = {wr['decode_partial']:.1f} + {wr['decode_merge']:.1f} (partial + merge)")
+    print(f"prefill_bytes = {pre:.0f}")
+    print(f"decode_bytes = {dec_f + dec_w:.0f}")
+    print(f"decode_read_bytes = {dec_f:.0f}")
+    print(f"decode_write_bytes = {dec_w:.0f}")
+    print(f"sources_sha256_16 = {sources_digest()}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,9 +342,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize:
         return summarize(args.summarize)
+    if args.traffic:
+        return traffic(*args.traffic)
     if args.gpus != 1:
         sys.exit(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the attention "
                  "kernels here are single-GPU, and multi-GPU sharding is not part of this build")
