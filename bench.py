@@ -301,7 +301,9 @@ def _counter_means(path, counter):
                        else "decode_merge" if "decode_merge" in n else "copy" if "neg_kernel" in n else None)
                 if key:
                     vals[key].append(float(r["Counter_Value"]))
-    return {k: (sum(v) / len(v) if v else float("nan")) for k, v in vals.items()}
+    # a kernel class with no dispatch contributes nothing (the copy is required)
+    return {k: (sum(v) / len(v) if v else (float("nan") if k == "copy" else 0.0))
+            for k, v in vals.items()}
 
 
 def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):

@@ -33,8 +33,8 @@
 //     translate every token separately.
 //   * Output per (sequence, head, split): normalised partial o[D] and its
 //     natural-log LSE, into the caller's workspace.
-// Merge kernel: one workgroup per (sequence, head), splits combined in fixed
-// order, result cast to the input type.
+// Merge kernel: 4 d per thread, splits combined in fixed order, result cast
+// to the input type.
 #include <limits.h>
 
 #include "device_common.h"
@@ -390,26 +390,43 @@ struct MergeArgs {
   const float* ws_lse;
   void* out;
   int splits;
+  int nbh;  // B * Hq
 };
 
+// One thread per 4 consecutive d of one (sequence, head); a workgroup covers
+// 256 / (D / 4) heads.  Every split's LSE and partial are loaded up front and
+// combined in split order.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(MergeArgs a) {
-  const size_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+  using E = Elem<T>;
+  constexpr int TPH = D / 4;      // threads per (sequence, head)
+  constexpr int HPW = 256 / TPH;  // (sequence, head) pairs per workgroup
+  const int t = threadIdx.x;
+  const size_t bh = (size_t)blockIdx.x * HPW + t / TPH;
+  if (bh >= (size_t)a.nbh) return;
+  const int d4 = (t % TPH) * 4;
   const float* lse = a.ws_lse + bh * a.splits;
+  const float* o = a.ws_o + bh * a.splits * D + d4;
   float M = kNegInf;
+#pragma unroll 8
   for (int s = 0; s < a.splits; ++s) M = __builtin_fmaxf(M, lse[s]);
-  float r = 0.f;
+  floatx4 r = {0.f, 0.f, 0.f, 0.f};
   if (M != kNegInf) {
-    float num = 0.f, den = 0.f;
+    floatx4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll 8
     for (int s = 0; s < a.splits; ++s) {
       const float w = expf(lse[s] - M);
-      num = __builtin_fmaf(w, a.ws_o[(bh * a.splits + s) * D + d], num);
+      const floatx4 v = *reinterpret_cast<const floatx4*>(o + (size_t)s * D);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = __builtin_fmaf(w, v[c], num[c]);
       den += w;
     }
-    r = num / den;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = num[c] / den;
   }
-  reinterpret_cast<T*>(a.out)[bh * D + d] = (T)r;
+  u32x2 w2 = {E::pack2(r[0], r[1]), E::pack2(r[2], r[3])};
+  *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.out) + bh * D + d4) = w2;
 }
 
 #ifndef ATTN_DECODE_WAVES
@@ -426,8 +443,10 @@ hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t st
     hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, false, NW>), grid, dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{p.ws_o, p.ws_lse, p.out, p.splits};
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(p.B * p.Hq), dim3(D), 0, stream, m);
+  MergeArgs m{p.ws_o, p.ws_lse, p.out, p.splits, p.B * p.Hq};
+  constexpr int HPW = 256 / (D / 4);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((p.B * p.Hq + HPW - 1) / HPW), dim3(256), 0,
+                     stream, m);
   return hipGetLastError();
 }
 
