@@ -125,6 +125,40 @@ def setup(torch, sdpa, W, dev):
     return wp, wd, pre, dec, lens.numpy()
 
 
+def run_dense(sdpa, w, t, alibi, stream):
+    sdpa.attn_fwd(t["q"], t["k"], t["v"], alibi, t["out"], softmax_scale=w.scale, causal=w.causal,
+                  window_left=w.window_left, window_right=w.window_right, softcap=w.softcap,
+                  stream=stream)
+
+
+def extra_prefill(torch, sdpa, W, dev, stream, launches=10):
+    """The other prefill workloads, timed on their own after the timed steps
+    (not part of a step): the long masked 8k prefill (causal + window 4096,
+    softcap 50, ALiBi) and the f16 chunked prefill with Sq != Sk."""
+    out = {}
+    for w in (W.LONG_MASKED_8K, W.CHUNKED_PREFILL):
+        q, k, v, alibi = W.dense_inputs(w)
+        t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
+        t["out"] = torch.empty_like(t["q"])
+        al = alibi.to(dev) if alibi is not None else None
+        for _ in range(3):
+            run_dense(sdpa, w, t, al, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(launches):
+            run_dense(sdpa, w, t, al, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / launches
+        tf = prefill_flops(w) / sec / 1e12
+        out[w.name] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype, "work_per_launch": prefill_flops(w),
+                       "ms_per_launch": sec * 1e3, "launches": launches}
+        del t
+    return out
+
+
 def run_prefill(sdpa, wp, pre, stream):
     sdpa.attn_fwd(pre["q"], pre["k"], pre["v"], None, pre["out"], softmax_scale=wp.scale,
                   causal=wp.causal, stream=stream)
@@ -229,6 +263,8 @@ def bench(args):
         "roofline": dominant,
         "rooflines": {"prefill": roof_pre, "decode": roof_dec},
     }
+    if not args.no_extra:
+        result["other_prefill"] = extra_prefill(torch, sdpa, W, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -342,6 +378,8 @@ def main():
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip timing the long masked and chunked prefill workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))

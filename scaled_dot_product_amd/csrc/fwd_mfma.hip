@@ -325,41 +325,42 @@ void fwd_mfma_kernel(FwdArgs a) {
   };
 
   // ---- software pipeline over the tiles t_begin + i:
-  //   step i:  S(i+1) = K(i+1) Q^T   (matrix cores)
-  //            softmax(S(i)), O += P(i) V(i)
+  //   step i:  softmax(S(i)), O += P(i) V(i)
+  //            S(i+1) = K(i+1) Q^T   (matrix cores, into the same registers)
   //   while K(i+2) and V(i+1) stream into the buffers freed by step i-1.
   // K(i) lives in kbuf[i % 2], V(i) in vbuf[i % 2].
   const int n = t_end - t_begin;
-  floatx16 sa[2], sb[2];
+  floatx16 sc[2];
   if (n > 0) {
     dma_k(kbuf0, t_begin);
     dma_v(vbuf0, t_begin);
     if (n > 1) dma_k(kbuf1, t_begin + 1);
     wait_vmem();
     __syncthreads();
-    if (live(t_begin)) qk_tile<T, D>(kbuf0, qf, ln, g, sa);
+    if (live(t_begin)) qk_tile<T, D>(kbuf0, qf, ln, g, sc);
   }
-  auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload,
-                  floatx16 (&s_cur)[2], floatx16 (&s_nxt)[2]) {
+  auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload) {
     const int t = t_begin + i;
     wait_vmem();
     __syncthreads();  // K(i+1), V(i) landed; everyone is done with step i-1's buffers
     if (i + 2 < n) dma_k(kload, t + 2);
     if (i + 1 < n) dma_v(vload, t + 1);
-    // The matrix phase runs at raised wave priority so that, of the two waves
+    if (live(t))
+      softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a, t * kBN, ip, ipa_w,
+                              ipb_w, slope_l2, lane, g);
+    // S(i+1) overwrites S(i), already consumed: one score buffer per wave.
+    // This matrix phase runs at raised wave priority so that, of the two waves
     // sharing a SIMD, the one with matrix work ready wins instruction issue
     // over the one in its softmax (vector) phase.
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
-    if (i + 1 < n && live(t + 1)) qk_tile<T, D>(kread, qf, ln, g, s_nxt);
+    if (i + 1 < n && live(t + 1)) qk_tile<T, D>(kread, qf, ln, g, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    if (live(t))
-      softmax_pv<T, D, FLAGS>(s_cur, reinterpret_cast<const T*>(vread), st, a, t * kBN, ip, ipa_w,
-                              ipb_w, slope_l2, lane, g);
   };
   for (int i = 0; i < n; i += 2) {
-    step(i, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
-    if (i + 1 < n) step(i + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
+    step(i, kbuf1, vbuf0, kbuf0, vbuf1);
+    if (i + 1 < n) step(i + 1, kbuf0, vbuf1, kbuf1, vbuf0);
   }
 
   // ---- epilogue: O = o / l (0 when no key was admissible)
