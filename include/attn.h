@@ -79,7 +79,8 @@ typedef struct attn_fwd_params {
   int64_t Hq;            /* query heads; a multiple of Hkv                      */
   int64_t Hkv;           /* key/value heads                                     */
   int64_t Sq;            /* query length (0 allowed: nothing to do)             */
-  int64_t Sk;            /* key length (0 allowed: output is all zero)          */
+  int64_t Sk;            /* key length (0 allowed: output is all zero); one    *
+                          * head's K (Sk * D * element size) must be < 2 GiB    */
   int64_t D;             /* head dim: 64 or 128                                 */
   int32_t dtype;         /* attn_dtype_t of q, k, v and out                     */
   int32_t causal;        /* nonzero: bottom-right causal mask                   */

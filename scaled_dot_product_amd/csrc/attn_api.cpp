@@ -74,6 +74,7 @@ attn_status_t fwd_shape(const attn_fwd_params_t* p, int64_t* q_bytes, int64_t* k
   const int64_t es = elem_bytes(p->dtype);
   if (!mul4(p->B, p->Hq, p->Sq, p->D * es, q_bytes)) return ATTN_ERR_SHAPE;
   if (!mul4(p->B, p->Hkv, p->Sk, p->D * es, kv_bytes)) return ATTN_ERR_SHAPE;
+  if (p->Sk * p->D * es > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's K (or V) < 2 GiB
   return ATTN_OK;
 }
 

@@ -131,6 +131,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
+// Same with a 32-bit size (clamped below at 0), for ranges known to be < 2 GiB:
+// the clamp stays in scalar arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes < 0 ? 0 : bytes, 0x00020000);
+}
+
 // Asynchronous copy of 16 bytes per lane from a buffer to LDS: lane l's bytes
 // land at lds_base + 16 * l (lds_base must be the same in every lane).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_base, int byte_off) {

@@ -167,12 +167,14 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
     }
   }
 
-  // row max: 32 values in-lane, then the other half of the keys
-  float mx = kNegInf;
+  // row max: 32 values in-lane (a chain of three-input max), then the other
+  // half of the keys
+  float mx = __builtin_fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[kb][r], sc[kb][r + 1]));
+  for (int q = 1; q < 16; ++q) {
+    const int kb = q >> 3, r = 2 * (q & 7);
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[kb][r]), sc[kb][r + 1]);
+  }
   float mt = mx;
   if constexpr (kRaw) mt = mx == kNegInf ? kNegInf : mx * a.c_score;
   mt = halves_max(mt);
@@ -302,10 +304,11 @@ void fwd_mfma_kernel(FwdArgs a) {
 
   // ---- asynchronous tile copies global -> LDS.  Chunk c of a tile sits at
   // LDS slot c, i.e. row c / NC, swizzled chunk c % NC; keys past Sk read 0.
-  const long long kv_bytes = (long long)Sk * D * sizeof(T);
+  // one head's K (or V) is < 2 GiB (checked by the host), so offsets fit int32
+  const int kv_bytes = Sk * D * (int)sizeof(T);
   auto dma_k = [&](u32x4* dst, int t) {
-    const long long base = (long long)t * kBN * D * sizeof(T);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(K) + base, kv_bytes - base);
+    const int base = t * kBN * D * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(reinterpret_cast<const char*>(K) + base, kv_bytes - base);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kThreads + tid;
@@ -314,8 +317,8 @@ void fwd_mfma_kernel(FwdArgs a) {
     }
   };
   auto dma_v = [&](u32x4* dst, int t) {
-    const long long base = (long long)t * kBN * D * sizeof(T);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(V) + base, kv_bytes - base);
+    const int base = t * kBN * D * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(reinterpret_cast<const char*>(V) + base, kv_bytes - base);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kThreads + tid;
