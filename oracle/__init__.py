@@ -20,5 +20,6 @@ from .sdpa import (  # noqa: F401
     query_positions,
     sdpa_naive_f64,
     sdpa_online_f64,
+    sdpa_lse_f64,
     transform_scores,
 )

@@ -98,6 +98,47 @@ def sdpa_bruteforce(q, k, v, *, scale, causal=False, window_left=None,
         return out
 
 
+def lse_bruteforce(q, k, *, scale, causal=False, window_left=None, window_right=None,
+                   softcap=None, alibi=None):
+    """Log-sum-exp ``ln(sum_j exp(s_j))`` of each query row's admissible
+    transformed scores, term by term in 50-digit decimal (no max subtracted);
+    ``None`` for a row with no admissible key.  Same inputs as
+    :func:`sdpa_bruteforce`; returns nested lists ``[B][Hq][Sq]``."""
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        sc = Decimal(repr(float(scale)))
+        cap = Decimal(repr(float(softcap))) if softcap else None
+        out = []
+        for b in range(len(q)):
+            Hq, Hkv = len(q[b]), len(k[b])
+            ob = []
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                Sq, Sk = len(q[b][h]), len(k[b][g])
+                oh = []
+                for i in range(Sq):
+                    i_abs = i + Sk - Sq
+                    total = Decimal(0)
+                    seen = False
+                    for j in range(Sk):
+                        if not _admit(i_abs, j, causal, window_left, window_right):
+                            continue
+                        dot = sum((Decimal(repr(float(q[b][h][i][d])))
+                                   * Decimal(repr(float(k[b][g][j][d]))) for d in range(len(q[b][h][i]))),
+                                  Decimal(0))
+                        s_ = sc * dot
+                        if cap is not None:
+                            s_ = cap * _tanh(s_ / cap)
+                        if alibi is not None:
+                            s_ = s_ + Decimal(repr(float(alibi[h]))) * (j - i_abs)
+                        total += _exp(s_)
+                        seen = True
+                    oh.append(total.ln() if seen else None)
+                ob.append(oh)
+            out.append(ob)
+        return out
+
+
 def paged_bruteforce(q, k_pool, v_pool, block_table, seq_lens, *, scale,
                      softcap=None, alibi=None):
     """Paged form of :func:`sdpa_bruteforce` (kernel-contract page,

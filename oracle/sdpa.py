@@ -46,6 +46,7 @@ __all__ = [
     "transform_scores",
     "sdpa_naive_f64",
     "sdpa_online_f64",
+    "sdpa_lse_f64",
     "attention_partial_f64",
     "lse_merge_f64",
     "paged_gather",
@@ -170,6 +171,46 @@ def sdpa_naive_f64(q, k, v, *, scale, causal=False, window_left=None,
                               where=has_key[:, None])
                 out[b, h, rows] = o
     return out
+
+
+def sdpa_lse_f64(q, k, *, scale, causal=False, window_left=None, window_right=None,
+                 softcap=None, alibi=None, row_block=512):
+    """Natural-log log-sum-exp of each query row's transformed admissible
+    scores, ``log(sum_j exp(s_j))``, with ``-inf`` for a row with no
+    admissible key.
+
+    This is the per-row state the derivation page's section 3 recurrence ends
+    with (``m + log l``) and the quantity its section 8 combines across key
+    splits; the kernel-contract page's ``attention_flash_backward`` consumes
+    it from the forward pass.  Computed from the materialised scores exactly
+    as ``sdpa_naive_f64`` forms them, stabilised by the row max (section 2).
+
+    Returns float64 ``[B, Hq, Sq]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, Hkv, Sq, Sk, D = _check_common(q, k, k, alibi, softcap)
+    slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
+    lse = np.full((B, Hq, Sq), -np.inf)
+    if Sq == 0 or Sk == 0:
+        return lse
+    ip_all = query_positions(Sq, Sk)
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            for r0 in range(0, Sq, row_block):
+                rows = slice(r0, min(Sq, r0 + row_block))
+                ok = admissible(Sq, Sk, causal, window_left, window_right, rows)
+                rel = j - ip_all[rows][:, None]
+                slope = None if slopes is None else slopes[h]
+                s = _scores(q[b, h, rows], k[b, g], scale, softcap, slope, rel, ok)
+                has_key = ok.any(axis=1)
+                m = np.where(has_key, s.max(axis=1), 0.0)
+                l = np.exp(s - m[:, None]).sum(axis=1)
+                lse[b, h, rows] = np.where(has_key, m + np.log(np.where(has_key, l, 1.0)),
+                                           -np.inf)
+    return lse
 
 
 def sdpa_online_f64(q, k, v, *, scale, tile=16, causal=False, window_left=None,

@@ -361,3 +361,72 @@ def test_argument_errors():
         osd.sdpa_naive_f64(q[:, :2], k, k, scale=1.0, softcap=-1.0)
     with pytest.raises(ValueError):
         osd.sdpa_naive_f64(q[:, :2], k, k, scale=1.0, alibi=np.zeros(3))
+
+
+# --------------------------------------------------------------------------
+# Per-row log-sum-exp (the forward state the backward pass consumes)
+# --------------------------------------------------------------------------
+
+def _lse_cases():
+    rng = np.random.default_rng(77)
+    q8 = lambda *s: np.round(rng.standard_normal(s) * 8) / 8  # multiples of 1/8: exact in decimal
+    base = dict(q=q8(1, 2, 4, 3), k=q8(1, 1, 5, 3))
+    return [
+        (base, dict(scale=0.7)),
+        (base, dict(scale=0.7, causal=True)),
+        (base, dict(scale=0.7, window_left=1, window_right=0)),
+        (base, dict(scale=0.7, causal=True, softcap=0.5, alibi=[0.25, 0.75])),
+        (dict(q=q8(1, 2, 6, 3), k=q8(1, 1, 4, 3)), dict(scale=0.9, causal=True)),   # Sq > Sk: empty rows
+        (dict(q=q8(2, 4, 3, 2), k=q8(2, 2, 3, 2)), dict(scale=1.1, window_left=0, window_right=1)),
+    ]
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_lse_matches_decimal_bruteforce(case):
+    """sdpa_lse_f64 against the log of the 50-digit sum of exponentials (no
+    max subtracted), every mask/softcap/ALiBi combination; empty rows -inf."""
+    from oracle.bruteforce import lse_bruteforce
+    t, kw = _lse_cases()[case]
+    got = osd.sdpa_lse_f64(t["q"], t["k"], **kw)
+    ref = lse_bruteforce(t["q"].tolist(), t["k"].tolist(), **kw)
+    for idx in np.ndindex(got.shape):
+        r = ref[idx[0]][idx[1]][idx[2]]
+        if r is None:
+            assert got[idx] == -np.inf
+        else:
+            assert abs(got[idx] - float(r)) <= 1e-12 * max(1.0, abs(float(r)))
+    if case == 4:
+        assert np.all(got[..., :2] == -np.inf) and np.all(np.isfinite(got[..., 2:]))
+
+
+def test_lse_closed_forms():
+    """Q = 0: every admissible score is 0, so lse = log(number of admissible
+    keys); with ALiBi the causal row sums a geometric series."""
+    Sq = Sk = 9
+    q = np.zeros((1, 1, Sq, 4))
+    k = np.ones((1, 1, Sk, 4))
+    got = osd.sdpa_lse_f64(q, k, scale=0.3, causal=True)[0, 0]
+    np.testing.assert_allclose(got, [math.log(i + 1) for i in range(Sq)], rtol=0, atol=1e-15)
+    got = osd.sdpa_lse_f64(q, k, scale=0.3, window_left=2, window_right=3)[0, 0]
+    want = [math.log(min(Sk - 1, i + 3) - max(0, i - 2) + 1) for i in range(Sq)]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+    slope = 0.4
+    got = osd.sdpa_lse_f64(q, k, scale=0.3, causal=True, alibi=np.array([slope]))[0, 0]
+    r = math.exp(-slope)
+    want = [math.log((1 - r ** (i + 1)) / (1 - r)) for i in range(Sq)]
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+
+
+def test_lse_shift_is_additive():
+    """Adding one vector w to every key adds scale * (q . w) to each row's
+    scores, so the lse moves by exactly that amount -- including shifts of
+    +-1e3 that overflow an unstabilised exp (derivation page section 2)."""
+    rng = np.random.default_rng(5)
+    q = _rand(rng, 1, 2, 7, 4)
+    k = _rand(rng, 1, 1, 11, 4)
+    base = osd.sdpa_lse_f64(q, k, scale=0.5, causal=True)
+    for amp in (1e3, -1e3):
+        w = np.full(4, amp / 4)
+        sh = osd.sdpa_lse_f64(q, k + w, scale=0.5, causal=True)
+        delta = 0.5 * (q[0] @ w)                    # [Hq, Sq]
+        np.testing.assert_allclose(sh[0] - base[0], delta, rtol=1e-10, atol=1e-9)
