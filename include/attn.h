@@ -109,6 +109,24 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v,
                        const float* alibi, void* out,
                        const attn_fwd_params_t* p, void* stream);
 
+/* Host-only validation of an attn_fwd_lse call: as attn_fwd_check, plus
+ *   lse   [B, Hq, Sq] float32, 4-byte aligned, overlapping no input and not
+ *         out; NULL only when B * Hq * Sq == 0. */
+attn_status_t attn_fwd_lse_check(const void* q, const void* k, const void* v,
+                                 const float* alibi, const void* out,
+                                 const float* lse, const attn_fwd_params_t* p);
+
+/* Attention forward that also writes, for every query row, the natural-log
+ * log-sum-exp of its transformed admissible scores, ln(sum_j exp(s_j)), or
+ * -infinity for a row with no admissible key.  This is the row state the
+ * online recurrence ends with (derivation page, section 3: m + log l) and
+ * the input the backward pass of the kernel-contract page
+ * (attention_flash_backward) needs from the forward.  Validates as
+ * attn_fwd_lse_check, then enqueues the same kernel as attn_fwd. */
+attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v,
+                           const float* alibi, void* out, float* lse,
+                           const attn_fwd_params_t* p, void* stream);
+
 /* Parameters of attn_paged_decode (kernel-contract page, attention_paged_naive:
  * the PagedAttn parameter set -- scale, block size, optional softcap -- plus
  * the number of key-dimension splits of the decode path, derivation page

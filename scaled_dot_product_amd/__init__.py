@@ -9,6 +9,7 @@ fails to load, every call raises.
 
     attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
              window_left=None, window_right=None, softcap=None, stream=None)
+    attn_fwd_lse(q, k, v, alibi=None, out=None, lse=None, *, ...)  -> (out, lse)
     attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
                       out=None, *, softmax_scale=None, softcap=None,
                       num_splits=8, workspace=None, error_flag=None, stream=None)
@@ -24,7 +25,7 @@ import torch
 
 __all__ = [
     "AttnError", "library", "LIB_PATH",
-    "attn_fwd", "attn_fwd_check", "attn_fwd_params",
+    "attn_fwd", "attn_fwd_check", "attn_fwd_params", "attn_fwd_lse", "attn_fwd_lse_check",
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
     "attn_paged_params", "attn_status_str", "attn_version",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16",
@@ -85,6 +86,10 @@ def library():
     lib.attn_fwd_check.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP, fwd_p, _VP]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_lse_check.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, fwd_p]
+    lib.attn_fwd_lse_check.restype = ctypes.c_int
+    lib.attn_fwd_lse.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, fwd_p, _VP]
+    lib.attn_fwd_lse.restype = ctypes.c_int
     lib.attn_paged_decode_workspace_size.argtypes = [pag_p]
     lib.attn_paged_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_paged_decode_check.argtypes = [_VP] * 8 + [ctypes.c_size_t, _VP, pag_p]
@@ -148,10 +153,14 @@ def attn_fwd_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr, params: attn_fwd_par
                                         None if params is None else ctypes.byref(params)))
 
 
-def attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
-             window_left=None, window_right=None, softcap=None, stream=None):
-    """Attention forward over ``[B, H, S, D]`` device tensors (see attn.h)."""
-    lib = library()
+def attn_fwd_lse_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr, lse_ptr,
+                       params: attn_fwd_params_t) -> int:
+    """Host-only argument check of attn_fwd_lse (no HIP call): the status code."""
+    return int(library().attn_fwd_lse_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr, lse_ptr,
+                                            None if params is None else ctypes.byref(params)))
+
+
+def _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left, window_right, softcap):
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("alibi", alibi), ("out", out)):
         _need_device(name, t, dev)
@@ -170,11 +179,40 @@ def attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
     p = attn_fwd_params(tuple(q.shape), tuple(k.shape), q.dtype, softmax_scale=softmax_scale,
                         causal=causal, window_left=window_left, window_right=window_right,
                         softcap=softcap)
+    return dev, out, p
+
+
+def attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
+             window_left=None, window_right=None, softcap=None, stream=None):
+    """Attention forward over ``[B, H, S, D]`` device tensors (see attn.h)."""
+    lib = library()
+    dev, out, p = _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left,
+                            window_right, softcap)
     st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alibi), _ptr(out), ctypes.byref(p),
                       _stream_handle(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_fwd")
     return out
+
+
+def attn_fwd_lse(q, k, v, alibi=None, out=None, lse=None, *, softmax_scale=None, causal=False,
+                 window_left=None, window_right=None, softcap=None, stream=None):
+    """As :func:`attn_fwd`, and also the float32 ``[B, Hq, Sq]`` natural-log
+    log-sum-exp of every row (``-inf`` for rows with no admissible key).
+    Returns ``(out, lse)``."""
+    lib = library()
+    dev, out, p = _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left,
+                            window_right, softcap)
+    _need_device("lse", lse, dev)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    elif lse.shape != q.shape[:3] or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Sq]")
+    st = lib.attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(alibi), _ptr(out), _ptr(lse),
+                          ctypes.byref(p), _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_lse")
+    return out, lse
 
 
 def attn_paged_params(q_shape, pool_shape, max_blocks_per_seq, dtype, *, softmax_scale=None,

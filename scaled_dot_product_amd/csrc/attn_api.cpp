@@ -124,17 +124,24 @@ attn_status_t paged_shape(const attn_paged_params_t* p) {
 
 }  // namespace
 
-extern "C" {
-
-attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const float* alibi,
-                             const void* out, const attn_fwd_params_t* p) {
-  return check_fwd(q, k, v, alibi, out, p);
+// The LSE output of attn_fwd_lse: float32 [B, Hq, Sq], 4-byte aligned, and
+// disjoint from every input and from out.
+static attn_status_t check_lse(const void* q, const void* k, const void* v, const float* alibi,
+                               const void* out, const float* lse, const attn_fwd_params_t* p) {
+  const int64_t es = p->dtype == ATTN_F32 ? 4 : 2;
+  const int64_t rows = p->B * p->Hq * p->Sq;
+  if (rows > 0 && !lse) return ATTN_ERR_NULL;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3) != 0) return ATTN_ERR_ALIGN;
+  const Span l{lse, rows * 4};
+  const int64_t qb = rows * p->D * es, kvb = p->B * p->Hkv * p->Sk * p->D * es;
+  if (overlaps(l, Span{q, qb}) || overlaps(l, Span{k, kvb}) || overlaps(l, Span{v, kvb}) ||
+      overlaps(l, Span{alibi, p->Hq * 4}) || overlaps(l, Span{out, qb}))
+    return ATTN_ERR_ALIAS;
+  return ATTN_OK;
 }
 
-attn_status_t attn_fwd(const void* q, const void* k, const void* v, const float* alibi, void* out,
-                       const attn_fwd_params_t* p, void* stream) {
-  const attn_status_t st = check_fwd(q, k, v, alibi, out, p);
-  if (st != ATTN_OK) return st;
+static attn_status_t launch_fwd(const void* q, const void* k, const void* v, const float* alibi, void* out,
+                         float* lse, const attn_fwd_params_t* p, void* stream) {
   if (p->B == 0 || p->Hq == 0 || p->Sq == 0) return ATTN_OK;
   attn::FwdProblem fp;
   fp.q = q;
@@ -142,6 +149,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, const float*
   fp.v = v;
   fp.alibi = alibi;
   fp.out = out;
+  fp.lse = lse;
   fp.B = (int)p->B;
   fp.Hq = (int)p->Hq;
   fp.Hkv = (int)p->Hkv;
@@ -158,6 +166,33 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, const float*
   const hipError_t e =
       p->dtype == ATTN_F32 ? attn::launch_fwd_f32(fp, s) : attn::launch_fwd_mfma(fp, p->dtype, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" {
+
+attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const float* alibi,
+                             const void* out, const attn_fwd_params_t* p) {
+  return check_fwd(q, k, v, alibi, out, p);
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, const float* alibi, void* out,
+                       const attn_fwd_params_t* p, void* stream) {
+  const attn_status_t st = check_fwd(q, k, v, alibi, out, p);
+  if (st != ATTN_OK) return st;
+  return launch_fwd(q, k, v, alibi, out, nullptr, p, stream);
+}
+
+attn_status_t attn_fwd_lse_check(const void* q, const void* k, const void* v, const float* alibi,
+                                 const void* out, const float* lse, const attn_fwd_params_t* p) {
+  const attn_status_t st = check_fwd(q, k, v, alibi, out, p);
+  return st != ATTN_OK ? st : check_lse(q, k, v, alibi, out, lse, p);
+}
+
+attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, const float* alibi,
+                           void* out, float* lse, const attn_fwd_params_t* p, void* stream) {
+  const attn_status_t st = attn_fwd_lse_check(q, k, v, alibi, out, lse, p);
+  if (st != ATTN_OK) return st;
+  return launch_fwd(q, k, v, alibi, out, lse, p, stream);
 }
 
 size_t attn_paged_decode_workspace_size(const attn_paged_params_t* p) {

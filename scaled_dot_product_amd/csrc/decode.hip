@@ -47,7 +47,6 @@ constexpr int kTB = 16;         // tokens per block
 constexpr int kRankMax = 2048;  // batches up to this size (and the LDS it fits) go longest-first
 constexpr int kPageWindow = 63; // blocks per page-id window: <= 64 lanes, a multiple of the ring size
 constexpr float kRescaleGap = 8.0f;
-constexpr float kLn2 = 0.69314718055994531f;
 
 struct DecArgs {
   const void* q;

@@ -24,6 +24,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define ATTN_LDS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

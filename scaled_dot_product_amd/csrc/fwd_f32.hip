@@ -24,6 +24,7 @@ struct F32Args {
   const float* v;
   const float* alibi;
   float* out;
+  float* lse;  // per-row log-sum-exp (natural log), or nullptr
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
   int wl, has_hi, dmax;
   float scale, softcap;
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
     float* orow = a.out + ((size_t)bh * Sq + qi) * D + qd * SL;
 #pragma unroll
     for (int e = 0; e < SL; ++e) orow[e] = l > 0.f ? o[e] / l : 0.f;
+    if (a.lse && qd == 0) a.lse[(size_t)bh * Sq + qi] = l > 0.f ? m + logf(l) : kNegInf;
   }
 }
 
@@ -129,6 +131,7 @@ hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream) {
   a.v = static_cast<const float*>(p.v);
   a.alibi = p.alibi;
   a.out = static_cast<float*>(p.out);
+  a.lse = p.lse;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
   a.Hq = p.Hq;

@@ -64,6 +64,7 @@ struct FwdArgs {
   const void* v;
   const float* alibi;
   void* out;
+  float* lse;   // per-row log-sum-exp (natural log), or nullptr
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
   int heavy_first;
   int wl;       // left window, -1 = unbounded
@@ -369,6 +370,11 @@ void fwd_mfma_kernel(FwdArgs a) {
   // ---- epilogue: O = o / l (0 when no key was admissible)
   const float l = halves_sum(st.l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse && qi < Sq && g == 0) {
+    // lse = ln(sum_j e^{s_j}) = ln 2 * (m + log2 l) with the weights 2^(x - m)
+    const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
+    a.lse[(size_t)bh * Sq + qi] = l > 0.f ? (m_use + __log2f(l)) * kLn2 : kNegInf;
+  }
   if (qi < Sq) {
     using E = Elem<T>;
     T* orow = O + (size_t)qi * D;
@@ -400,6 +406,7 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
   a.v = p.v;
   a.alibi = p.alibi;
   a.out = p.out;
+  a.lse = p.lse;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
   a.Hq = p.Hq;

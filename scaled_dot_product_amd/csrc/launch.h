@@ -14,6 +14,7 @@ struct FwdProblem {
   const void* v;
   const float* alibi;  // [Hq] float32 or nullptr
   void* out;
+  float* lse;     // [B, Hq, Sq] float32 natural-log LSE of each row, or nullptr
   int B, Hq, Hkv, Sq, Sk, D;
   int causal;
   int wl, wr;     // window; -1 = unbounded (already clamped to the useful range)

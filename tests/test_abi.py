@@ -103,6 +103,29 @@ def test_fwd_check_pointers():
     assert check_fwd(fwd(), al=OUT + 16) == ALIAS          # slopes inside out
 
 
+LSE = 0x100000000 * 12
+
+
+def test_fwd_lse_check():
+    """attn_fwd_lse_check: everything attn_fwd_check rejects, plus the lse
+    buffer (float32 [B, Hq, Sq]): required, 4-byte aligned, disjoint."""
+    lse_check = lambda p, lse=LSE, **kw: sdpa.attn_fwd_lse_check(
+        kw.get("q", Q), kw.get("k", K), kw.get("v", V), kw.get("al"), kw.get("out", OUT), lse, p)
+    assert lse_check(fwd()) == OK
+    assert lse_check(fwd(), lse=None) == NULL
+    assert lse_check(fwd(Sq=0), lse=None) == OK            # no rows: may be NULL
+    assert lse_check(fwd(), lse=LSE + 2) == ALIGN
+    assert lse_check(fwd(), lse=LSE + 4) == OK             # float alignment suffices
+    assert lse_check(fwd(), lse=OUT) == ALIAS               # lse == out
+    assert lse_check(fwd(), lse=Q + 64) == ALIAS            # lse inside q
+    assert lse_check(fwd(), lse=OUT - 4) == ALIAS           # last float overlaps out
+    assert lse_check(fwd(), lse=OUT - 2 * 8 * 100 * 4) == OK  # ends exactly where out starts
+    assert lse_check(fwd(D=80)) == HEAD_DIM                 # attn_fwd_check's rules first
+    lib = sdpa.library()
+    p = fwd()
+    assert lib.attn_fwd_lse(Q, K, V, None, OUT, None, ctypes.byref(p), None) == NULL
+
+
 def test_fwd_invalid_call_returns_before_any_launch():
     # attn_fwd validates first; on this GPU-less host nothing must be launched.
     lib = sdpa.library()

@@ -204,3 +204,63 @@ def test_binding_rejects_bad_arguments(gpu_lib):
     with pytest.raises(gpu_lib.AttnError) as e:
         gpu_lib.attn_fwd(q[..., :96].contiguous(), q[..., :96].contiguous(), q[..., :96].contiguous())
     assert e.value.status == 5
+
+
+# ----------------------------------------------------------------- LSE output
+
+# Largest |lse_gpu - lse_oracle| allowed.  The kernels sum the weights as they
+# enter the second matmul, i.e. rounded to the input dtype: round to nearest
+# even has unit roundoff 2^-8 for bf16 (7 stored mantissa bits) and 2^-11 for
+# f16 (10 bits), so if every weight of a row rounds the same way, ln(l) moves by
+# up to that much.  The float32 path sums exact float32 weights.  A
+# float32-accumulated score adds a relative 1e-5 of |lse|.
+LSE_TOL = {"bf16": 2.0 ** -8 + 1e-4, "f16": 2.0 ** -11 + 1e-4, "f32": 2e-6}
+
+
+def check_lse(got, ref, dtype, what):
+    g = got.detach().to("cpu", torch.float64).numpy()
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    empty = ~np.isfinite(ref)
+    assert np.all(np.isneginf(g[empty])), f"{what}: rows without keys must give -inf"
+    assert np.all(np.isfinite(g[~empty])), f"{what}: non-finite lse on a row with keys"
+    err = np.abs(g[~empty] - ref[~empty])
+    bound = LSE_TOL[dtype] + 1e-5 * np.abs(ref[~empty])
+    assert np.all(err <= bound), f"{what}: lse err {err.max(initial=0):.3g} (bound {LSE_TOL[dtype]:.3g})"
+
+
+def run_lse_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None,
+                 softcap=None, alibi=False, amp=1.0, seed=0):
+    name = (f"attn_fwd_lse {dtype} B{B} H{Hq}/{Hkv} Sq{Sq} Sk{Sk} D{D} causal={causal} "
+            f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
+    q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
+    sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
+    dev = torch.device("cuda:0")
+    args = (q.to(dev), k.to(dev), v.to(dev), None if sl is None else sl.to(dev))
+    kw = dict(softmax_scale=1.0 / math.sqrt(D), causal=causal, window_left=wl, window_right=wr,
+              softcap=softcap)
+    announce(name)
+    out, lse = sdpa.attn_fwd_lse(*args, **kw)
+    plain = sdpa.attn_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain), f"{name}: out differs from attn_fwd"
+    ref = oracle.sdpa_lse_f64(W.to_f64(q), W.to_f64(k), scale=kw["softmax_scale"], causal=causal,
+                              window_left=wl, window_right=wr, softcap=softcap,
+                              alibi=None if sl is None else W.to_f64(sl))
+    check_lse(lse, ref, dtype, name)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_lse_parity(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = SMALL[case]
+    run_lse_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=300 + case, **kw)
+
+
+@pytest.mark.parametrize("case", [
+    (1, 4, 2, 200, 250, 128, dict(causal=True)),
+    (2, 2, 1, 150, 150, 64, dict(causal=True, wl=30, wr=0, softcap=8.0, alibi=True)),
+    (1, 2, 2, 100, 70, 128, dict(causal=True)),          # Sq > Sk: rows 0..29 have no key
+])
+def test_lse_parity_f32(gpu_lib, case):
+    B, Hq, Hkv, Sq, Sk, D, kw = case
+    run_lse_case(gpu_lib, "f32", B, Hq, Hkv, Sq, Sk, D, seed=9, **kw)
