@@ -1,0 +1,63 @@
+"""The library's launches under HIP graph capture (torch.cuda.CUDAGraph).
+
+Host launch overhead dominates short decode and prefill calls (derivation
+page, the section on host overhead and graph replay), so callers capture them.
+Every buffer is allocated before capture and the library issues no memset or
+allocation of its own; each replay is checked bitwise against the eager
+result, with eager work and synchronisation between replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager(gpu_lib):
+    sdpa = gpu_lib
+    dev = torch.device("cuda:0")
+    announce("graph capture: attn_fwd + attn_fwd_lse + attn_paged_decode")
+    q, k, v = W.random_dense("bf16", 1, 8, 2, 200, 300, 128, 41, 1.0)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(q)
+    out2 = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, kp, vp, table, lens, _ = W.paged_inputs(W.PAGED_DECODE, seed=42, seq_lens=[700, 1500, 64, 3000])
+    dq, kp, vp = dq[:4].to(dev), kp.to(dev), vp.to(dev)
+    table, lens = table[:4].to(dev), lens.to(dev)
+    dout = torch.empty_like(dq)
+    p = sdpa.attn_paged_params(tuple(dq.shape), tuple(kp.shape), table.shape[1], dq.dtype, num_splits=8)
+    ws = torch.zeros(sdpa.attn_paged_decode_workspace_size(p), dtype=torch.uint8, device=dev)
+    scale = 1.0 / np.sqrt(128)
+
+    def work():
+        sdpa.attn_fwd(q, k, v, None, out, softmax_scale=scale, causal=True)
+        sdpa.attn_fwd_lse(q, k, v, None, out2, lse, softmax_scale=scale, causal=True, window_left=64)
+        sdpa.attn_paged_decode(dq, kp, vp, table, lens, None, dout, softmax_scale=scale,
+                               num_splits=8, workspace=ws)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, out2, lse, dout)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm up on the capture stream
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (out, out2, lse, dout):
+            t.fill_(7.0)                  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "out_lse", "lse", "decode"), (out, out2, lse, dout), eager):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from eager"
