@@ -16,6 +16,7 @@ from .sdpa import (  # noqa: F401
     kv_head_of,
     lse_merge_f64,
     paged_decode_f64,
+    paged_prefill_varlen_f64,
     paged_gather,
     query_positions,
     sdpa_naive_f64,

@@ -51,6 +51,7 @@ __all__ = [
     "lse_merge_f64",
     "paged_gather",
     "paged_decode_f64",
+    "paged_prefill_varlen_f64",
     "admissible_pair_count",
 ]
 
@@ -357,6 +358,45 @@ def paged_decode_f64(q, k_pool, v_pool, block_table, seq_lens, *, scale,
         vb = np.transpose(vb, (1, 0, 2))[None]
         out[b:b + 1] = sdpa_naive_f64(q[b:b + 1], kb, vb, scale=scale,
                                       causal=True, softcap=softcap, alibi=alibi)
+    return out
+
+
+def paged_prefill_varlen_f64(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, *, scale,
+                             causal=True, window_left=None, window_right=None, softcap=None,
+                             alibi=None):
+    """Variable-length prefill over the paged pool (kernel-contract page,
+    ``attention_paged_naive``, with the packed query layout of the derivation
+    page's section 5: queries ``[total_q, Hq, D]`` with a ``cu_seqlens_q``
+    prefix sum, and each sequence's key length in ``seq_lens``).
+
+    Sequence ``b`` owns query rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1``;
+    its live keys ``0 .. seq_lens[b]-1`` are gathered with :func:`paged_gather`
+    and the dense definition is applied with query row ``i`` at position
+    ``seq_lens[b] - Sq_b + i`` (the implicit bottom-right alignment) -- with
+    the causal mask when ``causal``, windows as for the dense form.  Returns
+    float64 ``[total_q, Hq, D]``; rows outside every sequence stay zero.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_pool = np.asarray(k_pool)
+    v_pool = np.asarray(v_pool)
+    if q.ndim != 3 or k_pool.shape != v_pool.shape or k_pool.ndim != 4:
+        raise ValueError("q must be [total_q, Hq, D]; pools [num_blocks, block_size, Hkv, D]")
+    cu = [int(c) for c in cu_seqlens_q]
+    if any(b < a for a, b in zip(cu, cu[1:])) or (cu and (cu[0] < 0 or cu[-1] > q.shape[0])):
+        raise ValueError("cu_seqlens_q must be a non-decreasing prefix sum within total_q")
+    block_size = k_pool.shape[1]
+    out = np.zeros(q.shape, dtype=np.float64)
+    for b in range(len(cu) - 1):
+        r0, r1 = cu[b], cu[b + 1]
+        if r1 == r0:
+            continue
+        ctx = int(seq_lens[b])
+        kb = np.transpose(paged_gather(k_pool, block_table, ctx, b, block_size), (1, 0, 2))[None]
+        vb = np.transpose(paged_gather(v_pool, block_table, ctx, b, block_size), (1, 0, 2))[None]
+        qb = np.transpose(q[r0:r1], (1, 0, 2))[None]            # [1, Hq, Sq_b, D]
+        ob = sdpa_naive_f64(qb, kb, vb, scale=scale, causal=causal, window_left=window_left,
+                            window_right=window_right, softcap=softcap, alibi=alibi)
+        out[r0:r1] = np.transpose(ob[0], (1, 0, 2))
     return out
 
 

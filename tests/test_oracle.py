@@ -430,3 +430,68 @@ def test_lse_shift_is_additive():
         sh = osd.sdpa_lse_f64(q, k + w, scale=0.5, causal=True)
         delta = 0.5 * (q[0] @ w)                    # [Hq, Sq]
         np.testing.assert_allclose(sh[0] - base[0], delta, rtol=1e-10, atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# Variable-length prefill over the paged pool
+# --------------------------------------------------------------------------
+
+def _varlen_case(rng, Hq=2, Hkv=1, D=3, bs=4, sq=(3, 0, 5), sk=(6, 2, 3)):
+    q8 = lambda *s: np.round(rng.standard_normal(s) * 8) / 8
+    nblk = [(c + bs - 1) // bs for c in sk]
+    nb = sum(nblk)
+    perm = rng.permutation(nb)
+    table = np.full((len(sk), max(nblk)), -1, dtype=np.int64)
+    pos = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    cu = np.concatenate([[0], np.cumsum(sq)]).astype(np.int64)
+    return dict(q=q8(int(cu[-1]), Hq, D), kp=q8(nb, bs, Hkv, D), vp=q8(nb, bs, Hkv, D),
+                table=table, lens=np.array(sk), cu=cu)
+
+
+@pytest.mark.parametrize("kw", [dict(causal=True), dict(causal=True, softcap=0.7, alibi=[0.3, 0.6]),
+                                dict(causal=False, window_left=1, window_right=1)])
+def test_varlen_matches_decimal_bruteforce(kw):
+    """Each sequence's rows against the 50-digit definition on its own keys,
+    gathered here by plain indexing of the pool (block table, slot)."""
+    from oracle.bruteforce import sdpa_bruteforce
+    c = _varlen_case(np.random.default_rng(3))
+    kw = dict(kw)
+    got = osd.paged_prefill_varlen_f64(c["q"], c["kp"], c["vp"], c["table"], c["lens"], c["cu"],
+                                       scale=0.8, **kw)
+    bs = c["kp"].shape[1]
+    for b in range(len(c["lens"])):
+        r0, r1 = int(c["cu"][b]), int(c["cu"][b + 1])
+        ctx = int(c["lens"][b])
+        if r1 == r0:
+            continue
+        krows = [[c["kp"][c["table"][b][t // bs]][t % bs][g].tolist() for t in range(ctx)]
+                 for g in range(c["kp"].shape[2])]
+        vrows = [[c["vp"][c["table"][b][t // bs]][t % bs][g].tolist() for t in range(ctx)]
+                 for g in range(c["vp"].shape[2])]
+        qrows = [[c["q"][r][h].tolist() for r in range(r0, r1)] for h in range(c["q"].shape[1])]
+        ref = np.array(sdpa_bruteforce([qrows], [krows], [vrows], scale=0.8, **kw), dtype=np.float64)
+        np.testing.assert_allclose(np.transpose(got[r0:r1], (1, 0, 2)), ref[0], rtol=1e-12, atol=1e-12)
+    # sequence 2 has 5 queries but 3 keys: causal rows 0 and 1 sit before every key
+    if kw.get("causal"):
+        r0 = int(c["cu"][2])
+        assert np.all(got[r0:r0 + 2] == 0) and np.all(np.abs(got[r0 + 2:r0 + 5]).sum(-1) > 0)
+
+
+def test_varlen_equal_lengths_is_the_paged_form():
+    """With every sequence of the same query length, packing the rows is only
+    a relayout of the [B, Hq, Sq, D] paged form."""
+    rng = np.random.default_rng(8)
+    c = _varlen_case(rng, Hq=4, Hkv=2, D=5, bs=3, sq=(4, 4, 4), sk=(7, 4, 9))
+    got = osd.paged_prefill_varlen_f64(c["q"], c["kp"], c["vp"], c["table"], c["lens"], c["cu"],
+                                       scale=0.5, causal=True, alibi=[0.1, 0.2, 0.3, 0.4])
+    q4 = np.transpose(c["q"].reshape(3, 4, 4, 5), (0, 2, 1, 3))   # [B, Hq, Sq, D]
+    ref = osd.paged_decode_f64(q4, c["kp"], c["vp"], c["table"], c["lens"], scale=0.5,
+                               alibi=[0.1, 0.2, 0.3, 0.4])
+    np.testing.assert_allclose(got.reshape(3, 4, 4, 5), np.transpose(ref, (0, 2, 1, 3)),
+                               rtol=1e-13, atol=1e-14)
+    with pytest.raises(ValueError):
+        osd.paged_prefill_varlen_f64(c["q"], c["kp"], c["vp"], c["table"], c["lens"],
+                                     [0, 5, 3, 12], scale=0.5)
