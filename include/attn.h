@@ -183,6 +183,61 @@ attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v
                                 int32_t* error_flag,
                                 const attn_paged_params_t* p, void* stream);
 
+/* Parameters of attn_paged_prefill: variable-length prefill over the paged
+ * pool (kernel-contract page, attention_paged_naive, with the packed query
+ * layout of the derivation page, section 5: queries [total_q, Hq, D] with a
+ * cu_seqlens_q prefix sum, per-sequence key lengths in seq_lens). */
+typedef struct attn_varlen_params {
+  int64_t B;                   /* sequences                                      */
+  int64_t Hq;                  /* query heads; a multiple of Hkv                 */
+  int64_t Hkv;                 /* key/value heads                                */
+  int64_t D;                   /* head dim: 64 or 128                            */
+  int64_t total_q;             /* rows of q and out                              */
+  int64_t max_seqlen_q;        /* >= cu_seqlens_q[b+1] - cu_seqlens_q[b] for all b */
+  int64_t num_blocks;          /* physical blocks in each pool                   */
+  int64_t block_size;          /* tokens per block: a multiple of 64             */
+  int64_t max_blocks_per_seq;  /* columns of block_table                         */
+  int32_t dtype;               /* attn_dtype_t of q, pools and out (F16, BF16)   */
+  int32_t causal;              /* nonzero: key t admissible iff t <= i'          */
+  int64_t window_left;         /* -1: unbounded; else keys t >= i' - window_left */
+  int64_t window_right;        /* -1: unbounded; else keys t <= i' + window_right*/
+  float softmax_scale;         /* finite, >= 0                                   */
+  float softcap;               /* 0: off; > 0: softcap * tanh(s / softcap)       */
+} attn_varlen_params_t;
+
+/* Host-only validation of an attn_paged_prefill call (no HIP call is made).
+ *   q             [total_q, Hq, D]                      dtype
+ *   k_pool,v_pool [num_blocks, block_size, Hkv, D]      dtype
+ *   block_table   [B, max_blocks_per_seq] int32
+ *   seq_lens      [B] int32: live keys of sequence b
+ *   cu_seqlens_q  [B + 1] int32: sequence b owns query rows
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1; row i of it sits
+ *                 at position i' = seq_lens[b] - Sq_b + i (bottom-right)
+ *   alibi         [Hq] float32 or NULL (ALiBi distance t - i')
+ *   out           [total_q, Hq, D] dtype
+ *   error_flag    NULL or one device int32.
+ * block_size must be a multiple of 64 (ATTN_ERR_UNSUPPORTED otherwise), as
+ * must be F32 (ATTN_ERR_UNSUPPORTED). */
+attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* cu_seqlens_q, const float* alibi,
+                                       const void* out, const int32_t* error_flag,
+                                       const attn_varlen_params_t* p);
+
+/* Variable-length prefill (or chunked prefill) over the paged pool:
+ * validates as attn_paged_prefill_check, then enqueues one kernel on `stream`
+ * and returns.  Rows of out outside every sequence are not written.
+ * Device-side errors do not fault: a prefix sum outside [0, total_q] or a
+ * sequence longer than max_seqlen_q is clamped, a seq_len outside
+ * [0, max_blocks_per_seq * block_size] is clamped, and a block_table entry
+ * outside [0, num_blocks) masks its keys; each stores 1 to *error_flag when
+ * error_flag is not NULL.  A row with no admissible key outputs zeros. */
+attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* cu_seqlens_q, const float* alibi, void* out,
+                                 int32_t* error_flag, const attn_varlen_params_t* p,
+                                 void* stream);
+
 /* Static string naming a status code. */
 const char* attn_status_str(attn_status_t status);
 

@@ -10,6 +10,10 @@ fails to load, every call raises.
     attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
              window_left=None, window_right=None, softcap=None, stream=None)
     attn_fwd_lse(q, k, v, alibi=None, out=None, lse=None, *, ...)  -> (out, lse)
+    attn_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q,
+                       alibi=None, out=None, *, max_seqlen_q=None, softmax_scale=None,
+                       causal=True, window_left=None, window_right=None,
+                       softcap=None, error_flag=None, stream=None)
     attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
                       out=None, *, softmax_scale=None, softcap=None,
                       num_splits=8, workspace=None, error_flag=None, stream=None)
@@ -28,6 +32,7 @@ __all__ = [
     "attn_fwd", "attn_fwd_check", "attn_fwd_params", "attn_fwd_lse", "attn_fwd_lse_check",
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
     "attn_paged_params", "attn_status_str", "attn_version",
+    "attn_paged_prefill", "attn_paged_prefill_check", "attn_varlen_params",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16",
 ]
 
@@ -67,6 +72,16 @@ class attn_paged_params_t(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("softcap", ctypes.c_float)]
 
 
+class attn_varlen_params_t(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("total_q", ctypes.c_int64), ("max_seqlen_q", ctypes.c_int64),
+                ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("max_blocks_per_seq", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("window_left", ctypes.c_int64),
+                ("window_right", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
+                ("softcap", ctypes.c_float)]
+
+
 _lib = None
 _VP = ctypes.c_void_p
 
@@ -96,6 +111,11 @@ def library():
     lib.attn_paged_decode_check.restype = ctypes.c_int
     lib.attn_paged_decode.argtypes = [_VP] * 8 + [ctypes.c_size_t, _VP, pag_p, _VP]
     lib.attn_paged_decode.restype = ctypes.c_int
+    var_p = ctypes.POINTER(attn_varlen_params_t)
+    lib.attn_paged_prefill_check.argtypes = [_VP] * 9 + [var_p]
+    lib.attn_paged_prefill_check.restype = ctypes.c_int
+    lib.attn_paged_prefill.argtypes = [_VP] * 9 + [var_p, _VP]
+    lib.attn_paged_prefill.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -281,4 +301,76 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=
                                _ptr(error_flag), ctypes.byref(p), _stream_handle(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_paged_decode")
+    return out
+
+
+def attn_varlen_params(q_shape, pool_shape, B, max_blocks_per_seq, max_seqlen_q, dtype, *,
+                       softmax_scale=None, causal=True, window_left=None, window_right=None,
+                       softcap=None) -> attn_varlen_params_t:
+    total_q, Hq, D = q_shape
+    num_blocks, block_size, Hkv, _ = pool_shape
+    return attn_varlen_params_t(
+        B=B, Hq=Hq, Hkv=Hkv, D=D, total_q=total_q, max_seqlen_q=int(max_seqlen_q),
+        num_blocks=num_blocks, block_size=block_size, max_blocks_per_seq=max_blocks_per_seq,
+        dtype=_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+        causal=1 if causal else 0,
+        window_left=-1 if window_left is None else int(window_left),
+        window_right=-1 if window_right is None else int(window_right),
+        softmax_scale=(1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale),
+        softcap=0.0 if not softcap else float(softcap))
+
+
+def attn_paged_prefill_check(q_ptr, kp_ptr, vp_ptr, table_ptr, lens_ptr, cu_ptr, alibi_ptr,
+                             out_ptr, err_ptr, params: attn_varlen_params_t) -> int:
+    """Host-only argument check of attn_paged_prefill (no HIP call)."""
+    return int(library().attn_paged_prefill_check(
+        q_ptr, kp_ptr, vp_ptr, table_ptr, lens_ptr, cu_ptr, alibi_ptr, out_ptr, err_ptr,
+        None if params is None else ctypes.byref(params)))
+
+
+def attn_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, alibi=None,
+                       out=None, *, max_seqlen_q=None, softmax_scale=None, causal=True,
+                       window_left=None, window_right=None, softcap=None, error_flag=None,
+                       stream=None):
+    """Variable-length prefill over the paged pool (see attn.h).  ``q`` and
+    ``out`` are packed ``[total_q, Hq, D]``; pass ``max_seqlen_q`` to avoid
+    reading ``cu_seqlens_q`` back to the host."""
+    lib = library()
+    dev = q.device
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_table", block_table), ("seq_lens", seq_lens),
+                    ("cu_seqlens_q", cu_seqlens_q), ("alibi", alibi), ("out", out),
+                    ("error_flag", error_flag)):
+        _need_device(name, t, dev)
+    if q.dim() != 3:
+        raise ValueError("q must be packed [total_q, Hq, D]")
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or k_pool.shape[3] != q.shape[2]:
+        raise ValueError("pools must both be [num_blocks, block_size, Hkv, D] with q's D")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q and the pools must share one dtype")
+    B = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
+    if seq_lens.dtype != torch.int32 or B < 0:
+        raise ValueError("seq_lens must be int32 [B]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_blocks_per_seq]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_q.shape != (B + 1,):
+        raise ValueError("cu_seqlens_q must be int32 [B + 1]")
+    if alibi is not None and (alibi.dtype != torch.float32 or alibi.shape != (q.shape[1],)):
+        raise ValueError("alibi slopes must be float32 [Hq]")
+    if error_flag is not None and (error_flag.dtype != torch.int32 or error_flag.numel() != 1):
+        raise ValueError("error_flag must be one int32")
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B > 0 else 0
+    p = attn_varlen_params(tuple(q.shape), tuple(k_pool.shape), B, block_table.shape[1],
+                           max_seqlen_q, q.dtype, softmax_scale=softmax_scale, causal=causal,
+                           window_left=window_left, window_right=window_right, softcap=softcap)
+    if out is None:
+        out = torch.zeros_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    st = lib.attn_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(alibi), _ptr(out),
+                                _ptr(error_flag), ctypes.byref(p), _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_paged_prefill")
     return out

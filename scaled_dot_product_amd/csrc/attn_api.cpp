@@ -24,6 +24,18 @@ hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream) {
     return p.D == 128 ? launch_fwd_mfma_bf16_d128(p, stream) : launch_fwd_mfma_bf16_d64(p, stream);
   return p.D == 128 ? launch_fwd_mfma_f16_d128(p, stream) : launch_fwd_mfma_f16_d64(p, stream);
 }
+
+hipError_t launch_paged_prefill_bf16_d128(const PagedPrefillProblem& p, hipStream_t stream);
+hipError_t launch_paged_prefill_bf16_d64(const PagedPrefillProblem& p, hipStream_t stream);
+hipError_t launch_paged_prefill_f16_d128(const PagedPrefillProblem& p, hipStream_t stream);
+hipError_t launch_paged_prefill_f16_d64(const PagedPrefillProblem& p, hipStream_t stream);
+
+hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream) {
+  if (dtype == ATTN_BF16)
+    return p.D == 128 ? launch_paged_prefill_bf16_d128(p, stream)
+                      : launch_paged_prefill_bf16_d64(p, stream);
+  return p.D == 128 ? launch_paged_prefill_f16_d128(p, stream) : launch_paged_prefill_f16_d64(p, stream);
+}
 }  // namespace attn
 
 namespace {
@@ -270,6 +282,94 @@ attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v
   dp.scale = p->softmax_scale;
   dp.softcap = p->softcap;
   const hipError_t e = attn::launch_paged_decode(dp, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* cu_seqlens_q, const float* alibi,
+                                       const void* out, const int32_t* error_flag,
+                                       const attn_varlen_params_t* p) {
+  if (!p) return ATTN_ERR_NULL;
+  if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
+  if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->D < 0 || p->total_q < 0 || p->max_seqlen_q < 0 ||
+      p->num_blocks < 0 || p->max_blocks_per_seq < 0 || p->block_size < 1)
+    return ATTN_ERR_SHAPE;
+  if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
+  if (p->D != 64 && p->D != 128) return ATTN_ERR_HEAD_DIM;
+  if (p->block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
+  if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_PARAM;
+  if (p->total_q > kMaxLen || p->max_seqlen_q > kMaxLen) return ATTN_ERR_SHAPE;
+  const int64_t es = elem_bytes(p->dtype);
+  int64_t cap, bh, grid, q_bytes, pool_bytes;
+  if (!mul(p->max_blocks_per_seq, p->block_size, &cap) || cap > kMaxLen) return ATTN_ERR_SHAPE;
+  if (!mul(p->B, p->Hq, &bh) || bh > kMaxLen) return ATTN_ERR_SHAPE;
+  if (!mul(bh, (p->max_seqlen_q + 127) / 128, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (!mul4(p->total_q, p->Hq, p->D, es, &q_bytes)) return ATTN_ERR_SHAPE;
+  if (!mul4(p->num_blocks, p->block_size, p->Hkv, p->D * es, &pool_bytes)) return ATTN_ERR_SHAPE;
+  // one 64-key tile spans 64 token rows of the pool: its offsets must fit int32
+  if (64 * p->Hkv * p->D * es > INT32_MAX) return ATTN_ERR_SHAPE;
+  const int64_t table_bytes = p->B * p->max_blocks_per_seq * 4;
+  const int64_t lens_bytes = p->B * 4, cu_bytes = (p->B + 1) * 4;
+  const bool work = q_bytes > 0 && p->B > 0;
+  if (work) {
+    if (!q || !out || !seq_lens || !cu_seqlens_q) return ATTN_ERR_NULL;
+    if (table_bytes > 0 && !block_table) return ATTN_ERR_NULL;
+    if (pool_bytes > 0 && (!k_pool || !v_pool)) return ATTN_ERR_NULL;
+  }
+  const void* ptrs16[] = {q, k_pool, v_pool, alibi, out};
+  for (const void* ptr : ptrs16)
+    if (ptr && !aligned16(ptr)) return ATTN_ERR_ALIGN;
+  const void* ptrs4[] = {block_table, seq_lens, cu_seqlens_q, error_flag};
+  for (const void* ptr : ptrs4)
+    if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3u)) return ATTN_ERR_ALIGN;
+  const Span o{out, q_bytes};
+  const Span inputs[] = {{q, q_bytes},          {k_pool, pool_bytes},    {v_pool, pool_bytes},
+                         {block_table, table_bytes}, {seq_lens, lens_bytes}, {cu_seqlens_q, cu_bytes},
+                         {alibi, p->Hq * 4},    {error_flag, 4}};
+  for (const Span& in : inputs)
+    if (overlaps(o, in)) return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* cu_seqlens_q, const float* alibi, void* out,
+                                 int32_t* error_flag, const attn_varlen_params_t* p,
+                                 void* stream) {
+  const attn_status_t st = attn_paged_prefill_check(q, k_pool, v_pool, block_table, seq_lens,
+                                                    cu_seqlens_q, alibi, out, error_flag, p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Hq == 0 || p->total_q == 0 || p->max_seqlen_q == 0) return ATTN_OK;
+  attn::PagedPrefillProblem pp;
+  pp.q = q;
+  pp.k_pool = k_pool;
+  pp.v_pool = v_pool;
+  pp.block_table = block_table;
+  pp.seq_lens = seq_lens;
+  pp.cu_seqlens_q = cu_seqlens_q;
+  pp.alibi = alibi;
+  pp.out = out;
+  pp.error_flag = error_flag;
+  pp.B = (int)p->B;
+  pp.Hq = (int)p->Hq;
+  pp.Hkv = (int)p->Hkv;
+  pp.D = (int)p->D;
+  pp.total_q = (int)p->total_q;
+  pp.max_sq = (int)p->max_seqlen_q;
+  pp.num_blocks = p->num_blocks > INT32_MAX ? INT32_MAX : (int)p->num_blocks;
+  pp.block_size = (int)p->block_size;
+  pp.max_blocks = (int)p->max_blocks_per_seq;
+  pp.causal = p->causal != 0;
+  const int64_t cap = p->max_blocks_per_seq * p->block_size;
+  // windows wider than every possible distance are the same as no window
+  pp.wl = (p->window_left < 0 || p->window_left >= cap) ? -1 : (int)p->window_left;
+  pp.wr = (p->window_right < 0 || p->window_right >= p->max_seqlen_q) ? -1 : (int)p->window_right;
+  pp.scale = p->softmax_scale;
+  pp.softcap = p->softcap;
+  const hipError_t e = attn::launch_paged_prefill(pp, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -56,7 +56,7 @@ constexpr int kBM = kNW * kQW;     // query rows per workgroup
 constexpr int kThreads = kNW * 64;
 constexpr float kRescaleGap = 8.0f;  // log2 units: weights stay <= 2^8
 
-enum : int { F_MASK = 1, F_SOFTCAP = 2, F_ALIBI = 4 };
+enum : int { F_MASK = 1, F_SOFTCAP = 2, F_ALIBI = 4, F_PAGED = 8 };
 
 struct FwdArgs {
   const void* q;
@@ -67,6 +67,13 @@ struct FwdArgs {
   float* lse;   // per-row log-sum-exp (natural log), or nullptr
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
   int heavy_first;
+  // paged, variable-length form (F_PAGED): queries packed [total_q, Hq, D]
+  // with a prefix sum, K/V in a [num_blocks, bs, Hkv, D] pool
+  const int32_t* table;   // [B, maxb] physical block of each logical block
+  const int32_t* kv_lens; // [B] live keys of each sequence
+  const int32_t* cu_q;    // [B + 1] query row prefix sum
+  int32_t* err;           // device error flag or nullptr
+  int maxb, bs, num_blocks, total_q, max_sq;
   int wl;       // left window, -1 = unbounded
   int has_hi;   // is j - i' bounded above?
   int dmax;     // that bound (causal and/or right window)
@@ -121,15 +128,14 @@ __device__ __forceinline__ void qk_tile(const u32x4* Ks, const u32x4* qf, int ln
 // Transform + mask + online update of one tile's scores, then O += P V.
 template <typename T, int D, int FLAGS>
 __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowState<D / 32>& st,
-                                           const FwdArgs& a, int n0, int ip, int ipa_w, int ipb_w,
-                                           float slope_l2, int lane, int g) {
+                                           const FwdArgs& a, int Sk, int n0, int ip, int ipa_w,
+                                           int ipb_w, float slope_l2, int lane, int g) {
   using E = Elem<T>;
   constexpr bool MASK = (FLAGS & F_MASK) != 0;
   constexpr bool SOFTCAP = (FLAGS & F_SOFTCAP) != 0;
   constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
   constexpr bool kRaw = !SOFTCAP && !ALIBI;  // max on raw scores, scale folded into exp
   constexpr int DB = D / 32;
-  const int Sk = a.Sk;
   const int rb = n0 + 4 * g - ip;            // j - i' of element offset 0
 
   if constexpr (!kRaw) {
@@ -234,6 +240,7 @@ template <typename T, int D, int FLAGS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdArgs a) {
   constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
+  constexpr bool PAGED = (FLAGS & F_PAGED) != 0;
   constexpr int NC = D / 8;              // 16-byte chunks per K/V row
   constexpr int TC = kBN * NC;           // chunks per K (or V) tile
   constexpr int CPT = TC / kThreads;     // chunks per thread per tile and tensor
@@ -260,13 +267,37 @@ void fwd_mfma_kernel(FwdArgs a) {
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int kvh = h / a.group;
-  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
   const int m0 = qb * kBM;
-
-  const T* Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * Sq * D;
-  const T* K = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * Sk * D;
-  const T* V = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * Sk * D;
-  T* O = reinterpret_cast<T*>(a.out) + (size_t)bh * Sq * D;
+  int Sq = a.Sq, Sk = a.Sk;
+  int q_row = D, kv_row = D;  // elements between consecutive Q/O rows and K/V rows
+  const T* Q;
+  const T* K;
+  const T* V;
+  T* O;
+  if constexpr (PAGED) {
+    // this sequence's query rows [q0, q0 + Sq) and live keys [0, Sk), clamped
+    // into the buffers (flagged when the prefix sum or a length was outside)
+    const int c0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+    const int c1 = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]);
+    const int q0 = min(max(c0, 0), a.total_q), q1 = min(max(c1, q0), a.total_q);
+    const int kl = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
+    Sq = min(q1 - q0, a.max_sq);
+    Sk = min(max(kl, 0), a.maxb * a.bs);
+    if ((q0 != c0 || q1 != c1 || Sq != q1 - q0 || Sk != kl) && a.err && tid == 0) *a.err = 1;
+    if (m0 >= Sq) return;  // no rows of this sequence in this block (whole workgroup)
+    q_row = a.Hq * D;
+    kv_row = a.Hkv * D;
+    Q = reinterpret_cast<const T*>(a.q) + ((size_t)q0 * a.Hq + h) * D;
+    O = reinterpret_cast<T*>(a.out) + ((size_t)q0 * a.Hq + h) * D;
+    K = reinterpret_cast<const T*>(a.k) + (size_t)kvh * D;  // pool; tiles add their block
+    V = reinterpret_cast<const T*>(a.v) + (size_t)kvh * D;
+  } else {
+    Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * Sq * D;
+    K = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * Sk * D;
+    V = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * Sk * D;
+    O = reinterpret_cast<T*>(a.out) + (size_t)bh * Sq * D;
+  }
+  const int off = Sk - Sq;
 
   // ---- admissible key ranges: [lo(i'_first), hi(i'_last))
   auto key_lo = [&](int ipa) { return a.wl >= 0 ? max(0, ipa - a.wl) : 0; };
@@ -292,7 +323,7 @@ void fwd_mfma_kernel(FwdArgs a) {
   u32x4 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
-    qf[s] = qi < Sq ? load16(Q + (size_t)qi * D + 16 * s + 8 * g) : zero_u32x4();
+    qf[s] = qi < Sq ? load16(Q + (size_t)qi * q_row + 16 * s + 8 * g) : zero_u32x4();
 
   float slope_l2 = 0.f;
   if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
@@ -305,26 +336,54 @@ void fwd_mfma_kernel(FwdArgs a) {
 
   // ---- asynchronous tile copies global -> LDS.  Chunk c of a tile sits at
   // LDS slot c, i.e. row c / NC, swizzled chunk c % NC; keys past Sk read 0.
-  // one head's K (or V) is < 2 GiB (checked by the host), so offsets fit int32
+  // One head's K (or V) is < 2 GiB, and a paged tile spans < 2 GiB of the pool
+  // (both checked by the host), so offsets within a tile fit int32.
   const int kv_bytes = Sk * D * (int)sizeof(T);
-  auto dma_k = [&](u32x4* dst, int t) {
-    const int base = t * kBN * D * (int)sizeof(T);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(reinterpret_cast<const char*>(K) + base, kv_bytes - base);
+  // Paged: tile t is rows (t % m) * 64 .. + 63 of logical block t / m (m =
+  // bs / 64).  Lane j of page_reg holds the physical block of logical block
+  // pbase + j; the window moves forward when a copy needs a later block.
+  const int m_tiles = PAGED ? a.bs / kBN : 1;
+  int pbase = 0, page_reg = 0;
+  auto load_pages = [&](int first) {
+    pbase = first;
+    const int j = first + lane;
+    page_reg = j < a.maxb ? a.table[(size_t)b * a.maxb + j] : 0;
+  };
+  bool bad_page = false;  // a table entry outside the pool was used (wave-uniform)
+  // Buffer resource of tile t; `ok` is false for a tile whose block is outside
+  // the pool (its keys are masked, its copies read nothing).
+  auto tile_rsrc = [&](const T* base_t, int t, bool& ok) -> __amdgpu_buffer_rsrc_t {
+    if constexpr (PAGED) {
+      const int lb = t / m_tiles;
+      const int phys = __builtin_amdgcn_readlane(page_reg, lb - pbase);
+      const int rows = min(max(Sk - t * kBN, 0), kBN);
+      ok = rows == 0 || (unsigned)phys < (unsigned)a.num_blocks;
+      bad_page |= !ok;
+      const long long row0 = ok ? (long long)phys * a.bs + (t - lb * m_tiles) * kBN : 0;
+      return make_rsrc32(base_t + row0 * kv_row, ok ? rows * kv_row * (int)sizeof(T) : 0);
+    } else {
+      ok = true;
+      const int base = t * kBN * D * (int)sizeof(T);
+      return make_rsrc32(reinterpret_cast<const char*>(base_t) + base, kv_bytes - base);
+    }
+  };
+  auto dma_k = [&](u32x4* dst, int t, bool& ok) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(K, t, ok);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / NC, pc = c % NC;
-      dma16(rs, dst + i * kThreads + wave * 64, (r * D + (pc ^ swz_k<D>(r)) * 8) * (int)sizeof(T));
+      dma16(rs, dst + i * kThreads + wave * 64, (r * kv_row + (pc ^ swz_k<D>(r)) * 8) * (int)sizeof(T));
     }
   };
   auto dma_v = [&](u32x4* dst, int t) {
-    const int base = t * kBN * D * (int)sizeof(T);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(reinterpret_cast<const char*>(V) + base, kv_bytes - base);
+    bool ok_unused;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(V, t, ok_unused);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / NC, pc = c % NC;
-      dma16(rs, dst + i * kThreads + wave * 64, (r * D + (pc ^ swz_v<D>(r)) * 8) * (int)sizeof(T));
+      dma16(rs, dst + i * kThreads + wave * 64, (r * kv_row + (pc ^ swz_v<D>(r)) * 8) * (int)sizeof(T));
     }
   };
 
@@ -333,24 +392,42 @@ void fwd_mfma_kernel(FwdArgs a) {
   //            S(i+1) = K(i+1) Q^T   (matrix cores, into the same registers)
   //   while K(i+2) and V(i+1) stream into the buffers freed by step i-1.
   // K(i) lives in kbuf[i % 2], V(i) in vbuf[i % 2].
+  // Paged: kok0 / kok1 say whether the tile in kbuf0 / kbuf1 lies in the pool;
+  // a tile that does not has its scores set to -inf right after its QK.
   const int n = t_end - t_begin;
   floatx16 sc[2];
+  bool kok0 = true, kok1 = true;
+  auto mask_bad = [&](bool ok) {
+    if (PAGED && !ok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = kNegInf;
+    }
+  };
+  if constexpr (PAGED) load_pages(t_begin / m_tiles);
   if (n > 0) {
-    dma_k(kbuf0, t_begin);
+    dma_k(kbuf0, t_begin, kok0);
     dma_v(vbuf0, t_begin);
-    if (n > 1) dma_k(kbuf1, t_begin + 1);
+    if (n > 1) dma_k(kbuf1, t_begin + 1, kok1);
     wait_vmem();
     __syncthreads();
-    if (live(t_begin)) qk_tile<T, D>(kbuf0, qf, ln, g, sc);
+    if (live(t_begin)) {
+      qk_tile<T, D>(kbuf0, qf, ln, g, sc);
+      mask_bad(kok0);
+    }
   }
-  auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload) {
+  auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload,
+                  const bool& ok_read, bool& ok_load) {
     const int t = t_begin + i;
     wait_vmem();
     __syncthreads();  // K(i+1), V(i) landed; everyone is done with step i-1's buffers
-    if (i + 2 < n) dma_k(kload, t + 2);
+    if constexpr (PAGED) {
+      // the copies below read blocks (t + 1) / m and (t + 2) / m
+      if (i + 2 < n && (t + 2) / m_tiles - pbase >= 64) load_pages((t + 1) / m_tiles);
+    }
+    if (i + 2 < n) dma_k(kload, t + 2, ok_load);
     if (i + 1 < n) dma_v(vload, t + 1);
     if (live(t))
-      softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a, t * kBN, ip, ipa_w,
+      softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a, Sk, t * kBN, ip, ipa_w,
                               ipb_w, slope_l2, lane, g);
     // S(i+1) overwrites S(i), already consumed: one score buffer per wave.
     // This matrix phase runs at raised wave priority so that, of the two waves
@@ -361,11 +438,13 @@ void fwd_mfma_kernel(FwdArgs a) {
     if (i + 1 < n && live(t + 1)) qk_tile<T, D>(kread, qf, ln, g, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
+    if (i + 1 < n && live(t + 1)) mask_bad(ok_read);
   };
   for (int i = 0; i < n; i += 2) {
-    step(i, kbuf1, vbuf0, kbuf0, vbuf1);
-    if (i + 1 < n) step(i + 1, kbuf0, vbuf1, kbuf1, vbuf0);
+    step(i, kbuf1, vbuf0, kbuf0, vbuf1, kok1, kok0);
+    if (i + 1 < n) step(i + 1, kbuf0, vbuf1, kbuf1, vbuf0, kok0, kok1);
   }
+  if (PAGED && bad_page && a.err && lane == 0) *a.err = 1;
 
   // ---- epilogue: O = o / l (0 when no key was admissible)
   const float l = halves_sum(st.l_part);
@@ -377,7 +456,7 @@ void fwd_mfma_kernel(FwdArgs a) {
   }
   if (qi < Sq) {
     using E = Elem<T>;
-    T* orow = O + (size_t)qi * D;
+    T* orow = O + (size_t)qi * q_row;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -433,6 +512,46 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
     case 5: return launch_flags<5>(a, grid, stream);
     case 6: return launch_flags<6>(a, grid, stream);
     default: return launch_flags<7>(a, grid, stream);
+  }
+}
+
+hipError_t ATTN_CAT(launch_paged_prefill_, ATTN_TAG)(const PagedPrefillProblem& p, hipStream_t stream) {
+  FwdArgs a = {};
+  a.q = p.q;
+  a.k = p.k_pool;
+  a.v = p.v_pool;
+  a.alibi = p.alibi;
+  a.out = p.out;
+  a.lse = nullptr;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.group = p.Hq / p.Hkv;
+  a.nbh = p.B * p.Hq;
+  a.nqb = (p.max_sq + kBM - 1) / kBM;
+  a.heavy_first = p.causal;
+  a.table = p.block_table;
+  a.kv_lens = p.seq_lens;
+  a.cu_q = p.cu_seqlens_q;
+  a.err = p.error_flag;
+  a.maxb = p.max_blocks;
+  a.bs = p.block_size;
+  a.num_blocks = p.num_blocks;
+  a.total_q = p.total_q;
+  a.max_sq = p.max_sq;
+  a.wl = p.wl;
+  a.has_hi = p.causal || p.wr >= 0;
+  a.dmax = p.causal ? (p.wr >= 0 ? min(p.wr, 0) : 0) : p.wr;
+  const bool softcap = p.softcap > 0.f;
+  a.c_score = softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
+  a.c_cap = kLog2e * p.softcap;
+  const int grid = a.nqb * a.nbh;
+  // lengths vary per sequence: the masked variants always
+  const int flags = F_PAGED | F_MASK | (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0);
+  switch (flags) {
+    case F_PAGED | F_MASK: return launch_flags<F_PAGED | F_MASK>(a, grid, stream);
+    case F_PAGED | F_MASK | F_SOFTCAP: return launch_flags<F_PAGED | F_MASK | F_SOFTCAP>(a, grid, stream);
+    case F_PAGED | F_MASK | F_ALIBI: return launch_flags<F_PAGED | F_MASK | F_ALIBI>(a, grid, stream);
+    default: return launch_flags<F_PAGED | F_MASK | F_SOFTCAP | F_ALIBI>(a, grid, stream);
   }
 }
 

@@ -22,6 +22,24 @@ struct FwdProblem {
   float softcap;  // 0 = off
 };
 
+// Variable-length prefill over the paged pool (queries packed by a prefix sum).
+struct PagedPrefillProblem {
+  const void* q;          // [total_q, Hq, D]
+  const void* k_pool;     // [num_blocks, block_size, Hkv, D]
+  const void* v_pool;
+  const int32_t* block_table;   // [B, max_blocks]
+  const int32_t* seq_lens;      // [B] live keys
+  const int32_t* cu_seqlens_q;  // [B + 1]
+  const float* alibi;
+  void* out;              // [total_q, Hq, D]
+  int32_t* error_flag;
+  int B, Hq, Hkv, D, total_q, max_sq;
+  int num_blocks, block_size, max_blocks;
+  int causal;
+  int wl, wr;             // -1 = unbounded (already clamped to the useful range)
+  float scale, softcap;
+};
+
 // Paged decode problem.
 struct DecodeProblem {
   const void* q;
@@ -44,6 +62,7 @@ struct DecodeProblem {
 // 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
 hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
 
 }  // namespace attn

@@ -196,3 +196,44 @@ def test_paged_check_pointers_and_workspace():
     assert check_paged(p, ws=LEN) == ALIAS
     assert check_paged(p, err=WS + 64) == ALIAS
     assert check_paged(p, out=WS + 1024) == ALIAS
+
+
+def varlen(**kw):
+    base = dict(B=3, Hq=8, Hkv=2, D=128, total_q=500, max_seqlen_q=300, num_blocks=40,
+                block_size=64, max_blocks_per_seq=12, dtype=sdpa.ATTN_BF16, causal=1,
+                window_left=-1, window_right=-1, softmax_scale=0.088, softcap=0.0)
+    base.update(kw)
+    return sdpa.attn_varlen_params_t(**base)
+
+
+CU = 0x100000000 * 13
+
+
+def check_varlen(p, **kw):
+    a = dict(q=Q, kp=KP, vp=VP, tab=TAB, lens=LEN, cu=CU, al=None, out=OUT, err=None)
+    a.update(kw)
+    return sdpa.attn_paged_prefill_check(a["q"], a["kp"], a["vp"], a["tab"], a["lens"], a["cu"],
+                                         a["al"], a["out"], a["err"], p)
+
+
+def test_paged_prefill_check():
+    assert check_varlen(varlen()) == OK
+    assert check_varlen(varlen(block_size=128)) == OK
+    assert check_varlen(varlen(dtype=sdpa.ATTN_F32)) == UNSUPPORTED
+    assert check_varlen(varlen(block_size=16)) == UNSUPPORTED
+    assert check_varlen(varlen(D=80)) == HEAD_DIM
+    assert check_varlen(varlen(Hq=6, Hkv=4)) == GQA
+    assert check_varlen(varlen(window_left=-2)) == PARAM
+    assert check_varlen(varlen(softcap=-1.0)) == PARAM
+    assert check_varlen(varlen(total_q=-1)) == SHAPE
+    assert check_varlen(varlen(), cu=None) == NULL
+    assert check_varlen(varlen(), lens=None) == NULL
+    assert check_varlen(varlen(total_q=0), q=None, out=None, cu=None, lens=None) == OK
+    assert check_varlen(varlen(), cu=CU + 2) == ALIGN
+    assert check_varlen(varlen(), q=Q + 8) == ALIGN
+    assert check_varlen(varlen(), out=Q) == ALIAS
+    assert check_varlen(varlen(), cu=OUT + 64) == ALIAS
+    assert check_varlen(None) == NULL
+    lib = sdpa.library()
+    p = varlen(D=80)
+    assert lib.attn_paged_prefill(Q, KP, VP, TAB, LEN, CU, None, OUT, None, ctypes.byref(p), None) == HEAD_DIM
