@@ -56,7 +56,7 @@ constexpr int kBM = kNW * kQW;     // query rows per workgroup
 constexpr int kThreads = kNW * 64;
 constexpr float kRescaleGap = 8.0f;  // log2 units: weights stay <= 2^8
 
-enum : int { F_MASK = 1, F_SOFTCAP = 2, F_ALIBI = 4, F_PAGED = 8 };
+enum : int { F_MASK = 1, F_SOFTCAP = 2, F_ALIBI = 4, F_PAGED = 8, F_SPLIT = 16 };
 
 struct FwdArgs {
   const void* q;
@@ -236,11 +236,18 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
   }
 }
 
+// Key-split mode (F_SPLIT, for grids too small to fill the chip): the
+// workgroup has two groups of kNW waves on the same 128 query rows; group 0
+// takes the first half of the key tiles, group 1 the second, each with its own
+// LDS buffers, and group 1 hands its (o, m, l) to group 0 at the end.
 template <typename T, int D, int FLAGS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__((FLAGS & F_SPLIT) ? 2 * kThreads : kThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdArgs a) {
   constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
   constexpr bool PAGED = (FLAGS & F_PAGED) != 0;
+  constexpr bool SPLIT = (FLAGS & F_SPLIT) != 0;
+  constexpr int NG = SPLIT ? 2 : 1;      // key groups
   constexpr int NC = D / 8;              // 16-byte chunks per K/V row
   constexpr int TC = kBN * NC;           // chunks per K (or V) tile
   constexpr int CPT = TC / kThreads;     // chunks per thread per tile and tensor
@@ -249,12 +256,16 @@ void fwd_mfma_kernel(FwdArgs a) {
   static_assert(CPT * kThreads == TC, "tile must split evenly over the workgroup");
 
   // Four separate LDS objects so that the compiler can tell the buffer being
-  // filled by the asynchronous copy from the buffers being read.
-  __shared__ u32x4 kbuf0[TC], kbuf1[TC], vbuf0[TC], vbuf1[TC];
+  // filled by the asynchronous copy from the buffers being read (one tile per
+  // key group in each).
+  __shared__ u32x4 kbuf0[NG * TC], kbuf1[NG * TC], vbuf0[NG * TC], vbuf1[NG * TC];
 
-  const int tid = threadIdx.x;
+  const int tid_wg = threadIdx.x;
+  const int wave_wg = __builtin_amdgcn_readfirstlane(tid_wg >> 6);  // wave-uniform
+  const int grp = SPLIT ? wave_wg / kNW : 0;    // key group
+  const int tid = tid_wg - grp * kThreads;      // thread within the group
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = wave_wg - grp * kNW;         // wave within the group
   const int g = lane >> 5;               // lane half
   const int ln = lane & 31;
 
@@ -305,8 +316,12 @@ void fwd_mfma_kernel(FwdArgs a) {
   const int wg_last = min(m0 + kBM, Sq) - 1;
   const int n_lo = key_lo(m0 + off);
   const int n_hi = key_hi(wg_last + off);
-  const int t_begin = n_lo / kBN;
-  const int t_end = n_hi > n_lo ? (n_hi + kBN - 1) / kBN : t_begin;
+  const int t_first = n_lo / kBN;
+  const int t_last = n_hi > n_lo ? (n_hi + kBN - 1) / kBN : t_first;   // one past
+  // this group's tiles [t_begin, t_end); with one group that is all of them
+  const int half = SPLIT ? (t_last - t_first + 1) / 2 : 0;
+  const int t_begin = SPLIT && grp == 1 ? t_first + half : t_first;
+  const int t_end = SPLIT && grp == 0 ? t_first + half : t_last;
 
   const int wq0 = m0 + wave * kQW;
   const bool wave_live = wq0 < Sq;
@@ -395,6 +410,13 @@ void fwd_mfma_kernel(FwdArgs a) {
   // Paged: kok0 / kok1 say whether the tile in kbuf0 / kbuf1 lies in the pool;
   // a tile that does not has its scores set to -inf right after its QK.
   const int n = t_end - t_begin;
+  // steps every wave of the workgroup runs (barriers must match): group 0 of a
+  // split workgroup has at least as many tiles as group 1
+  const int n_steps = SPLIT ? half : n;
+  u32x4* const kb0 = kbuf0 + grp * TC;
+  u32x4* const kb1 = kbuf1 + grp * TC;
+  u32x4* const vb0 = vbuf0 + grp * TC;
+  u32x4* const vb1 = vbuf1 + grp * TC;
   floatx16 sc[2];
   bool kok0 = true, kok1 = true;
   auto mask_bad = [&](bool ok) {
@@ -404,14 +426,16 @@ void fwd_mfma_kernel(FwdArgs a) {
     }
   };
   if constexpr (PAGED) load_pages(t_begin / m_tiles);
-  if (n > 0) {
-    dma_k(kbuf0, t_begin, kok0);
-    dma_v(vbuf0, t_begin);
-    if (n > 1) dma_k(kbuf1, t_begin + 1, kok1);
+  if (n_steps > 0) {
+    if (n > 0) {
+      dma_k(kb0, t_begin, kok0);
+      dma_v(vb0, t_begin);
+    }
+    if (n > 1) dma_k(kb1, t_begin + 1, kok1);
     wait_vmem();
     __syncthreads();
-    if (live(t_begin)) {
-      qk_tile<T, D>(kbuf0, qf, ln, g, sc);
+    if (n > 0 && live(t_begin)) {
+      qk_tile<T, D>(kb0, qf, ln, g, sc);
       mask_bad(kok0);
     }
   }
@@ -440,14 +464,58 @@ void fwd_mfma_kernel(FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
     if (i + 1 < n && live(t + 1)) mask_bad(ok_read);
   };
-  for (int i = 0; i < n; i += 2) {
-    step(i, kbuf1, vbuf0, kbuf0, vbuf1, kok1, kok0);
-    if (i + 1 < n) step(i + 1, kbuf0, vbuf1, kbuf1, vbuf0, kok0, kok1);
+  for (int i = 0; i < n_steps; i += 2) {
+    step(i, kb1, vb0, kb0, vb1, kok1, kok0);
+    if (i + 1 < n_steps) step(i + 1, kb0, vb1, kb1, vb0, kok0, kok1);
   }
   if (PAGED && bad_page && a.err && lane == 0) *a.err = 1;
 
+  // ---- key groups: group 1 hands (o, m, l) to group 0 through LDS (the tile
+  // buffers are free now), one 32-row block of O^T at a time; group 0 rebases
+  // both to their common reference max.
+  float l = halves_sum(st.l_part);
+  if constexpr (SPLIT) {
+    float* xo = reinterpret_cast<float*>(kbuf0);  // [64 lanes x 4 waves][16]
+    float* xml = reinterpret_cast<float*>(vbuf0); // [64 x 4][2]
+    const int slot = wave * 64 + lane;
+    __syncthreads();  // every wave is done with the tile buffers
+    if (grp == 1) {
+      xml[2 * slot] = st.m_run;
+      xml[2 * slot + 1] = l;
+    }
+    float a0 = 1.f, a1 = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (grp == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+          *reinterpret_cast<floatx4*>(xo + slot * 16 + r) =
+              floatx4{st.o[db][r], st.o[db][r + 1], st.o[db][r + 2], st.o[db][r + 3]};
+      }
+      __syncthreads();
+      if (grp == 0) {
+        if (db == 0) {
+          const float m1 = xml[2 * slot], l1 = xml[2 * slot + 1];
+          const float m0 = st.m_run;
+          const float M = __builtin_fmaxf(m0, m1);
+          a0 = m0 == kNegInf ? 0.f : fast_exp2(m0 - M);
+          a1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
+          st.m_run = M;
+          l = l * a0 + l1 * a1;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const floatx4 x = *reinterpret_cast<const floatx4*>(xo + slot * 16 + r);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) st.o[db][r + c] = st.o[db][r + c] * a0 + x[c] * a1;
+        }
+      }
+      __syncthreads();
+    }
+    if (grp == 1) return;
+  }
+
   // ---- epilogue: O = o / l (0 when no key was admissible)
-  const float l = halves_sum(st.l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (a.lse && qi < Sq && g == 0) {
     // lse = ln(sum_j e^{s_j}) = ln 2 * (m + log2 l) with the weights 2^(x - m)
@@ -471,9 +539,22 @@ void fwd_mfma_kernel(FwdArgs a) {
 
 template <int FLAGS>
 hipError_t launch_flags(const FwdArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_mfma_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fwd_mfma_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid),
+                     dim3((FLAGS & F_SPLIT) ? 2 * kThreads : kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                   ? n : 256;
+  }
+  return cus[dev];
 }
 
 }  // namespace
@@ -502,8 +583,21 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
   a.c_cap = kLog2e * p.softcap;
   const int grid = a.nqb * a.nbh;
   const bool mask = p.causal || p.wl >= 0 || p.wr >= 0 || (p.Sk % kBN) != 0;
-  const int flags = (mask ? F_MASK : 0) | (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0);
+  // Fewer workgroups than two per compute unit leave SIMDs with a single
+  // wave: split the key range of each workgroup over two wave groups instead
+  // (only worth it with enough key tiles to share).
+  const bool split = grid < 2 * device_cus() && p.Sk >= 8 * kBN;
+  const int flags = (mask ? F_MASK : 0) | (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0) |
+                    (split ? F_SPLIT : 0);
   switch (flags) {
+    case F_SPLIT | 0: return launch_flags<F_SPLIT | 0>(a, grid, stream);
+    case F_SPLIT | 1: return launch_flags<F_SPLIT | 1>(a, grid, stream);
+    case F_SPLIT | 2: return launch_flags<F_SPLIT | 2>(a, grid, stream);
+    case F_SPLIT | 3: return launch_flags<F_SPLIT | 3>(a, grid, stream);
+    case F_SPLIT | 4: return launch_flags<F_SPLIT | 4>(a, grid, stream);
+    case F_SPLIT | 5: return launch_flags<F_SPLIT | 5>(a, grid, stream);
+    case F_SPLIT | 6: return launch_flags<F_SPLIT | 6>(a, grid, stream);
+    case F_SPLIT | 7: return launch_flags<F_SPLIT | 7>(a, grid, stream);
     case 0: return launch_flags<0>(a, grid, stream);
     case 1: return launch_flags<1>(a, grid, stream);
     case 2: return launch_flags<2>(a, grid, stream);
@@ -545,13 +639,20 @@ hipError_t ATTN_CAT(launch_paged_prefill_, ATTN_TAG)(const PagedPrefillProblem& 
   a.c_score = softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
   a.c_cap = kLog2e * p.softcap;
   const int grid = a.nqb * a.nbh;
-  // lengths vary per sequence: the masked variants always
-  const int flags = F_PAGED | F_MASK | (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0);
+  // lengths vary per sequence: the masked variants always; the key split on
+  // the same rule as the dense launch, with the longest possible key range
+  const bool split = grid < 2 * device_cus() && (long long)p.max_blocks * p.block_size >= 8 * kBN;
+  constexpr int PM = F_PAGED | F_MASK;
+  const int flags = (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0) | (split ? F_SPLIT : 0);
   switch (flags) {
-    case F_PAGED | F_MASK: return launch_flags<F_PAGED | F_MASK>(a, grid, stream);
-    case F_PAGED | F_MASK | F_SOFTCAP: return launch_flags<F_PAGED | F_MASK | F_SOFTCAP>(a, grid, stream);
-    case F_PAGED | F_MASK | F_ALIBI: return launch_flags<F_PAGED | F_MASK | F_ALIBI>(a, grid, stream);
-    default: return launch_flags<F_PAGED | F_MASK | F_SOFTCAP | F_ALIBI>(a, grid, stream);
+    case 0: return launch_flags<PM>(a, grid, stream);
+    case F_SOFTCAP: return launch_flags<PM | F_SOFTCAP>(a, grid, stream);
+    case F_ALIBI: return launch_flags<PM | F_ALIBI>(a, grid, stream);
+    case F_SOFTCAP | F_ALIBI: return launch_flags<PM | F_SOFTCAP | F_ALIBI>(a, grid, stream);
+    case F_SPLIT: return launch_flags<PM | F_SPLIT>(a, grid, stream);
+    case F_SPLIT | F_SOFTCAP: return launch_flags<PM | F_SPLIT | F_SOFTCAP>(a, grid, stream);
+    case F_SPLIT | F_ALIBI: return launch_flags<PM | F_SPLIT | F_ALIBI>(a, grid, stream);
+    default: return launch_flags<PM | F_SPLIT | F_SOFTCAP | F_ALIBI>(a, grid, stream);
   }
 }
 

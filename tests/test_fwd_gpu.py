@@ -86,6 +86,30 @@ def test_small_parity(gpu_lib, dtype, D, case):
     run_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=100 + case, **kw)
 
 
+# Small grids with long key ranges: the launch splits each workgroup's key
+# tiles over two wave groups and merges them; odd and even tile counts, rows
+# with no admissible key, and every mask kind.
+KEY_SPLIT = [
+    (1, 2, 1, 128, 512, dict()),
+    (1, 2, 2, 100, 577, dict()),
+    (1, 4, 2, 700, 600, dict(causal=True)),                  # rows 0..99 empty
+    (2, 2, 1, 333, 1111, dict(causal=True)),
+    (1, 2, 2, 256, 900, dict(causal=True, wl=200, wr=0)),
+    (1, 2, 1, 200, 640, dict(wl=300, wr=50, softcap=10.0, amp=2.0)),
+    (1, 4, 4, 64, 2000, dict(alibi=True)),
+    (1, 2, 2, 300, 1500, dict(causal=True, softcap=20.0, alibi=True, amp=1.5)),
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("case", range(len(KEY_SPLIT)))
+def test_key_split_parity(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = KEY_SPLIT[case]
+    out = run_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=300 + case, **kw)
+    if kw.get("causal") and Sq > Sk:
+        assert torch.count_nonzero(out[:, :, :Sq - Sk]).item() == 0
+
+
 @pytest.mark.parametrize("case", [
     (1, 4, 4, 128, 128, 64, dict()),
     (1, 4, 2, 200, 250, 128, dict(causal=True)),
@@ -254,6 +278,12 @@ def run_lse_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, w
 def test_lse_parity(gpu_lib, dtype, D, case):
     B, Hq, Hkv, Sq, Sk, kw = SMALL[case]
     run_lse_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=300 + case, **kw)
+
+
+@pytest.mark.parametrize("case", [2, 4, 7])
+def test_lse_key_split_parity(gpu_lib, case):
+    B, Hq, Hkv, Sq, Sk, kw = KEY_SPLIT[case]
+    run_lse_case(gpu_lib, "bf16", B, Hq, Hkv, Sq, Sk, 128, seed=400 + case, **kw)
 
 
 @pytest.mark.parametrize("case", [
