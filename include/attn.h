@@ -53,7 +53,8 @@ extern "C" {
 typedef enum attn_dtype {
   ATTN_F32 = 0,
   ATTN_F16 = 1,
-  ATTN_BF16 = 2
+  ATTN_BF16 = 2,
+  ATTN_F64 = 3   /* dense forward only (kernel-contract page: F64 accepted) */
 } attn_dtype_t;
 
 typedef enum attn_status {
@@ -62,7 +63,7 @@ typedef enum attn_status {
   ATTN_ERR_DTYPE = 2,        /* dtype is not an attn_dtype_t value                  */
   ATTN_ERR_SHAPE = 3,        /* a size is negative, inconsistent or too large       */
   ATTN_ERR_GQA = 4,          /* Hkv == 0 or Hq is not a multiple of Hkv             */
-  ATTN_ERR_HEAD_DIM = 5,     /* D is not 64 or 128                                  */
+  ATTN_ERR_HEAD_DIM = 5,     /* D not built for the dtype (see attn_fwd_params_t)   */
   ATTN_ERR_PARAM = 6,        /* scale/softcap/window/split parameter out of range   */
   ATTN_ERR_ALIGN = 7,        /* a pointer is not 16-byte aligned                    */
   ATTN_ERR_ALIAS = 8,        /* out overlaps an input or the workspace              */
@@ -81,7 +82,8 @@ typedef struct attn_fwd_params {
   int64_t Sq;            /* query length (0 allowed: nothing to do)             */
   int64_t Sk;            /* key length (0 allowed: output is all zero); one    *
                           * head's K (Sk * D * element size) must be < 2 GiB    */
-  int64_t D;             /* head dim: 64 or 128                                 */
+  int64_t D;             /* head dim: 64 or 128 for F16/BF16 (matrix cores);    *
+                          * 32, 64, 128 or 256 for F32/F64 (vector ALU)         */
   int32_t dtype;         /* attn_dtype_t of q, k, v and out                     */
   int32_t causal;        /* nonzero: bottom-right causal mask                   */
   int64_t window_left;   /* -1: unbounded; else keys j >= i' - window_left      */
@@ -103,15 +105,16 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v,
 /* Attention forward: validates as attn_fwd_check, then enqueues the kernel
  * for p->dtype and p->D on `stream` and returns.  F16/BF16 compute both
  * matmuls on the matrix cores with float32 accumulation (the softmax weights
- * enter the second matmul rounded to the input dtype); F32 computes in
- * float32 throughout. */
+ * enter the second matmul rounded to the input dtype); F32 and F64 compute in
+ * their own precision throughout, on the vector ALU. */
 attn_status_t attn_fwd(const void* q, const void* k, const void* v,
                        const float* alibi, void* out,
                        const attn_fwd_params_t* p, void* stream);
 
 /* Host-only validation of an attn_fwd_lse call: as attn_fwd_check, plus
- *   lse   [B, Hq, Sq] float32, 4-byte aligned, overlapping no input and not
- *         out; NULL only when B * Hq * Sq == 0. */
+ *   lse   [B, Hq, Sq] float32 (for every dtype, F64 included), 4-byte
+ *         aligned, overlapping no input and not out; NULL only when
+ *         B * Hq * Sq == 0. */
 attn_status_t attn_fwd_lse_check(const void* q, const void* k, const void* v,
                                  const float* alibi, const void* out,
                                  const float* lse, const attn_fwd_params_t* p);

@@ -33,13 +33,14 @@ __all__ = [
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
     "attn_paged_params", "attn_status_str", "attn_version",
     "attn_paged_prefill", "attn_paged_prefill_check", "attn_varlen_params",
-    "ATTN_F32", "ATTN_F16", "ATTN_BF16",
+    "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_F64",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
-ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
-_DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_F64 = 0, 1, 2, 3
+_DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16,
+               torch.float64: ATTN_F64}
 
 STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DTYPE", 3: "ATTN_ERR_SHAPE",
@@ -189,7 +190,7 @@ def _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left, window_ri
     if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
         raise ValueError("batch and head dim of k/v must match q")
     if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPE_CODE:
-        raise ValueError("q, k, v must share one dtype of float32 / float16 / bfloat16")
+        raise ValueError("q, k, v must share one dtype of float32 / float64 / float16 / bfloat16")
     if alibi is not None and (alibi.dtype != torch.float32 or alibi.shape != (q.shape[1],)):
         raise ValueError("alibi slopes must be float32 [Hq]")
     if out is None:

@@ -43,8 +43,14 @@ namespace {
 constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions stay far inside int32
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
-bool valid_dtype(int32_t d) { return d == ATTN_F32 || d == ATTN_F16 || d == ATTN_BF16; }
-int64_t elem_bytes(int32_t d) { return d == ATTN_F32 ? 4 : 2; }
+bool valid_dtype(int32_t d) { return d == ATTN_F32 || d == ATTN_F16 || d == ATTN_BF16 || d == ATTN_F64; }
+int64_t elem_bytes(int32_t d) { return d == ATTN_F64 ? 8 : (d == ATTN_F32 ? 4 : 2); }
+// Dense forward head dims: the matrix-core path (F16, BF16) takes 64 and 128,
+// the vector-ALU path (F32, F64) 32, 64, 128 and 256.
+bool fwd_head_dim_ok(int32_t dtype, int64_t D) {
+  if (dtype == ATTN_F32 || dtype == ATTN_F64) return D == 32 || D == 64 || D == 128 || D == 256;
+  return D == 64 || D == 128;
+}
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // a * b * ... without overflow (all factors >= 0); false on overflow.
@@ -76,11 +82,11 @@ attn_status_t fwd_shape(const attn_fwd_params_t* p, int64_t* q_bytes, int64_t* k
   if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->Sq < 0 || p->Sk < 0 || p->D < 0)
     return ATTN_ERR_SHAPE;
   if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
-  if (p->D != 64 && p->D != 128) return ATTN_ERR_HEAD_DIM;
+  if (!fwd_head_dim_ok(p->dtype, p->D)) return ATTN_ERR_HEAD_DIM;
   if (p->Sq > kMaxLen || p->Sk > kMaxLen) return ATTN_ERR_SHAPE;
   int64_t bh;
   if (!mul(p->B, p->Hq, &bh) || bh > kMaxLen) return ATTN_ERR_SHAPE;
-  const int64_t qblocks = (p->Sq + 63) / 64;
+  const int64_t qblocks = (p->Sq + 31) / 32;  // the smallest row block of any forward kernel
   int64_t grid;
   if (!mul(bh, qblocks, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
   const int64_t es = elem_bytes(p->dtype);
@@ -140,7 +146,7 @@ attn_status_t paged_shape(const attn_paged_params_t* p) {
 // disjoint from every input and from out.
 static attn_status_t check_lse(const void* q, const void* k, const void* v, const float* alibi,
                                const void* out, const float* lse, const attn_fwd_params_t* p) {
-  const int64_t es = p->dtype == ATTN_F32 ? 4 : 2;
+  const int64_t es = elem_bytes(p->dtype);
   const int64_t rows = p->B * p->Hq * p->Sq;
   if (rows > 0 && !lse) return ATTN_ERR_NULL;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3) != 0) return ATTN_ERR_ALIGN;
@@ -175,8 +181,9 @@ static attn_status_t launch_fwd(const void* q, const void* k, const void* v, con
   fp.scale = p->softmax_scale;
   fp.softcap = p->softcap;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e =
-      p->dtype == ATTN_F32 ? attn::launch_fwd_f32(fp, s) : attn::launch_fwd_mfma(fp, p->dtype, s);
+  const hipError_t e = (p->dtype == ATTN_F32 || p->dtype == ATTN_F64)
+                            ? attn::launch_fwd_valu(fp, p->dtype == ATTN_F64, s)
+                            : attn::launch_fwd_mfma(fp, p->dtype, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -220,7 +227,7 @@ attn_status_t attn_paged_decode_check(const void* q, const void* k_pool, const v
                                       const attn_paged_params_t* p) {
   if (!p) return ATTN_ERR_NULL;
   if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
-  if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t st = paged_shape(p);
   if (st != ATTN_OK) return st;
   if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
@@ -292,7 +299,7 @@ attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const 
                                        const attn_varlen_params_t* p) {
   if (!p) return ATTN_ERR_NULL;
   if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
-  if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) return ATTN_ERR_UNSUPPORTED;
   if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->D < 0 || p->total_q < 0 || p->max_seqlen_q < 0 ||
       p->num_blocks < 0 || p->max_blocks_per_seq < 0 || p->block_size < 1)
     return ATTN_ERR_SHAPE;
@@ -380,7 +387,7 @@ const char* attn_status_str(attn_status_t status) {
     case ATTN_ERR_DTYPE: return "invalid dtype";
     case ATTN_ERR_SHAPE: return "invalid or too large shape";
     case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
-    case ATTN_ERR_HEAD_DIM: return "head dim must be 64 or 128";
+    case ATTN_ERR_HEAD_DIM: return "head dim not built for this dtype";
     case ATTN_ERR_PARAM: return "parameter out of range";
     case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case ATTN_ERR_ALIAS: return "output overlaps an input";

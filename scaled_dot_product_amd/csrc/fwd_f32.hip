@@ -1,11 +1,12 @@
-// fwd_f32.hip -- attention forward in float32 throughout (vector ALU).
+// fwd_f32.hip -- attention forward in float32 or float64 throughout (vector
+// ALU).
 //
 // Same definition as the matrix-core path (kernel-contract page,
-// attention_naive; derivation page sections 1-4), for F32 inputs: four lanes
-// share one query row and each owns a quarter of the head dim; key/value
-// tiles of 32 keys are staged in LDS; the per-tile online update uses the
-// exact tile max and accurate expf.  Meant for correctness at f32 tolerance,
-// not for speed.
+// attention_naive; derivation page sections 1-4), for F32 and F64 inputs:
+// LPR lanes share one query row and each owns D / LPR of the head dim;
+// key/value tiles are staged in LDS; the per-tile online update uses the exact
+// tile max and the accurate exp of the element type.  Meant for correctness
+// at the element type's tolerance, not for speed.
 #include <limits.h>
 
 #include "device_common.h"
@@ -14,123 +15,169 @@
 namespace attn {
 namespace {
 
-constexpr int kRows = 64;     // query rows per workgroup (4 lanes each)
-constexpr int kKeys = 32;     // keys per tile
 constexpr int kThreads = 256;
 
-struct F32Args {
-  const float* q;
-  const float* k;
-  const float* v;
+template <typename T> struct VMath;
+template <> struct VMath<float> {
+  static __device__ float fma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+  static __device__ float exp(float x) { return expf(x); }
+  static __device__ float log(float x) { return logf(x); }
+  static __device__ float tanh(float x) { return tanhf(x); }
+  static __device__ float max(float a, float b) { return __builtin_fmaxf(a, b); }
+};
+template <> struct VMath<double> {
+  static __device__ double fma(double a, double b, double c) { return __builtin_fma(a, b, c); }
+  static __device__ double exp(double x) { return ::exp(x); }
+  static __device__ double log(double x) { return ::log(x); }
+  static __device__ double tanh(double x) { return ::tanh(x); }
+  static __device__ double max(double a, double b) { return __builtin_fmax(a, b); }
+};
+
+struct VArgs {
+  const void* q;
+  const void* k;
+  const void* v;
   const float* alibi;
-  float* out;
+  void* out;
   float* lse;  // per-row log-sum-exp (natural log), or nullptr
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
   int wl, has_hi, dmax;
   float scale, softcap;
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
-  constexpr int SL = D / 4;  // head-dim slice per lane
-  __shared__ float ks[kKeys][D];
-  __shared__ float vs[kKeys][D];
+// Lanes per query row and keys per LDS tile for element type T and head dim D:
+// at most 32 elements of q and of o per lane, and K + V tiles within 64 KiB.
+template <typename T, int D> struct VGeom {
+  static constexpr int LPR = D / 32 > 4 ? D / 32 : 4;
+  static constexpr int ROWS = kThreads / LPR;
+  static constexpr int KEYS = (int)(32768 / (D * sizeof(T))) < 32 ? (int)(32768 / (D * sizeof(T))) : 32;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void fwd_valu_kernel(VArgs a) {
+  using M = VMath<T>;
+  using G = VGeom<T, D>;
+  constexpr int LPR = G::LPR, ROWS = G::ROWS, KEYS = G::KEYS;
+  constexpr int SL = D / LPR;              // head-dim slice per lane
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr T kNInf = -__builtin_huge_val();
+  __shared__ T ks[KEYS][D];
+  __shared__ T vs[KEYS][D];
 
   const int tid = threadIdx.x;
-  const int quad = tid >> 2, qd = tid & 3;
+  const int row = tid / LPR, qd = tid % LPR;
   const int bh = blockIdx.x % a.nbh;
   const int qb = blockIdx.x / a.nbh;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int kvh = h / a.group;
   const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
-  const int m0 = qb * kRows;
-  const int qi = m0 + quad;
+  const int m0 = qb * ROWS;
+  const int qi = m0 + row;
   const int ip = qi + off;
 
-  const float* Q = a.q + (size_t)bh * Sq * D;
-  const float* K = a.k + (size_t)(b * a.Hkv + kvh) * Sk * D;
-  const float* V = a.v + (size_t)(b * a.Hkv + kvh) * Sk * D;
+  const T* Q = static_cast<const T*>(a.q) + (size_t)bh * Sq * D;
+  const T* K = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * Sk * D;
+  const T* V = static_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * Sk * D;
 
-  float qv[SL], o[SL];
+  T qv[SL], o[SL];
 #pragma unroll
   for (int e = 0; e < SL; ++e) {
-    qv[e] = qi < Sq ? Q[(size_t)qi * D + qd * SL + e] : 0.f;
-    o[e] = 0.f;
+    qv[e] = qi < Sq ? Q[(size_t)qi * D + qd * SL + e] : T(0);
+    o[e] = T(0);
   }
-  const float slope = a.alibi ? a.alibi[h] : 0.f;
+  const T slope = a.alibi ? (T)a.alibi[h] : T(0);
+  const T scale = (T)a.scale, cap = (T)a.softcap;
 
-  const int last = min(m0 + kRows, Sq) - 1;
+  const int last = min(m0 + ROWS, Sq) - 1;
   const int n_lo = a.wl >= 0 ? max(0, m0 + off - a.wl) : 0;
   const int n_hi = a.has_hi ? min(Sk, max(0, last + off + a.dmax + 1)) : Sk;
   int lo = -ip, hi = Sk - 1 - ip;  // admissible: lo <= j - i' <= hi
   if (a.wl >= 0) lo = max(lo, -a.wl);
   if (a.has_hi) hi = min(hi, a.dmax);
 
-  float m = kNegInf, l = 0.f;
-  for (int n0 = (n_lo / kKeys) * kKeys; n0 < n_hi; n0 += kKeys) {
+  T m = kNInf, l = T(0);
+  for (int n0 = (n_lo / KEYS) * KEYS; n0 < n_hi; n0 += KEYS) {
     __syncthreads();
-    for (int c = tid; c < kKeys * D / 4; c += kThreads) {
-      const int r = c / (D / 4), cc = c % (D / 4);
-      floatx4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+    for (int c = tid; c < KEYS * D / EPC; c += kThreads) {
+      const int r = c / (D / EPC), cc = c % (D / EPC);
+      u32x4 kk = zero_u32x4(), vv = zero_u32x4();
       if (n0 + r < Sk) {
-        kk = *reinterpret_cast<const floatx4*>(K + (size_t)(n0 + r) * D + 4 * cc);
-        vv = *reinterpret_cast<const floatx4*>(V + (size_t)(n0 + r) * D + 4 * cc);
+        kk = *reinterpret_cast<const u32x4*>(K + (size_t)(n0 + r) * D + EPC * cc);
+        vv = *reinterpret_cast<const u32x4*>(V + (size_t)(n0 + r) * D + EPC * cc);
       }
-      *reinterpret_cast<floatx4*>(&ks[r][4 * cc]) = kk;
-      *reinterpret_cast<floatx4*>(&vs[r][4 * cc]) = vv;
+      *reinterpret_cast<u32x4*>(&ks[r][EPC * cc]) = kk;
+      *reinterpret_cast<u32x4*>(&vs[r][EPC * cc]) = vv;
     }
     __syncthreads();
 
-    float s[kKeys];
-    float mt = kNegInf;
+    T s[KEYS];
+    T mt = kNInf;
 #pragma unroll
-    for (int j = 0; j < kKeys; ++j) {
-      float part = 0.f;
+    for (int j = 0; j < KEYS; ++j) {
+      T part = T(0);
 #pragma unroll
-      for (int e = 0; e < SL; ++e) part = __builtin_fmaf(qv[e], ks[j][qd * SL + e], part);
-      part += __shfl_xor(part, 1);
-      part += __shfl_xor(part, 2);
-      float x = part * a.scale;
-      if (a.softcap > 0.f) x = a.softcap * tanhf(x / a.softcap);
+      for (int e = 0; e < SL; ++e) part = M::fma(qv[e], ks[j][qd * SL + e], part);
+#pragma unroll
+      for (int w = 1; w < LPR; w <<= 1) part += __shfl_xor(part, w);
+      T x = part * scale;
+      if (a.softcap > 0.f) x = cap * M::tanh(x / cap);
       const int rel = n0 + j - ip;
-      if (a.alibi) x = __builtin_fmaf(slope, (float)rel, x);
-      if (rel < lo || rel > hi) x = kNegInf;
+      if (a.alibi) x = M::fma(slope, (T)rel, x);
+      if (rel < lo || rel > hi) x = kNInf;
       s[j] = x;
-      mt = __builtin_fmaxf(mt, x);
+      mt = M::max(mt, x);
     }
-    const float m_new = __builtin_fmaxf(m, mt);
-    if (m_new == kNegInf) continue;  // nothing admissible so far for this row
-    const float alpha = expf(m - m_new);
+    const T m_new = M::max(m, mt);
+    if (m_new == kNInf) continue;  // nothing admissible so far for this row
+    const T alpha = M::exp(m - m_new);
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < SL; ++e) o[e] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kKeys; ++j) {
-      const float p = expf(s[j] - m_new);
-      l += p;
+    for (int j = 0; j < KEYS; ++j) {
+      const T pj = M::exp(s[j] - m_new);
+      l += pj;
 #pragma unroll
-      for (int e = 0; e < SL; ++e) o[e] = __builtin_fmaf(p, vs[j][qd * SL + e], o[e]);
+      for (int e = 0; e < SL; ++e) o[e] = M::fma(pj, vs[j][qd * SL + e], o[e]);
     }
     m = m_new;
   }
 
   if (qi < Sq) {
-    float* orow = a.out + ((size_t)bh * Sq + qi) * D + qd * SL;
+    T* orow = static_cast<T*>(a.out) + ((size_t)bh * Sq + qi) * D + qd * SL;
 #pragma unroll
-    for (int e = 0; e < SL; ++e) orow[e] = l > 0.f ? o[e] / l : 0.f;
-    if (a.lse && qd == 0) a.lse[(size_t)bh * Sq + qi] = l > 0.f ? m + logf(l) : kNegInf;
+    for (int e = 0; e < SL; ++e) orow[e] = l > T(0) ? o[e] / l : T(0);
+    if (a.lse && qd == 0) a.lse[(size_t)bh * Sq + qi] = l > T(0) ? (float)(m + M::log(l)) : kNegInf;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_valu(const VArgs& a0, const FwdProblem& p, hipStream_t stream) {
+  VArgs a = a0;
+  a.nqb = (p.Sq + VGeom<T, D>::ROWS - 1) / VGeom<T, D>::ROWS;
+  hipLaunchKernelGGL((fwd_valu_kernel<T, D>), dim3(a.nqb * a.nbh), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_valu_d(const VArgs& a, const FwdProblem& p, hipStream_t stream) {
+  switch (p.D) {
+    case 32: return launch_valu<T, 32>(a, p, stream);
+    case 64: return launch_valu<T, 64>(a, p, stream);
+    case 128: return launch_valu<T, 128>(a, p, stream);
+    default: return launch_valu<T, 256>(a, p, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream) {
-  F32Args a;
-  a.q = static_cast<const float*>(p.q);
-  a.k = static_cast<const float*>(p.k);
-  a.v = static_cast<const float*>(p.v);
+hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream) {
+  VArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
   a.alibi = p.alibi;
-  a.out = static_cast<float*>(p.out);
+  a.out = p.out;
   a.lse = p.lse;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
@@ -138,18 +185,13 @@ hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream) {
   a.Hkv = p.Hkv;
   a.group = p.Hq / p.Hkv;
   a.nbh = p.B * p.Hq;
-  a.nqb = (p.Sq + kRows - 1) / kRows;
+  a.nqb = 0;
   a.wl = p.wl;
   a.has_hi = p.causal || p.wr >= 0;
   a.dmax = p.causal ? (p.wr >= 0 ? min(p.wr, 0) : 0) : p.wr;
   a.scale = p.scale;
   a.softcap = p.softcap;
-  const int grid = a.nqb * a.nbh;
-  if (p.D == 128)
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return f64 ? launch_valu_d<double>(a, p, stream) : launch_valu_d<float>(a, p, stream);
 }
 
 }  // namespace attn

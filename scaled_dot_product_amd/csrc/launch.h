@@ -61,7 +61,7 @@ struct DecodeProblem {
 
 // 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
 hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream);
-hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream);
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
 

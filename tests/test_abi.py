@@ -69,6 +69,27 @@ def test_fwd_check_accepts_valid_calls():
                          softcap=30.0), al=AL) == OK
     assert check_fwd(fwd(dtype=sdpa.ATTN_F32)) == OK
     assert check_fwd(fwd(Hkv=8)) == OK
+    # the vector-ALU path (F32, F64) takes head dims 32 .. 256
+    for dt in (sdpa.ATTN_F32, sdpa.ATTN_F64):
+        for d in (32, 64, 128, 256):
+            assert check_fwd(fwd(dtype=dt, D=d)) == OK, (dt, d)
+
+
+@pytest.mark.parametrize("dt,d", [(sdpa.ATTN_BF16, 32), (sdpa.ATTN_F16, 256), (sdpa.ATTN_F32, 96),
+                                  (sdpa.ATTN_F64, 80), (sdpa.ATTN_F64, 512)])
+def test_fwd_check_head_dim_per_dtype(dt, d):
+    assert check_fwd(fwd(dtype=dt, D=d)) == HEAD_DIM
+
+
+def test_fwd_check_f64_sizes_and_alias():
+    # F64 operands are 8 bytes an element: out overlapping the end of q aliases
+    p = fwd(dtype=sdpa.ATTN_F64, B=1, Hq=2, Hkv=2, Sq=4, Sk=4, D=32)
+    q_bytes = 1 * 2 * 4 * 32 * 8
+    assert check_fwd(p, out=Q + q_bytes) == OK
+    assert check_fwd(p, out=Q + q_bytes - 16) == ALIAS
+    # one head's K must stay under 2 GiB: Sk * D * 8 bytes
+    assert check_fwd(fwd(dtype=sdpa.ATTN_F64, D=256, Sk=(1 << 20))) == SHAPE
+    assert check_fwd(fwd(dtype=sdpa.ATTN_F64, D=256, Sk=(1 << 20) - 1)) == OK
 
 
 def test_fwd_check_empty_tensors_may_be_null():
@@ -82,7 +103,7 @@ def test_fwd_check_empty_tensors_may_be_null():
     (dict(B=-1), SHAPE), (dict(Sq=-2), SHAPE), (dict(Sk=-1), SHAPE),
     (dict(Sq=(1 << 30) + 1), SHAPE),
     (dict(Hkv=3), GQA), (dict(Hkv=0), GQA),
-    (dict(D=96), HEAD_DIM), (dict(D=256), HEAD_DIM),
+    (dict(D=96), HEAD_DIM), (dict(D=256), HEAD_DIM), (dict(D=32), HEAD_DIM),
     (dict(softmax_scale=float("nan")), PARAM), (dict(softmax_scale=-1.0), PARAM),
     (dict(softcap=-0.5), PARAM), (dict(softcap=float("inf")), PARAM),
     (dict(window_left=-2), PARAM), (dict(window_right=-5), PARAM),
@@ -171,6 +192,7 @@ def test_paged_check_accepts_valid_calls():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), DTYPE), (dict(dtype=sdpa.ATTN_F32), UNSUPPORTED),
+    (dict(dtype=sdpa.ATTN_F64), UNSUPPORTED),
     (dict(B=-1), SHAPE), (dict(block_size=0), SHAPE), (dict(B=70000), SHAPE),
     (dict(max_blocks_per_seq=1 << 30), SHAPE),
     (dict(Hkv=5), GQA), (dict(D=32), HEAD_DIM),
@@ -220,6 +242,7 @@ def test_paged_prefill_check():
     assert check_varlen(varlen()) == OK
     assert check_varlen(varlen(block_size=128)) == OK
     assert check_varlen(varlen(dtype=sdpa.ATTN_F32)) == UNSUPPORTED
+    assert check_varlen(varlen(dtype=sdpa.ATTN_F64)) == UNSUPPORTED
     assert check_varlen(varlen(block_size=16)) == UNSUPPORTED
     assert check_varlen(varlen(D=80)) == HEAD_DIM
     assert check_varlen(varlen(Hq=6, Hkv=4)) == GQA

@@ -16,7 +16,7 @@ from gpu_util import announce, compare
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}
 
 
 def gpu_fwd(sdpa, q, k, v, alibi, **kw):
@@ -45,7 +45,8 @@ def run_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=No
             f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
     q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
     sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
-    kw = dict(scale=1.0 / math.sqrt(D), causal=causal, window_left=wl, window_right=wr,
+    # the ABI takes the scale as float32: both sides get that value
+    kw = dict(scale=float(np.float32(1.0 / math.sqrt(D))), causal=causal, window_left=wl, window_right=wr,
               softcap=softcap)
     announce(name)
     out = gpu_fwd(sdpa, q, k, v, sl, softmax_scale=kw["scale"], causal=causal,
@@ -119,6 +120,30 @@ def test_key_split_parity(gpu_lib, dtype, D, case):
 def test_f32_parity(gpu_lib, case):
     B, Hq, Hkv, Sq, Sk, D, kw = case
     run_case(gpu_lib, "f32", B, Hq, Hkv, Sq, Sk, D, seed=7, **kw)
+
+
+# The vector-ALU path in float64, and both vector-ALU precisions at the head
+# dims only it builds (32 and 256): every mask kind, ragged tiles, GQA.
+VALU_CASES = [
+    (1, 2, 2, 77, 77, dict()),
+    (2, 4, 2, 130, 100, dict(causal=True)),                       # Sq > Sk: rows 0..29 empty
+    (1, 4, 1, 100, 161, dict(causal=True, wl=40, wr=0, softcap=6.0, alibi=True, amp=2.0)),
+    (1, 2, 2, 90, 70, dict(wl=9, wr=4)),
+]
+
+
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+@pytest.mark.parametrize("case", range(len(VALU_CASES)))
+def test_f64_parity(gpu_lib, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = VALU_CASES[case]
+    run_case(gpu_lib, "f64", B, Hq, Hkv, Sq, Sk, D, seed=500 + case, **kw)
+
+
+@pytest.mark.parametrize("D", [32, 256])
+@pytest.mark.parametrize("case", range(len(VALU_CASES)))
+def test_f32_new_head_dims(gpu_lib, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = VALU_CASES[case]
+    run_case(gpu_lib, "f32", B, Hq, Hkv, Sq, Sk, D, seed=600 + case, **kw)
 
 
 def test_tiny_f32_workload(gpu_lib):
@@ -238,7 +263,9 @@ def test_binding_rejects_bad_arguments(gpu_lib):
 # f16 (10 bits), so if every weight of a row rounds the same way, ln(l) moves by
 # up to that much.  The float32 path sums exact float32 weights.  A
 # float32-accumulated score adds a relative 1e-5 of |lse|.
-LSE_TOL = {"bf16": 2.0 ** -8 + 1e-4, "f16": 2.0 ** -11 + 1e-4, "f32": 2e-6}
+# f64: the LSE is stored in float32 for every dtype, so its rounding (half an
+# ulp of |lse| <= 20, < 1e-6) is the bar
+LSE_TOL = {"bf16": 2.0 ** -8 + 1e-4, "f16": 2.0 ** -11 + 1e-4, "f32": 2e-6, "f64": 1e-6}
 
 
 def check_lse(got, ref, dtype, what):
@@ -260,7 +287,7 @@ def run_lse_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, w
     sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
     dev = torch.device("cuda:0")
     args = (q.to(dev), k.to(dev), v.to(dev), None if sl is None else sl.to(dev))
-    kw = dict(softmax_scale=1.0 / math.sqrt(D), causal=causal, window_left=wl, window_right=wr,
+    kw = dict(softmax_scale=float(np.float32(1.0 / math.sqrt(D))), causal=causal, window_left=wl, window_right=wr,
               softcap=softcap)
     announce(name)
     out, lse = sdpa.attn_fwd_lse(*args, **kw)
@@ -294,3 +321,9 @@ def test_lse_key_split_parity(gpu_lib, case):
 def test_lse_parity_f32(gpu_lib, case):
     B, Hq, Hkv, Sq, Sk, D, kw = case
     run_lse_case(gpu_lib, "f32", B, Hq, Hkv, Sq, Sk, D, seed=9, **kw)
+
+
+@pytest.mark.parametrize("D", [32, 256])
+def test_lse_parity_f64(gpu_lib, D):
+    B, Hq, Hkv, Sq, Sk, kw = VALU_CASES[2]
+    run_lse_case(gpu_lib, "f64", B, Hq, Hkv, Sq, Sk, D, seed=11, **kw)

@@ -123,6 +123,11 @@ def dense_inputs(w: Dense, seed: Optional[int] = None):
 def random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp=1.0):
     """Ad-hoc dense case with the same recipe (tests of edge shapes)."""
     rng = np.random.default_rng(seed)
+    if dtype == "f64":  # drawn in float64 directly: full 53-bit inputs
+        q = rng.standard_normal((B, Hq, Sq, D)) * amp
+        k = rng.standard_normal((B, Hkv, Sk, D)) * amp
+        v = rng.standard_normal((B, Hkv, Sk, D)) * amp
+        return torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)
     q = rng.standard_normal((B, Hq, Sq, D), dtype=np.float32) * np.float32(amp)
     k = rng.standard_normal((B, Hkv, Sk, D), dtype=np.float32) * np.float32(amp)
     v = rng.standard_normal((B, Hkv, Sk, D), dtype=np.float32) * np.float32(amp)
