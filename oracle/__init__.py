@@ -5,7 +5,8 @@ CPU-baseline leg may import this package.  The HIP library never imports it,
 links it or calls it, and the two share no code.
 
 * :mod:`oracle.sdpa`       -- NumPy float64: materialised-score definition,
-  online (tiled) recurrence, split partial + log-sum-exp merge, paged decode.
+  online (tiled) recurrence, split partial + log-sum-exp merge, paged decode,
+  varlen paged prefill, per-row log-sum-exp and the backward pass.
 * :mod:`oracle.bruteforce` -- pure-Python 50-digit decimal statement of the same
   definition, for tiny inputs.
 """
@@ -22,5 +23,6 @@ from .sdpa import (  # noqa: F401
     sdpa_naive_f64,
     sdpa_online_f64,
     sdpa_lse_f64,
+    sdpa_backward_f64,
     transform_scores,
 )

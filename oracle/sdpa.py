@@ -9,11 +9,12 @@ reads anything the HIP library produced.
 Sources (cited by page title and section; no other authority is used):
 
 * "fuel-reference-backend -- attention kernel contracts" (the kernel-contract
-  page), sections ``attention_naive``, ``attention_flash`` and
-  ``attention_paged_naive``: shapes ``[B, H, S, D]``, GQA broadcast, the order
-  of the score transforms (scale, softcap, ALiBi), the mask rules, stable
-  softmax, the zero output of a fully masked row, and paged address
-  translation with its implicit causal position.
+  page), sections ``attention_naive``, ``attention_flash``,
+  ``attention_paged_naive`` and ``attention_flash_backward``: shapes
+  ``[B, H, S, D]``, GQA broadcast, the order of the score transforms (scale,
+  softcap, ALiBi), the mask rules, stable softmax, the zero output of a fully
+  masked row, paged address translation with its implicit causal position,
+  and the gradient closed form of the backward pass.
 * "gfx942 unified attention, from the math up" (the derivation page): section 1
   (definition), section 2 (shift invariance of softmax), section 3 (the online
   recurrence), section 4 (bottom-right causal alignment when Sq != Sk),
@@ -52,6 +53,10 @@ __all__ = [
     "paged_gather",
     "paged_decode_f64",
     "paged_prefill_varlen_f64",
+    "sdpa_backward_f64",
+    "softmax_backward",
+    "softcap_derivative",
+    "score_input_grads",
     "admissible_pair_count",
 ]
 
@@ -398,6 +403,86 @@ def paged_prefill_varlen_f64(q, k_pool, v_pool, block_table, seq_lens, cu_seqlen
                             window_right=window_right, softcap=softcap, alibi=alibi)
         out[r0:r1] = np.transpose(ob[0], (1, 0, 2))
     return out
+
+
+def softmax_backward(p, dp):
+    """``dS = (dP - sum_j' P dP) P`` row by row (kernel-contract page,
+    ``attention_flash_backward``: the softmax backward)."""
+    return (dp - (p * dp).sum(axis=1, keepdims=True)) * p
+
+
+def softcap_derivative(s_pre, softcap):
+    """``d/ds_pre [c tanh(s_pre / c)] = 1 - tanh^2(s_pre / c)`` (kernel-contract
+    page, ``attention_flash_backward``: the softcap-derivative factor)."""
+    return 1.0 - np.tanh(s_pre / softcap) ** 2
+
+
+def score_input_grads(ds, qrows, kmat, scale):
+    """``(dQ rows, dK)`` of the scaled scores ``s_pre = scale Q K^T`` for the
+    score gradient ``ds``: ``scale dS K`` and ``scale dS^T Q``."""
+    return scale * (ds @ kmat), scale * (ds.T @ qrows)
+
+
+def sdpa_backward_f64(q, k, v, do, *, scale, causal=False, window_left=None,
+                      window_right=None, softcap=None, alibi=None, row_block=256):
+    """Gradients ``(dq, dk, dv)`` of the attention forward with respect to
+    ``q, k, v`` for the upstream gradient ``do`` of its output.
+
+    Kernel-contract page, ``attention_flash_backward``: recompute each row's
+    stable-softmax weights ``P`` (and its pre-softcap score), then
+
+    * ``dV[j] += P[i, j] dO[i]``
+    * ``dP[i, j] = dO[i] . V[j]``
+    * ``dS[i, j] = (dP[i, j] - sum_j' P[i, j'] dP[i, j']) P[i, j]``, times
+      ``1 - tanh^2(s_pre / c)`` when a softcap ``c`` is set (``s_pre`` = the
+      scaled score before the softcap; ALiBi adds a constant, no factor)
+    * ``dQ[i] += scale sum_j dS[i, j] K[j]`` and ``dK[j] += scale sum_i dS[i, j] Q[i]``.
+
+    dK and dV are ``[B, Hkv, Sk, D]``, summed over the query heads of each KV
+    head's group; dQ is ``[B, Hq, Sq, D]``.  A row with no admissible key
+    contributes nothing (its weights are all zero).  Rows are processed
+    ``row_block`` at a time only to bound memory.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Hkv, Sq, Sk, D = _check_common(q, k, v, alibi, softcap)
+    if do.shape != q.shape:
+        raise ValueError("do must have the shape of q")
+    slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if Sq == 0 or Sk == 0:
+        return dq, dk, dv
+    ip_all = query_positions(Sq, Sk)
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            for r0 in range(0, Sq, row_block):
+                rows = slice(r0, min(Sq, r0 + row_block))
+                ok = admissible(Sq, Sk, causal, window_left, window_right, rows)
+                has_key = ok.any(axis=1)
+                s_pre = (q[b, h, rows] @ k[b, g].T) * scale
+                s = transform_scores(s_pre, softcap, None if slopes is None else slopes[h],
+                                     j - ip_all[rows][:, None])
+                s = np.where(ok, s, -np.inf)
+                m = np.where(has_key, s.max(axis=1), 0.0)[:, None]
+                e = np.exp(s - m)                                   # 0 where masked
+                den = e.sum(axis=1, keepdims=True)
+                p = np.divide(e, den, out=np.zeros_like(e), where=has_key[:, None])
+                dov = do[b, h, rows]
+                dv[b, g] += p.T @ dov
+                dp = dov @ v[b, g].T
+                ds = softmax_backward(p, dp)
+                if softcap:
+                    ds = ds * softcap_derivative(s_pre, softcap)
+                dqr, dkr = score_input_grads(ds, q[b, h, rows], k[b, g], scale)
+                dq[b, h, rows] += dqr
+                dk[b, g] += dkr
+    return dq, dk, dv
 
 
 def admissible_pair_count(Sq, Sk, causal, window_left=None, window_right=None):

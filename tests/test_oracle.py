@@ -495,3 +495,132 @@ def test_varlen_equal_lengths_is_the_paged_form():
     with pytest.raises(ValueError):
         osd.paged_prefill_varlen_f64(c["q"], c["kp"], c["vp"], c["table"], c["lens"],
                                      [0, 5, 3, 12], scale=0.5)
+
+
+# --------------------------------------------------------------------------
+# Backward pass (kernel-contract page, attention_flash_backward)
+# --------------------------------------------------------------------------
+
+BWD_KW = [
+    dict(),
+    dict(causal=True),
+    dict(causal=True, window_left=2, window_right=0),
+    dict(window_left=1, window_right=2),
+    dict(softcap=1.5),
+    dict(alibi=[0.5, -0.3]),
+    dict(causal=True, softcap=2.0, alibi=[0.25, 0.75]),
+]
+
+
+def _bwd_case(rng, B=1, Hq=2, Hkv=1, Sq=4, Sk=5, D=3, amp=1.0):
+    return (_rand(rng, B, Hq, Sq, D, amp=amp), _rand(rng, B, Hkv, Sk, D, amp=amp),
+            _rand(rng, B, Hkv, Sk, D), _rand(rng, B, Hq, Sq, D))
+
+
+def check_bwd_finite_differences(bwd):
+    """Each gradient is the derivative of L = sum(dO * O) through the (pinned)
+    forward definition: central differences, step 1e-5, on every element of
+    q, k and v; the truncation error is O(h^2) ~ 1e-10 and the rounding error
+    ~ 1e-16 / h, both far under the 1e-7 bar."""
+    rng = np.random.default_rng(41)
+    h = 1e-5
+    for kw in BWD_KW:
+        for Sq, Sk in ((4, 5), (6, 4)):           # (6, 4) causal: rows 0, 1 have no key
+            q, k, v, do = _bwd_case(rng, Sq=Sq, Sk=Sk, amp=1.3)
+            got = bwd(q, k, v, do, scale=0.7, **kw)
+
+            def loss(q_, k_, v_):
+                return float(np.sum(do * osd.sdpa_naive_f64(q_, k_, v_, scale=0.7, **kw)))
+            for which, x in enumerate((q, k, v)):
+                num = np.zeros_like(x)
+                for idx in np.ndindex(x.shape):
+                    xp, xm = x.copy(), x.copy()
+                    xp[idx] += h
+                    xm[idx] -= h
+                    args_p = [q, k, v]
+                    args_m = [q, k, v]
+                    args_p[which], args_m[which] = xp, xm
+                    num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                err = np.abs(got[which] - num).max()
+                assert err < 1e-7, (kw, Sq, Sk, "qkv"[which], err)
+
+
+def check_bwd_constant_v(bwd):
+    """V rows all equal to one vector c make O = c for every row with a key,
+    independent of q and k: dQ = dK = 0, and dV[j] = sum_i P[i, j] dO[i], so
+    the dV rows of a head sum to the sum of its dO rows with a key."""
+    rng = np.random.default_rng(42)
+    q, k, _, do = _bwd_case(rng, Hq=4, Hkv=2, Sq=7, Sk=5, D=4)
+    c = rng.standard_normal(4)
+    v = np.broadcast_to(c, (1, 2, 5, 4)).copy()
+    for kw in (dict(), dict(causal=True), dict(causal=True, softcap=1.0, alibi=[0.1, 0.2, 0.3, 0.4])):
+        dq, dk, dv = bwd(q, k, v, do, scale=0.9, **kw)
+        assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13, kw
+        has_key = osd.admissible(7, 5, kw.get("causal", False)).any(axis=1)
+        for g in range(2):
+            want = do[0, 2 * g:2 * g + 2][:, has_key].sum(axis=(0, 1))
+            np.testing.assert_allclose(dv[0, g].sum(axis=0), want, rtol=1e-12, atol=1e-12)
+
+
+def check_bwd_dk_rows_sum_to_zero(bwd):
+    """Adding one vector w to every key shifts each row's scores by the
+    per-row constant scale q_i . w, which softmax ignores (derivation page,
+    section 2): without a softcap the dK rows of each KV head sum to zero,
+    masks and ALiBi included."""
+    rng = np.random.default_rng(43)
+    q, k, v, do = _bwd_case(rng, B=2, Hq=4, Hkv=2, Sq=6, Sk=8, D=5)
+    for kw in (dict(), dict(causal=True), dict(window_left=2, window_right=1, alibi=[0.3, -0.2, 0.5, 0.1])):
+        _, dk, _ = bwd(q, k, v, do, scale=0.6, **kw)
+        assert np.abs(dk.sum(axis=2)).max() < 1e-12, kw
+
+
+def check_bwd_gqa_is_summed_mha(bwd):
+    """GQA = MHA on repeat-interleaved K/V (derivation page, section 5), so
+    the GQA dK/dV of a KV head is the sum of the MHA dK/dV of its group."""
+    rng = np.random.default_rng(44)
+    q, k, v, do = _bwd_case(rng, Hq=6, Hkv=2, Sq=5, Sk=6, D=3)
+    kw = dict(causal=True, softcap=2.5, alibi=[0.1, 0.2, 0.3, 0.4, 0.5, 0.6])
+    dq, dk, dv = bwd(q, k, v, do, scale=0.8, **kw)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    dq2, dk2, dv2 = bwd(q, kr, vr, do, scale=0.8, **kw)
+    np.testing.assert_allclose(dq, dq2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(1, 2, 3, 6, 3).sum(axis=2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(1, 2, 3, 6, 3).sum(axis=2), rtol=1e-12, atol=1e-13)
+
+
+def check_bwd_empty_rows_and_linearity(bwd):
+    """Rows with no admissible key contribute nothing: their dQ rows are 0 and
+    their dO is ignored; the gradients are linear in dO."""
+    rng = np.random.default_rng(45)
+    q, k, v, do = _bwd_case(rng, Sq=7, Sk=4, D=3)      # causal: rows 0..2 have no key
+    kw = dict(causal=True, alibi=[0.2, 0.4])
+    dq, dk, dv = bwd(q, k, v, do, scale=1.1, **kw)
+    assert np.all(dq[:, :, :3] == 0)
+    do2 = do.copy()
+    do2[:, :, :3] = rng.standard_normal(do2[:, :, :3].shape) * 100
+    _, dk2, dv2 = bwd(q, k, v, do2, scale=1.1, **kw)
+    np.testing.assert_allclose(dk2, dk, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dv2, dv, rtol=1e-12, atol=1e-12)
+    e = rng.standard_normal(do.shape)
+    sums = bwd(q, k, v, do + 2 * e, scale=1.1, **kw)
+    parts = [a + 2 * b for a, b in zip(bwd(q, k, v, do, scale=1.1, **kw), bwd(q, k, v, e, scale=1.1, **kw))]
+    for x, y in zip(sums, parts):
+        np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-12)
+
+
+BWD_CHECKS = [check_bwd_finite_differences, check_bwd_constant_v, check_bwd_dk_rows_sum_to_zero,
+              check_bwd_gqa_is_summed_mha, check_bwd_empty_rows_and_linearity]
+
+
+@pytest.mark.parametrize("check", BWD_CHECKS, ids=lambda c: c.__name__)
+def test_backward_pins(check):
+    check(osd.sdpa_backward_f64)
+
+
+def test_backward_zero_extents_and_errors():
+    q = np.zeros((1, 2, 0, 4))
+    k = np.zeros((1, 1, 3, 4))
+    dq, dk, dv = osd.sdpa_backward_f64(q, k, k, q, scale=1.0)
+    assert dq.shape == (1, 2, 0, 4) and np.all(dk == 0) and np.all(dv == 0)
+    with pytest.raises(ValueError):
+        osd.sdpa_backward_f64(np.zeros((1, 2, 3, 4)), k, k, np.zeros((1, 2, 2, 4)), scale=1.0)

@@ -93,6 +93,27 @@ def _gather_row_wrong(pool, block_table, seq_len, b, block_size):
     return np.asarray(pool)[phys, t % block_size]
 
 
+def _sm_bwd_row_term_dropped(p, dp):
+    return dp * p
+
+
+def _cap_deriv_dropped(s_pre, softcap):
+    return np.ones_like(s_pre)
+
+
+def _cap_deriv_unsquared(s_pre, softcap):
+    return 1.0 - np.tanh(s_pre / softcap)
+
+
+def _grads_dk_unscaled(ds, qrows, kmat, scale):
+    return scale * (ds @ kmat), ds.T @ qrows
+
+
+def _grads_dk_rows_permuted(ds, qrows, kmat, scale):
+    # dK taken against the query rows in reverse order (a transposed index)
+    return scale * (ds @ kmat), scale * (ds.T @ qrows[::-1])
+
+
 MUTANTS = {
     "causal_top_left": ("query_positions", lambda Sq, Sk: np.arange(Sq)),
     "causal_strict": ("admissible", _adm_strict_causal),
@@ -107,6 +128,11 @@ MUTANTS = {
     "query_rows_permuted": ("_scores", _scores_kq_swapped),
     "paged_slot_off_by_one": ("paged_gather", _gather_slot_wrong),
     "paged_wrong_sequence_row": ("paged_gather", _gather_row_wrong),
+    "bwd_softmax_row_term_dropped": ("softmax_backward", _sm_bwd_row_term_dropped),
+    "bwd_softcap_derivative_dropped": ("softcap_derivative", _cap_deriv_dropped),
+    "bwd_softcap_derivative_unsquared": ("softcap_derivative", _cap_deriv_unsquared),
+    "bwd_dk_unscaled": ("score_input_grads", _grads_dk_unscaled),
+    "bwd_dk_query_rows_permuted": ("score_input_grads", _grads_dk_rows_permuted),
 }
 
 
@@ -126,6 +152,11 @@ def _run_all_checks():
         pins.test_paged_equals_dense_and_decode_noncausal()
     except (AssertionError, ValueError, IndexError):
         failures.append("paged_equals_dense")
+    for check in pins.BWD_CHECKS:
+        try:
+            check(osd.sdpa_backward_f64)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failures.append(check.__name__)
     return failures
 
 
