@@ -241,6 +241,44 @@ attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* 
                                  int32_t* error_flag, const attn_varlen_params_t* p,
                                  void* stream);
 
+/* ---- backward (kernel-contract page, attention_flash_backward) ----------
+ * Gradients of attn_fwd with respect to q, k and v for the upstream gradient
+ * dout of its output, by recompute: the entry point re-runs the forward
+ * softmax of every row (its log-sum-exp and dout . out land in the
+ * workspace), then forms dV += P^T dO, dP = dO V^T, dS = (dP - rowsum(P dP))
+ * P (times 1 - tanh^2(s_pre / softcap) with a softcap), dQ = scale dS K and
+ * dK = scale dS^T Q.  dk and dv are [B, Hkv, Sk, D], summed over the query
+ * heads of each KV head's group; dq is [B, Hq, Sq, D].  A row with no
+ * admissible key contributes nothing.  F16/BF16 only (matrix cores, float32
+ * accumulation, P and dS rounded to the input dtype as matmul operands);
+ * F32/F64 give ATTN_ERR_UNSUPPORTED.  Deterministic: no atomics, fixed
+ * order. */
+
+/* Workspace bytes attn_bwd needs for p (8 * B * Hq * Sq), 0 for an invalid p. */
+size_t attn_bwd_workspace_size(const attn_fwd_params_t* p);
+
+/* Host-only validation of an attn_bwd call (no HIP call is made).
+ *   q, dout    [B, Hq, Sq, D]   dtype
+ *   k, v       [B, Hkv, Sk, D]  dtype
+ *   alibi      [Hq] float32 or NULL
+ *   dq         [B, Hq, Sq, D]   dtype
+ *   dk, dv     [B, Hkv, Sk, D]  dtype
+ *   workspace  >= attn_bwd_workspace_size(p) bytes, 16-byte aligned.
+ * The outputs and the workspace overlap no input and no other output.  The
+ * rules of attn_fwd_check apply to p, q, k, v and alibi. */
+attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const void* dout,
+                             const float* alibi, const void* dq, const void* dk,
+                             const void* dv, const void* workspace, size_t workspace_bytes,
+                             const attn_fwd_params_t* p);
+
+/* Attention backward: validates as attn_bwd_check, then enqueues three
+ * kernels on `stream` (the forward's row statistics, dK/dV, dQ) and returns.
+ * The workspace is scratch for the duration of the call; its contents
+ * afterwards are unspecified. */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                       const float* alibi, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, const attn_fwd_params_t* p, void* stream);
+
 /* Static string naming a status code. */
 const char* attn_status_str(attn_status_t status);
 

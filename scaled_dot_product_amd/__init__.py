@@ -33,6 +33,7 @@ __all__ = [
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
     "attn_paged_params", "attn_status_str", "attn_version",
     "attn_paged_prefill", "attn_paged_prefill_check", "attn_varlen_params",
+    "attn_bwd", "attn_bwd_check", "attn_bwd_workspace_size",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_F64",
 ]
 
@@ -117,6 +118,12 @@ def library():
     lib.attn_paged_prefill_check.restype = ctypes.c_int
     lib.attn_paged_prefill.argtypes = [_VP] * 9 + [var_p, _VP]
     lib.attn_paged_prefill.restype = ctypes.c_int
+    lib.attn_bwd_workspace_size.argtypes = [fwd_p]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd_check.argtypes = [_VP] * 9 + [ctypes.c_size_t, fwd_p]
+    lib.attn_bwd_check.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [_VP] * 9 + [ctypes.c_size_t, fwd_p, _VP]
+    lib.attn_bwd.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -234,6 +241,48 @@ def attn_fwd_lse(q, k, v, alibi=None, out=None, lse=None, *, softmax_scale=None,
     if st != 0:
         raise AttnError(st, "attn_fwd_lse")
     return out, lse
+
+
+def attn_bwd_workspace_size(params: attn_fwd_params_t) -> int:
+    return int(library().attn_bwd_workspace_size(None if params is None else ctypes.byref(params)))
+
+
+def attn_bwd_check(q_ptr, k_ptr, v_ptr, do_ptr, alibi_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
+                   ws_bytes, params: attn_fwd_params_t) -> int:
+    """Host-only argument check of attn_bwd (no HIP call): the status code."""
+    return int(library().attn_bwd_check(q_ptr, k_ptr, v_ptr, do_ptr, alibi_ptr, dq_ptr, dk_ptr,
+                                        dv_ptr, ws_ptr, ws_bytes,
+                                        None if params is None else ctypes.byref(params)))
+
+
+def attn_bwd(q, k, v, dout, alibi=None, *, softmax_scale=None, causal=False, window_left=None,
+             window_right=None, softcap=None, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """Gradients ``(dq, dk, dv)`` of :func:`attn_fwd` for the upstream gradient
+    ``dout`` (see attn.h); dk/dv are summed over each KV head's query group."""
+    lib = library()
+    # (q stands in for the forward's output: only its shape and dtype are checked)
+    dev, _, p = _fwd_args(q, k, v, alibi, q, softmax_scale, causal, window_left,
+                          window_right, softcap)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv), ("workspace", workspace)):
+        _need_device(name, t, dev)
+    if dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must match q in shape and dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its input")
+    need = attn_bwd_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(alibi), _ptr(dq), _ptr(dk),
+                      _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                      ctypes.byref(p), _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_paged_params(q_shape, pool_shape, max_blocks_per_seq, dtype, *, softmax_scale=None,

@@ -38,10 +38,11 @@ UNITS = [("attn_api.cpp", [], "attn_api.o"),
          ("decode.hip", KERNEL_FLAGS, "decode.o")]
 for _elem, _tag in (("__bf16", "bf16"), ("_Float16", "f16")):
     for _d in (128, 64):
-        UNITS.append(("fwd_mfma.hip",
-                      KERNEL_FLAGS + [f"-DATTN_ELEM={_elem}", f"-DATTN_D={_d}",
-                                      f"-DATTN_TAG={_tag}_d{_d}"],
-                      f"fwd_mfma_{_tag}_d{_d}.o"))
+        for _src in ("fwd_mfma", "bwd_mfma"):
+            UNITS.append((f"{_src}.hip",
+                          KERNEL_FLAGS + [f"-DATTN_ELEM={_elem}", f"-DATTN_D={_d}",
+                                          f"-DATTN_TAG={_tag}_d{_d}"],
+                          f"{_src}_{_tag}_d{_d}.o"))
 
 
 def hipcc() -> str:

@@ -25,6 +25,17 @@ hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream) {
   return p.D == 128 ? launch_fwd_mfma_f16_d128(p, stream) : launch_fwd_mfma_f16_d64(p, stream);
 }
 
+hipError_t launch_bwd_mfma_bf16_d128(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_mfma_bf16_d64(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_mfma_f16_d128(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_mfma_f16_d64(const BwdProblem& p, hipStream_t stream);
+
+hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream) {
+  if (dtype == ATTN_BF16)
+    return p.D == 128 ? launch_bwd_mfma_bf16_d128(p, stream) : launch_bwd_mfma_bf16_d64(p, stream);
+  return p.D == 128 ? launch_bwd_mfma_f16_d128(p, stream) : launch_bwd_mfma_f16_d64(p, stream);
+}
+
 hipError_t launch_paged_prefill_bf16_d128(const PagedPrefillProblem& p, hipStream_t stream);
 hipError_t launch_paged_prefill_bf16_d64(const PagedPrefillProblem& p, hipStream_t stream);
 hipError_t launch_paged_prefill_f16_d128(const PagedPrefillProblem& p, hipStream_t stream);
@@ -212,6 +223,102 @@ attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, const fl
   const attn_status_t st = attn_fwd_lse_check(q, k, v, alibi, out, lse, p);
   if (st != ATTN_OK) return st;
   return launch_fwd(q, k, v, alibi, out, lse, p, stream);
+}
+
+size_t attn_bwd_workspace_size(const attn_fwd_params_t* p) {
+  if (!p || !valid_dtype(p->dtype)) return 0;
+  int64_t qb, kvb;
+  if (fwd_shape(p, &qb, &kvb) != ATTN_OK) return 0;
+  return (size_t)(p->B * p->Hq * p->Sq * 8);
+}
+
+attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const void* dout,
+                             const float* alibi, const void* dq, const void* dk, const void* dv,
+                             const void* workspace, size_t workspace_bytes,
+                             const attn_fwd_params_t* p) {
+  if (!p) return ATTN_ERR_NULL;
+  if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
+  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) return ATTN_ERR_UNSUPPORTED;
+  // q, k, v, alibi and the parameters as for the forward, with dq in out's place
+  attn_status_t st = check_fwd(q, k, v, alibi, dq, p);
+  if (st != ATTN_OK) return st;
+  int64_t qb, kvb;
+  fwd_shape(p, &qb, &kvb);
+  if (qb > 0 && !dout) return ATTN_ERR_NULL;
+  if (kvb > 0 && (!dk || !dv)) return ATTN_ERR_NULL;
+  const int64_t ws_need = p->B * p->Hq * p->Sq * 8;
+  if (ws_need > 0 && (!workspace || workspace_bytes < (size_t)ws_need)) return ATTN_ERR_WORKSPACE;
+  const void* ptrs[] = {dout, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return ATTN_ERR_ALIGN;
+  const Span in[] = {{q, qb}, {k, kvb}, {v, kvb}, {dout, qb}, {alibi, p->Hq * 4}};
+  const Span outs[] = {{dq, qb}, {dk, kvb}, {dv, kvb}, {workspace, ws_need}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Span& x : in)
+      if (overlaps(outs[i], x)) return ATTN_ERR_ALIAS;
+    for (int j2 = i + 1; j2 < 4; ++j2)
+      if (overlaps(outs[i], outs[j2])) return ATTN_ERR_ALIAS;
+  }
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                       const float* alibi, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, const attn_fwd_params_t* p, void* stream) {
+  const attn_status_t st =
+      attn_bwd_check(q, k, v, dout, alibi, dq, dk, dv, workspace, workspace_bytes, p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Hkv == 0) return ATTN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int wl = (p->window_left < 0 || p->window_left >= p->Sk) ? -1 : (int)p->window_left;
+  const int wr = (p->window_right < 0 || p->window_right >= p->Sq) ? -1 : (int)p->window_right;
+  // 1. the forward's row statistics (LSE, dO . O) into the workspace
+  if (p->Hq > 0 && p->Sq > 0) {
+    attn::FwdProblem fp;
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.alibi = alibi;
+    fp.out = nullptr;
+    fp.lse = nullptr;
+    fp.dout = dout;
+    fp.stats = static_cast<float*>(workspace);
+    fp.B = (int)p->B;
+    fp.Hq = (int)p->Hq;
+    fp.Hkv = (int)p->Hkv;
+    fp.Sq = (int)p->Sq;
+    fp.Sk = (int)p->Sk;
+    fp.D = (int)p->D;
+    fp.causal = p->causal != 0;
+    fp.wl = wl;
+    fp.wr = wr;
+    fp.scale = p->softmax_scale;
+    fp.softcap = p->softcap;
+    if (attn::launch_fwd_mfma(fp, p->dtype, s) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  // 2. dK, dV (every key row, zero where no query sees it) and dQ
+  attn::BwdProblem bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.dout = dout;
+  bp.alibi = alibi;
+  bp.stats = static_cast<const float*>(workspace);
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.B = (int)p->B;
+  bp.Hq = (int)p->Hq;
+  bp.Hkv = (int)p->Hkv;
+  bp.Sq = (int)p->Sq;
+  bp.Sk = (int)p->Sk;
+  bp.D = (int)p->D;
+  bp.causal = p->causal != 0;
+  bp.wl = wl;
+  bp.wr = wr;
+  bp.scale = p->softmax_scale;
+  bp.softcap = p->softcap;
+  return attn::launch_bwd_mfma(bp, p->dtype, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 size_t attn_paged_decode_workspace_size(const attn_paged_params_t* p) {

@@ -1,0 +1,544 @@
+// bwd_mfma.hip -- attention backward on the matrix cores (bf16 / f16, head
+// dim 64 or 128): dQ, dK, dV by recompute.
+//
+// Kernel-contract page, attention_flash_backward: with P the stable-softmax
+// weights of the forward (recomputed from Q, K and the forward's per-row
+// log-sum-exp), dV += P^T dO, dP = dO V^T, dS = (dP - rowsum(P dP)) P, times
+// 1 - tanh^2(s_pre / c) under a softcap c, dQ = scale dS K, dK = scale dS^T Q,
+// with dK / dV summed over each KV head's query group.  rowsum(P dP) equals
+// dO . O (the derivation page's section 1: O is the P-weighted sum of V rows),
+// which the forward pass computes per row from its float32 accumulator
+// (`stats`, together with the log-sum-exp in log2 units).
+//
+// Two kernels, each owning what it writes, so no atomics and a fixed order:
+//
+//  * bwd_dkdv_kernel: a workgroup owns 128 keys of one (sequence, KV head),
+//    each of its 4 waves 32 of them.  It walks every query head of the group
+//    and every 32-query tile that can see those keys; the tiles of Q, dO and
+//    the row statistics are copied global -> LDS asynchronously, double
+//    buffered, shared by the 4 waves.  Per tile and wave, with the wave's
+//    keys in the accumulator columns (one key per lane):
+//      S  = Q K^T   (Q rows from LDS, K in registers)     8 MFMAs at D = 128
+//      dP = dO V^T  (dO rows from LDS, V in registers)    8
+//      dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read through the
+//      LDS transpose read and P, dS already in the B-operand layout   8 + 8
+//  * bwd_dq_kernel: the forward kernel's shape -- 4 waves x 32 query rows, K
+//    and V tiles of 64 keys through LDS -- with, per tile,
+//      S^T = K Q^T and dP^T = V dO^T (Q and dO in registers)          16 + 16
+//      dQ^T += K^T dS^T (K^T through the LDS transpose read)          16
+#include <limits.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+#ifndef ATTN_ELEM
+#error "build with -DATTN_ELEM=<__bf16|_Float16> -DATTN_D=<64|128> -DATTN_TAG=<name>"
+#endif
+#define ATTN_CAT2(a, b) a##b
+#define ATTN_CAT(a, b) ATTN_CAT2(a, b)
+
+namespace attn {
+namespace {
+
+constexpr int kNW = 4;
+constexpr int kThreads = kNW * 64;
+constexpr int kBQ = 32;       // dK/dV: queries per tile
+constexpr int kKW = 32;       // dK/dV: keys per wave
+constexpr int kBK = kNW * kKW;  // dK/dV: keys per workgroup
+constexpr int kBN = 64;       // dQ: keys per tile
+constexpr int kQW = 32;       // dQ: query rows per wave
+constexpr int kBM = kNW * kQW;  // dQ: query rows per workgroup
+
+enum : int { B_MASK = 1, B_SOFTCAP = 2, B_ALIBI = 4 };
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* alibi;
+  const float2* stats;  // [B * Hq * Sq]: (LSE in log2 units, +inf without keys; dO . O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int Sq, Sk, Hq, Hkv, group;
+  int wl;        // left window, -1 = unbounded
+  int has_hi;    // is j - i' bounded above?
+  int dmax;      // that bound
+  float scale;   // softmax scale
+  float c_score; // log2(e) * scale; with softcap 2 * log2(e) * scale / cap
+  float c_cap;   // log2(e) * cap
+  int nbh_kv;    // B * Hkv
+  int nbh;       // B * Hq
+  int nqb;       // dQ: 128-row query blocks per head
+  int heavy_first;
+};
+
+// XOR swizzle of the 16-byte chunk index of tile row r: the matrix-operand
+// row reads (32 rows, one chunk each) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Transformed score in log2 units (softcap, then ALiBi) of the raw dot
+// product x, and tanh(s_pre / cap) for the softcap derivative.
+template <bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ float transform(float x, const BwdArgs& a, float slope_l2, int rel,
+                                           float& t) {
+  float y;
+  if constexpr (SOFTCAP) {
+    const float e = fast_exp2(x * a.c_score);
+    t = 1.f - 2.f * fast_rcp(1.f + e);
+    y = a.c_cap * t;
+  } else {
+    t = 0.f;
+    y = x * a.c_score;
+  }
+  if constexpr (ALIBI) y = __builtin_fmaf(slope_l2, (float)rel, y);
+  return y;
+}
+
+// A = X^T (d rows x 16 tile rows per step) through the LDS transpose read, for
+// the 32x32x16 instruction: step ks covers tile rows 16 ks .. 16 ks + 15 in
+// the order the accumulator holds them (rows 4 g .. 4 g + 3, then 8 + 4 g ..),
+// d block db.  Tile rows are D elements, chunks swizzled by swz.
+template <typename T, int D>
+__device__ __forceinline__ u32x4 tr_operand(const T* X, int ks, int db, int lane) {
+  const int g = (lane >> 5) & 1;
+  const int trow = 4 * g + ((lane & 15) >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int r0 = 16 * ks + trow;
+  const int col = 32 * db + tcol;
+  const int c_lo = ((col >> 3) ^ swz<D>(r0)) * 8 + (col & 7);
+  const int c_hi = ((col >> 3) ^ swz<D>(r0 + 8)) * 8 + (col & 7);
+  const u32x2 lo = lds_read_tr16(X + r0 * D + c_lo);
+  const u32x2 hi = lds_read_tr16(X + (r0 + 8) * D + c_hi);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Asynchronous copy of rows [row0, row0 + ROWS) of a [*, D] tensor (rows past
+// `rows_left` read zero) into a swizzled LDS tile, by all threads.
+template <typename T, int D, int ROWS>
+__device__ __forceinline__ void copy_tile(const T* base, int rows_left, u32x4* dst, int tid,
+                                          int wave) {
+  constexpr int NC = D / 8;
+  constexpr int TC = ROWS * NC;
+  constexpr int CPT = TC / kThreads;
+  static_assert(CPT * kThreads == TC, "tile must split evenly over the workgroup");
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc32(base, rows_left * D * (int)sizeof(T));
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * kThreads + tid;
+    const int r = c / NC, pc = c % NC;
+    dma16(rs, dst + i * kThreads + wave * 64, (r * D + (pc ^ swz<D>(r)) * 8) * (int)sizeof(T));
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <typename T, int D, int FLAGS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  using E = Elem<T>;
+  constexpr bool MASK = (FLAGS & B_MASK) != 0;
+  constexpr bool SOFTCAP = (FLAGS & B_SOFTCAP) != 0;
+  constexpr bool ALIBI = (FLAGS & B_ALIBI) != 0;
+  constexpr int NC = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TC = kBQ * NC;
+
+  __shared__ u32x4 qbuf0[TC], qbuf1[TC], obuf0[TC], obuf1[TC];
+  __shared__ float2 sbuf0[kBQ], sbuf1[kBQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int ln = lane & 31;
+
+  // ---- work item: key block kblk of (b, kvh); low key blocks see the most
+  // queries under a causal mask, so they go first
+  const int id = blockIdx.x;
+  const int kblk = id / a.nbh_kv;
+  const int bkv = id - kblk * a.nbh_kv;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const int k0 = kblk * kBK;
+  const int j0 = k0 + wave * kKW;  // this wave's first key
+  const int j = j0 + ln;           // this lane's key
+  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * Sk * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + kv_off;
+  const T* V = reinterpret_cast<const T*>(a.v) + kv_off;
+
+  // K and V rows of this lane's key as B operands: chunk 2 s + g
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = j < Sk ? load16(K + (size_t)j * D + 16 * s + 8 * g) : zero_u32x4();
+    vf[s] = j < Sk ? load16(V + (size_t)j * D + 16 * s + 8 * g) : zero_u32x4();
+  }
+
+  // admissible iff lo <= j - i' <= hi
+  const int lo = a.wl >= 0 ? -a.wl : INT_MIN / 2;
+  const int hi = a.has_hi ? a.dmax : INT_MAX / 2;
+  // query rows that can see a key of this workgroup: i' in [k0 - hi, k_last - lo]
+  const int k_last = min(k0 + kBK, Sk) - 1;
+  const int q_lo = a.has_hi ? max(0, k0 - hi - off) : 0;
+  const int q_hi = a.wl >= 0 ? min(Sq, k_last - lo - off + 1) : Sq;  // one past
+  const int t_lo = q_lo / kBQ;
+  const int nt = q_hi > q_lo && k_last >= k0 ? (q_hi + kBQ - 1) / kBQ - t_lo : 0;
+  const int n_items = nt * a.group;
+
+  // per wave: keys [j0, jw_last]
+  const int jw_last = min(j0 + kKW, Sk) - 1;
+  auto live = [&](int q0) {
+    if (jw_last < j0) return false;
+    const int ql = min(q0 + kBQ, Sq) - 1;
+    const int dlo = j0 - (ql + off), dhi = jw_last - (q0 + off);
+    return dhi >= lo && dlo <= hi;
+  };
+  auto full = [&](int q0) {
+    const int dlo = j0 - (q0 + kBQ - 1 + off), dhi = j0 + kKW - 1 - (q0 + off);
+    return q0 + kBQ <= Sq && j0 + kKW <= Sk && dlo >= lo && dhi <= hi;
+  };
+
+  floatx16 dkt[DB], dvt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkt[db] = floatx16{};
+    dvt[db] = floatx16{};
+  }
+
+  auto item_head = [&](int it) { return kvh * a.group + it / nt; };
+  auto item_q0 = [&](int it) { return (t_lo + it % nt) * kBQ; };
+  auto copy_item = [&](int it, u32x4* qd, u32x4* od, float2* sd) {
+    const int h = item_head(it), q0 = item_q0(it);
+    const size_t row0 = (size_t)(b * a.Hq + h) * Sq + q0;
+    copy_tile<T, D, kBQ>(reinterpret_cast<const T*>(a.q) + row0 * D, Sq - q0, qd, tid, wave);
+    copy_tile<T, D, kBQ>(reinterpret_cast<const T*>(a.dout) + row0 * D, Sq - q0, od, tid, wave);
+    if (wave == 0) {
+      // 32 (LSE, dO.O) pairs: one dword per lane
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc32(a.stats + row0, (Sq - q0) * 8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)sd, 4, 4 * lane, 0, 0, 0);
+    }
+  };
+
+  auto compute = [&](int it, const u32x4* qs, const u32x4* os, const float2* ss) {
+    const int h = item_head(it), q0 = item_q0(it);
+    if (!live(q0)) return;
+    // S = Q K^T, dP = dO V^T: 32 queries (rows) x this wave's 32 keys (lanes)
+    floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int c = (2 * st + g) ^ swz<D>(ln);
+      s = E::mma32(qs[ln * NC + c], kf[st], s);
+      dp = E::mma32(os[ln * NC + c], vf[st], dp);
+    }
+    float slope_l2 = 0.f;
+    if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
+    const bool need_mask = MASK && !full(q0);
+    const float4* sp = reinterpret_cast<const float4*>(ss);
+    uint32_t pp[8], dsp[8];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      // accumulator rows 8 rr + 4 g + 0..3: statistics of 4 consecutive rows
+      const float4 s01 = sp[4 * rr + 2 * g], s23 = sp[4 * rr + 2 * g + 1];
+      const float lse2[4] = {s01.x, s01.z, s23.x, s23.z};
+      const float dlt[4] = {s01.y, s01.w, s23.y, s23.w};
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * rr + c;
+        const int qrow = q0 + 8 * rr + 4 * g + c;
+        const int rel = j - (qrow + off);
+        float t;
+        float x = transform<SOFTCAP, ALIBI>(s[r], a, slope_l2, rel, t);
+        if (need_mask && (qrow >= Sq || j >= Sk || rel < lo || rel > hi)) x = kNegInf;
+        const float p = fast_exp2(x - lse2[c]);
+        float d = p * (dp[r] - dlt[c]);
+        if constexpr (SOFTCAP) d *= 1.f - t * t;
+        pv[c] = p;
+        dsv[c] = d;
+      }
+      pp[2 * rr] = E::pack2(pv[0], pv[1]);
+      pp[2 * rr + 1] = E::pack2(pv[2], pv[3]);
+      dsp[2 * rr] = E::pack2(dsv[0], dsv[1]);
+      dsp[2 * rr + 1] = E::pack2(dsv[2], dsv[3]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over the tile's 32 queries
+    const T* Os = reinterpret_cast<const T*>(os);
+    const T* Qs = reinterpret_cast<const T*>(qs);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pf = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
+      const u32x4 df = {dsp[4 * ks], dsp[4 * ks + 1], dsp[4 * ks + 2], dsp[4 * ks + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dvt[db] = E::mma32(tr_operand<T, D>(Os, ks, db, lane), pf, dvt[db]);
+        dkt[db] = E::mma32(tr_operand<T, D>(Qs, ks, db, lane), df, dkt[db]);
+      }
+    }
+  };
+
+  if (n_items > 0) copy_item(0, qbuf0, obuf0, sbuf0);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < n_items; it += 2) {
+    if (it + 1 < n_items) copy_item(it + 1, qbuf1, obuf1, sbuf1);
+    compute(it, qbuf0, obuf0, sbuf0);
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < n_items) {
+      if (it + 2 < n_items) copy_item(it + 2, qbuf0, obuf0, sbuf0);
+      compute(it + 1, qbuf1, obuf1, sbuf1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // ---- store: this lane's key row; d = 32 db + 8 jj + 4 g .. + 3
+  if (j < Sk) {
+    T* dkr = reinterpret_cast<T*>(a.dk) + kv_off + (size_t)j * D;
+    T* dvr = reinterpret_cast<T*>(a.dv) + kv_off + (size_t)j * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x2 wk, wv;
+        wk[0] = E::pack2(dkt[db][4 * jj] * a.scale, dkt[db][4 * jj + 1] * a.scale);
+        wk[1] = E::pack2(dkt[db][4 * jj + 2] * a.scale, dkt[db][4 * jj + 3] * a.scale);
+        wv[0] = E::pack2(dvt[db][4 * jj], dvt[db][4 * jj + 1]);
+        wv[1] = E::pack2(dvt[db][4 * jj + 2], dvt[db][4 * jj + 3]);
+        *reinterpret_cast<u32x2*>(dkr + 32 * db + 8 * jj + 4 * g) = wk;
+        *reinterpret_cast<u32x2*>(dvr + 32 * db + 8 * jj + 4 * g) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <typename T, int D, int FLAGS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdArgs a) {
+  using E = Elem<T>;
+  constexpr bool MASK = (FLAGS & B_MASK) != 0;
+  constexpr bool SOFTCAP = (FLAGS & B_SOFTCAP) != 0;
+  constexpr bool ALIBI = (FLAGS & B_ALIBI) != 0;
+  constexpr int NC = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TC = kBN * NC;
+
+  __shared__ u32x4 kbuf0[TC], kbuf1[TC], vbuf0[TC], vbuf1[TC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int ln = lane & 31;
+
+  // ---- work item: (query block, head, batch), heaviest first when causal;
+  // contiguous runs of heads per dispatch round go to one XCD (shared K/V)
+  const int id = blockIdx.x;
+  const int round = id / a.nbh;
+  const int u = id - round * a.nbh;
+  const int bh = (a.nbh & 7) == 0 ? ((u & 7) * (a.nbh >> 3) + (u >> 3)) : u;
+  const int qb = a.heavy_first ? (a.nqb - 1 - round) : round;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int kvh = h / a.group;
+  const int m0 = qb * kBM;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * Sk * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + kv_off;
+  const T* V = reinterpret_cast<const T*>(a.v) + kv_off;
+
+  const int lo = a.wl >= 0 ? -a.wl : INT_MIN / 2;
+  const int hi = a.has_hi ? a.dmax : INT_MAX / 2;
+  auto key_lo = [&](int ipa) { return a.wl >= 0 ? max(0, ipa - a.wl) : 0; };
+  auto key_hi = [&](int ipb) { return a.has_hi ? min(Sk, max(0, ipb + a.dmax + 1)) : Sk; };
+  const int wg_last = min(m0 + kBM, Sq) - 1;
+  const int n_lo = key_lo(m0 + off);
+  const int n_hi = key_hi(wg_last + off);
+  const int t_begin = n_lo / kBN;
+  const int t_end = n_hi > n_lo ? (n_hi + kBN - 1) / kBN : t_begin;
+  const int n = t_end - t_begin;
+
+  const int wq0 = m0 + wave * kQW;
+  const bool wave_live = wq0 < Sq;
+  const int wq_last = min(wq0 + kQW, Sq) - 1;
+  const int w_lo = key_lo(wq0 + off);
+  const int w_hi = key_hi(wq_last + off);
+  auto live = [&](int t) { return wave_live && t * kBN < w_hi && (t + 1) * kBN > w_lo; };
+  auto full = [&](int t) {
+    const int n0 = t * kBN;
+    return n0 + kBN <= Sk && wq0 + kQW <= Sq && (n0 + kBN - 1) - (wq0 + off) <= hi &&
+           n0 - (wq0 + kQW - 1 + off) >= lo;
+  };
+
+  const int qi = wq0 + ln;
+  const int ip = qi + off;
+  const T* Qr = reinterpret_cast<const T*>(a.q) + ((size_t)bh * Sq + qi) * D;
+  const T* dOr = reinterpret_cast<const T*>(a.dout) + ((size_t)bh * Sq + qi) * D;
+  u32x4 qf[KS], of[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = qi < Sq ? load16(Qr + 16 * s + 8 * g) : zero_u32x4();
+    of[s] = qi < Sq ? load16(dOr + 16 * s + 8 * g) : zero_u32x4();
+  }
+  const float2 stt = qi < Sq ? a.stats[(size_t)bh * Sq + qi] : float2{__builtin_inff(), 0.f};
+  float slope_l2 = 0.f;
+  if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
+
+  floatx16 dqt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqt[db] = floatx16{};
+
+  const int kv_rows = Sk;
+  auto copy_kv = [&](int t, u32x4* kd, u32x4* vd) {
+    const int n0 = t * kBN;
+    copy_tile<T, D, kBN>(K + (size_t)n0 * D, kv_rows - n0, kd, tid, wave);
+    copy_tile<T, D, kBN>(V + (size_t)n0 * D, kv_rows - n0, vd, tid, wave);
+  };
+
+  auto compute = [&](int t, const u32x4* ks_, const u32x4* vs_) {
+    if (!live(t)) return;
+    const int n0 = t * kBN;
+    // S^T = K Q^T and dP^T = V dO^T: sc[kb] keys 32 kb .. + 31 (rows) x queries (lanes)
+    floatx16 sc[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = floatx16{};
+      dp[kb] = floatx16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int r = 32 * kb + ln;
+        const int c = (2 * s + g) ^ swz<D>(r);
+        sc[kb] = E::mma32(ks_[r * NC + c], qf[s], sc[kb]);
+        dp[kb] = E::mma32(vs_[r * NC + c], of[s], dp[kb]);
+      }
+    }
+    const bool need_mask = MASK && !full(t);
+    uint32_t dsp[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float dv2[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int key = n0 + 32 * kb + 8 * ((r + c) >> 2) + 4 * g + ((r + c) & 3);
+          const int rel = key - ip;
+          float tt;
+          float x = transform<SOFTCAP, ALIBI>(sc[kb][r + c], a, slope_l2, rel, tt);
+          if (need_mask && (qi >= Sq || key >= Sk || rel < lo || rel > hi)) x = kNegInf;
+          const float p = fast_exp2(x - stt.x);
+          float d = p * (dp[kb][r + c] - stt.y);
+          if constexpr (SOFTCAP) d *= 1.f - tt * tt;
+          dv2[c] = d;
+        }
+        dsp[kb * 8 + r / 2] = E::pack2(dv2[0], dv2[1]);
+      }
+    // dQ^T += K^T dS^T over the tile's 64 keys, 16 per step
+    const T* Ks = reinterpret_cast<const T*>(ks_);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 df = {dsp[4 * ks], dsp[4 * ks + 1], dsp[4 * ks + 2], dsp[4 * ks + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqt[db] = E::mma32(tr_operand<T, D>(Ks, ks, db, lane), df, dqt[db]);
+    }
+  };
+
+  if (n > 0) copy_kv(t_begin, kbuf0, vbuf0);
+  wait_vmem();
+  __syncthreads();
+  for (int i = 0; i < n; i += 2) {
+    if (i + 1 < n) copy_kv(t_begin + i + 1, kbuf1, vbuf1);
+    compute(t_begin + i, kbuf0, vbuf0);
+    wait_vmem();
+    __syncthreads();
+    if (i + 1 < n) {
+      if (i + 2 < n) copy_kv(t_begin + i + 2, kbuf0, vbuf0);
+      compute(t_begin + i + 1, kbuf1, vbuf1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  if (qi < Sq) {
+    T* dqr = reinterpret_cast<T*>(a.dq) + ((size_t)bh * Sq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x2 w;
+        w[0] = E::pack2(dqt[db][4 * jj] * a.scale, dqt[db][4 * jj + 1] * a.scale);
+        w[1] = E::pack2(dqt[db][4 * jj + 2] * a.scale, dqt[db][4 * jj + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(dqr + 32 * db + 8 * jj + 4 * g) = w;
+      }
+  }
+}
+
+template <int FLAGS>
+hipError_t launch_pair(const BwdArgs& a, int grid_kv, int grid_q, hipStream_t stream) {
+  if (grid_kv > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_kv), dim3(kThreads), 0,
+                       stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (grid_q > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_q), dim3(kThreads), 0,
+                       stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t ATTN_CAT(launch_bwd_mfma_, ATTN_TAG)(const BwdProblem& p, hipStream_t stream) {
+  BwdArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.dout = p.dout;
+  a.alibi = p.alibi;
+  a.stats = reinterpret_cast<const float2*>(p.stats);
+  a.dq = p.dq;
+  a.dk = p.dk;
+  a.dv = p.dv;
+  a.Sq = p.Sq;
+  a.Sk = p.Sk;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.group = p.Hq / p.Hkv;
+  a.wl = p.wl;
+  a.has_hi = p.causal || p.wr >= 0;
+  a.dmax = p.causal ? (p.wr >= 0 ? min(p.wr, 0) : 0) : p.wr;
+  a.scale = p.scale;
+  const bool softcap = p.softcap > 0.f;
+  a.c_score = softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
+  a.c_cap = kLog2e * p.softcap;
+  a.nbh_kv = p.B * p.Hkv;
+  a.nbh = p.B * p.Hq;
+  a.nqb = (p.Sq + kBM - 1) / kBM;
+  a.heavy_first = p.causal;
+  const int grid_kv = a.nbh_kv * ((p.Sk + kBK - 1) / kBK);
+  const int grid_q = a.nbh * a.nqb;
+  const bool mask = p.causal || p.wl >= 0 || p.wr >= 0 || (p.Sk % kBK) != 0 || (p.Sq % kBM) != 0;
+  const int flags = (mask ? B_MASK : 0) | (softcap ? B_SOFTCAP : 0) | (p.alibi ? B_ALIBI : 0);
+  switch (flags) {
+    case 0: return launch_pair<0>(a, grid_kv, grid_q, stream);
+    case 1: return launch_pair<1>(a, grid_kv, grid_q, stream);
+    case 2: return launch_pair<2>(a, grid_kv, grid_q, stream);
+    case 3: return launch_pair<3>(a, grid_kv, grid_q, stream);
+    case 4: return launch_pair<4>(a, grid_kv, grid_q, stream);
+    case 5: return launch_pair<5>(a, grid_kv, grid_q, stream);
+    case 6: return launch_pair<6>(a, grid_kv, grid_q, stream);
+    default: return launch_pair<7>(a, grid_kv, grid_q, stream);
+  }
+}
+
+}  // namespace attn

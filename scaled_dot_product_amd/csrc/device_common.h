@@ -58,6 +58,8 @@ struct Elem<__bf16> {
                                            c, false);
   }
   static constexpr uint32_t kOnePair = 0x3f803f80u;  // (1.0, 1.0)
+  // the low 16 bits of h as a bf16 value
+  static __device__ __forceinline__ float to_float(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
   static __device__ __forceinline__ float lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
   static __device__ __forceinline__ float hi(uint32_t v) {
     return __builtin_bit_cast(float, v & 0xffff0000u);
@@ -84,6 +86,10 @@ struct Elem<_Float16> {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(x2, a), __builtin_bit_cast(x2, b), c, false);
   }
   static constexpr uint32_t kOnePair = 0x3c003c00u;  // (1.0, 1.0)
+  // the low 16 bits of h as an f16 value
+  static __device__ __forceinline__ float to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+  }
   static __device__ __forceinline__ float lo(uint32_t v) {
     return (float)__builtin_bit_cast(f16x2, v)[0];
   }

@@ -63,8 +63,12 @@ struct FwdArgs {
   const void* k;
   const void* v;
   const float* alibi;
-  void* out;
+  void* out;    // nullptr: the output is not stored
   float* lse;   // per-row log-sum-exp (natural log), or nullptr
+  // backward support: with dout, stats[row] = (lse in log2 units, or +inf for
+  // a row without keys; sum_d dO * O from the float32 accumulator)
+  const void* dout;
+  float* stats;
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
   int heavy_first;
   // paged, variable-length form (F_PAGED): queries packed [total_q, Hq, D]
@@ -522,7 +526,32 @@ void fwd_mfma_kernel(FwdArgs a) {
     const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
     a.lse[(size_t)bh * Sq + qi] = l > 0.f ? (m_use + __log2f(l)) * kLn2 : kNegInf;
   }
-  if (qi < Sq) {
+  if constexpr (!PAGED) {
+    if (a.stats) {
+      // this lane holds d = 32 db + 8 j + 4 g .. + 3 of row qi; the other lane
+      // half holds the rest
+      const T* dorow = reinterpret_cast<const T*>(a.dout) + ((size_t)bh * Sq + min(qi, Sq - 1)) * D;
+      float part = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(dorow + 32 * db + 8 * j + 4 * g);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t hw = (w[c >> 1] >> (16 * (c & 1))) & 0xffffu;
+            part = __builtin_fmaf(st.o[db][4 * j + c], Elem<T>::to_float(hw), part);
+          }
+        }
+      const float delta = halves_sum(part) * inv;
+      if (qi < Sq && g == 0) {
+        const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
+        float2* srow = reinterpret_cast<float2*>(a.stats) + (size_t)bh * Sq + qi;
+        *srow = float2{l > 0.f ? m_use + __log2f(l) : __builtin_inff(), delta};
+      }
+    }
+  }
+  if (qi < Sq && a.out) {
     using E = Elem<T>;
     T* orow = O + (size_t)qi * q_row;
 #pragma unroll
@@ -567,6 +596,8 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
   a.alibi = p.alibi;
   a.out = p.out;
   a.lse = p.lse;
+  a.dout = p.dout;
+  a.stats = p.stats;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
   a.Hq = p.Hq;
@@ -617,6 +648,8 @@ hipError_t ATTN_CAT(launch_paged_prefill_, ATTN_TAG)(const PagedPrefillProblem& 
   a.alibi = p.alibi;
   a.out = p.out;
   a.lse = nullptr;
+  a.dout = nullptr;
+  a.stats = nullptr;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.group = p.Hq / p.Hkv;

@@ -15,6 +15,10 @@ struct FwdProblem {
   const float* alibi;  // [Hq] float32 or nullptr
   void* out;
   float* lse;     // [B, Hq, Sq] float32 natural-log LSE of each row, or nullptr
+  // backward support (matrix-core path): with dout [B, Hq, Sq, D], stats
+  // [B, Hq, Sq] of float pairs (log2-unit LSE, +inf without keys; dO . O)
+  const void* dout = nullptr;
+  float* stats = nullptr;
   int B, Hq, Hkv, Sq, Sk, D;
   int causal;
   int wl, wr;     // window; -1 = unbounded (already clamped to the useful range)
@@ -59,10 +63,30 @@ struct DecodeProblem {
   float softcap;
 };
 
+// Backward (matrix-core path): dQ, dK, dV from Q, K, V, dO and the forward's
+// per-row statistics.
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;     // [B, Hq, Sq, D]
+  const float* alibi;   // [Hq] float32 or nullptr
+  const float* stats;   // [B, Hq, Sq] float pairs written by the forward (FwdProblem::stats)
+  void* dq;             // [B, Hq, Sq, D]
+  void* dk;             // [B, Hkv, Sk, D]
+  void* dv;
+  int B, Hq, Hkv, Sq, Sk, D;
+  int causal;
+  int wl, wr;
+  float scale;
+  float softcap;
+};
+
 // 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
 hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream);
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
+hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream);
 
 }  // namespace attn

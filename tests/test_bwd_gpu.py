@@ -1,0 +1,146 @@
+"""Parity of attn_bwd (HIP, through the C ABI) with the float64 oracle's
+backward (kernel-contract page, attention_flash_backward).
+
+Small cases span several 32/64/128-row tiles with ragged tails, rows without
+keys, every mask kind, softcap and ALiBi, GQA; the full-size causal workload
+is checked on sampled heads.  Inputs are rounded to the dtype first and the
+oracle sees the rounded values.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+DEV = torch.device("cuda:0")
+
+# Bar for the gradients (the pages fix none): every gradient element is a sum
+# of products one of whose factors -- P or dS -- enters the matrix cores
+# rounded to the input dtype (unit roundoff u = 2^-8 for bf16, 2^-11 for f16),
+# and the result is rounded once more to the dtype.  The tensor relative L2
+# error is therefore a small multiple of u; 3u leaves room for the accumulated
+# roundings.  Element-wise, cancellation in dS = P (dP - rowsum(P dP)) can make
+# a small element's relative error large, so the element bar is taken relative
+# to the largest element of the tensor: 6u of it.
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def compare_grad(got, ref, dtype, what):
+    g = got.detach().to("cpu", torch.float64).numpy()
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    err = np.abs(g - ref)
+    scale = np.abs(ref).max(initial=0.0)
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(g - ref) / nref if nref > 0 else np.linalg.norm(g)
+    announce(f"{what}: rel L2 {rel:.3g}, max err {err.max(initial=0):.3g} of max |ref| {scale:.3g}")
+    assert rel <= 3 * U[dtype], f"{what}: relative L2 {rel:.3g} > {3 * U[dtype]:.3g}"
+    assert err.max(initial=0.0) <= 6 * U[dtype] * scale + 1e-6, \
+        f"{what}: max err {err.max():.3g} > {6 * U[dtype]:.3g} * {scale:.3g}"
+
+
+def run_bwd(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None, softcap=None,
+            alibi=False, amp=1.0, seed=0):
+    name = (f"attn_bwd {dtype} B{B} H{Hq}/{Hkv} Sq{Sq} Sk{Sk} D{D} causal={causal} "
+            f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
+    q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
+    do = W.random_dense(dtype, B, Hq, Hkv, Sq, 1, D, seed + 7919, 1.0)[0]
+    sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    announce(name)
+    dq, dk, dv = sdpa.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV),
+                               None if sl is None else sl.to(DEV), softmax_scale=scale,
+                               causal=causal, window_left=wl, window_right=wr, softcap=softcap)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do),
+                                   scale=scale, causal=causal, window_left=wl, window_right=wr,
+                                   softcap=softcap, alibi=None if sl is None else W.to_f64(sl))
+    for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        compare_grad(got, r, dtype, f"{name} {nm}")
+    return (q, k, v, do, sl, scale), (dq, dk, dv)
+
+
+CASES = [
+    # (B, Hq, Hkv, Sq, Sk, kwargs)
+    (1, 2, 2, 128, 128, dict()),                                   # aligned: no mask code
+    (1, 4, 2, 200, 333, dict(causal=True)),
+    (2, 4, 1, 300, 250, dict(causal=True)),                        # Sq > Sk: rows 0..49 empty
+    (1, 2, 2, 190, 190, dict(softcap=5.0, amp=2.0)),
+    (1, 4, 4, 257, 300, dict(causal=True, wl=64, wr=0, alibi=True)),
+    (1, 8, 2, 130, 400, dict(wl=30, wr=20, softcap=20.0, alibi=True, amp=1.5)),
+    (1, 2, 1, 64, 1000, dict()),
+    (1, 2, 2, 700, 64, dict(causal=True)),
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_bwd_parity(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = CASES[case]
+    run_bwd(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=700 + case, **kw)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("case", [1, 4, 5])
+def test_bwd_parity_other_dims(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = CASES[case]
+    run_bwd(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=800 + case, **kw)
+
+
+def test_bwd_deterministic(gpu_lib):
+    (q, k, v, do, sl, scale), first = run_bwd(gpu_lib, "bf16", 1, 4, 2, 200, 333, 128,
+                                              causal=True, seed=900)
+    again = gpu_lib.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), None,
+                             softmax_scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)
+
+
+def test_bwd_no_queries_or_keys(gpu_lib):
+    """Sq = 0: dk = dv = 0.  Sk = 0: dq = 0."""
+    q, k, v = W.random_dense("bf16", 1, 2, 2, 0, 70, 64, 3, 1.0)
+    do = torch.empty_like(q)
+    announce("attn_bwd Sq=0")
+    dk0 = torch.full_like(k, 7.0).to(DEV)
+    dv0 = torch.full_like(v, 7.0).to(DEV)
+    _, dk, dv = gpu_lib.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), None,
+                                 dk=dk0, dv=dv0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
+    q, k, v = W.random_dense("bf16", 1, 2, 2, 90, 0, 64, 4, 1.0)
+    do = torch.ones_like(q)
+    announce("attn_bwd Sk=0")
+    dq0 = torch.full_like(q, 7.0).to(DEV)
+    dq, _, _ = gpu_lib.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), None, dq=dq0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq).item() == 0
+
+
+def test_bwd_gqa_causal_2k_workload(gpu_lib):
+    """The 2048-token causal GQA workload (2 x 32 query heads over 8 KV heads,
+    D = 128): dQ of two query heads and dK/dV of one KV head (its whole group
+    of 4 query heads) against the oracle."""
+    w = W.GQA_CAUSAL_2K
+    q, k, v, _ = W.dense_inputs(w)
+    do = W.random_dense(w.dtype, w.B, w.Hq, w.Hkv, w.Sq, 1, w.D, 4242, 1.0)[0]
+    announce(f"attn_bwd {w.name}")
+    dq, dk, dv = gpu_lib.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), None,
+                                  softmax_scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, g in ((1, 5),):
+        hs = slice(g * G, (g + 1) * G)
+        ref = oracle.sdpa_backward_f64(W.to_f64(q[b:b + 1, hs]), W.to_f64(k[b:b + 1, g:g + 1]),
+                                       W.to_f64(v[b:b + 1, g:g + 1]), W.to_f64(do[b:b + 1, hs]),
+                                       scale=w.scale, causal=True)
+        compare_grad(dq[b:b + 1, hs], ref[0], w.dtype, f"{w.name} dq b{b} heads {hs}")
+        compare_grad(dk[b:b + 1, g:g + 1], ref[1], w.dtype, f"{w.name} dk b{b} kv {g}")
+        compare_grad(dv[b:b + 1, g:g + 1], ref[2], w.dtype, f"{w.name} dv b{b} kv {g}")
