@@ -159,6 +159,47 @@ def extra_prefill(torch, sdpa, W, dev, stream, launches=10):
     return out
 
 
+def backward_flops(w) -> int:
+    """Algorithmic work of the backward: the five matmuls per admissible
+    (query, key) pair (S = Q K^T, dP = dO V^T, dV, dQ, dK), 2 D FLOP each."""
+    return 10 * w.D * w.B * w.Hq * admissible_pairs(w.Sq, w.Sk, w.causal, w.window_left,
+                                                    w.window_right)
+
+
+def extra_backward(torch, sdpa, W, dev, stream, launches=10):
+    """attn_bwd on the 2048-token causal GQA workload (the forward's row
+    statistics, dK/dV and dQ), timed on its own after the timed steps."""
+    w = W.GQA_CAUSAL_2K
+    q, k, v, _ = W.dense_inputs(w)
+    do = W.random_dense(w.dtype, w.B, w.Hq, w.Hkv, w.Sq, 1, w.D, 4242, 1.0)[0]
+    t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev), do=do.to(dev))
+    t["dq"], t["dk"], t["dv"] = (torch.empty_like(t["q"]), torch.empty_like(t["k"]),
+                                 torch.empty_like(t["v"]))
+    p = sdpa.attn_fwd_params(tuple(q.shape), tuple(k.shape), q.dtype, softmax_scale=w.scale,
+                             causal=True)
+    ws = torch.empty(sdpa.attn_bwd_workspace_size(p), dtype=torch.uint8, device=dev)
+
+    def run():
+        sdpa.attn_bwd(t["q"], t["k"], t["v"], t["do"], None, softmax_scale=w.scale, causal=True,
+                      dq=t["dq"], dk=t["dk"], dv=t["dv"], workspace=ws, stream=stream)
+    for _ in range(3):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(launches):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / launches
+    tf = backward_flops(w) / sec / 1e12
+    return {w.name: {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype,
+                     "work_per_launch": backward_flops(w), "ms_per_launch": sec * 1e3,
+                     "launches": launches,
+                     "kernels": "forward statistics + bwd_dkdv_kernel + bwd_dq_kernel"}}
+
+
 def run_prefill(sdpa, wp, pre, stream):
     sdpa.attn_fwd(pre["q"], pre["k"], pre["v"], None, pre["out"], softmax_scale=wp.scale,
                   causal=wp.causal, stream=stream)
@@ -265,6 +306,7 @@ def bench(args):
     }
     if not args.no_extra:
         result["other_prefill"] = extra_prefill(torch, sdpa, W, dev, stream)
+        result["backward"] = extra_backward(torch, sdpa, W, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -296,6 +338,25 @@ def profile(args):
     print(json.dumps({"profile_launches": args.launches, "prefill_flops": prefill_flops(wp),
                       "decode_bytes": decode_bytes(wd, lens), "copy_bytes_each_way": src.numel() * 4,
                       "sources_sha256_16": sources_digest()}), flush=True)
+
+
+def profile_backward(args):
+    """Fixed launches of attn_bwd on the 2048-token causal GQA workload for
+    rocprofv3 (its three kernels: the forward's row statistics, dK/dV, dQ)."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = W.GQA_CAUSAL_2K
+    q, k, v, _ = W.dense_inputs(w)
+    do = W.random_dense(w.dtype, w.B, w.Hq, w.Hkv, w.Sq, 1, w.D, 4242, 1.0)[0]
+    q, k, v, do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    for _ in range(2 + args.launches):
+        sdpa.attn_bwd(q, k, v, do, None, softmax_scale=w.scale, causal=True, stream=stream)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_launches": args.launches, "backward_flops": backward_flops(w)}),
+          flush=True)
 
 
 def summarize(path):
@@ -375,11 +436,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "profile", "profile_backward"], default="bench")
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip timing the long masked and chunked prefill workloads")
+                    help="skip timing the other prefill workloads and the backward")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -393,6 +454,8 @@ def main():
                  "kernels here are single-GPU, and multi-GPU sharding is not part of this build")
     if args.mode == "profile":
         return profile(args)
+    if args.mode == "profile_backward":
+        return profile_backward(args)
     return bench(args)
 
 

@@ -225,11 +225,33 @@ attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, const fl
   return launch_fwd(q, k, v, alibi, out, lse, p, stream);
 }
 
+// Backward workspace: the forward's row statistics (8 bytes a row), then, at
+// a 256-byte boundary, the float32 dK/dV partials of the key blocks split
+// into several chunks.
+struct BwdLayout {
+  int wl, wr;               // windows clamped to the useful range
+  int chunk_items, max_chunks;
+  int64_t stats_bytes, part_offset, part_bytes, total;
+};
+static BwdLayout bwd_layout(const attn_fwd_params_t* p) {
+  BwdLayout L;
+  L.wl = (p->window_left < 0 || p->window_left >= p->Sk) ? -1 : (int)p->window_left;
+  L.wr = (p->window_right < 0 || p->window_right >= p->Sq) ? -1 : (int)p->window_right;
+  attn::bwd_chunking((int)p->B, (int)p->Hkv, (int)p->Hq, (int)p->Sq, (int)p->Sk, p->causal != 0,
+                     L.wl, L.wr, &L.chunk_items, &L.max_chunks);
+  L.stats_bytes = p->B * p->Hq * p->Sq * 8;
+  L.part_offset = (L.stats_bytes + 255) / 256 * 256;
+  const int64_t nkb = (p->Sk + 127) / 128;
+  L.part_bytes = L.max_chunks > 1 ? p->B * p->Hkv * nkb * L.max_chunks * 2 * 128 * p->D * 4 : 0;
+  L.total = L.part_bytes > 0 ? L.part_offset + L.part_bytes : L.stats_bytes;
+  return L;
+}
+
 size_t attn_bwd_workspace_size(const attn_fwd_params_t* p) {
   if (!p || !valid_dtype(p->dtype)) return 0;
   int64_t qb, kvb;
   if (fwd_shape(p, &qb, &kvb) != ATTN_OK) return 0;
-  return (size_t)(p->B * p->Hq * p->Sq * 8);
+  return (size_t)bwd_layout(p).total;
 }
 
 attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const void* dout,
@@ -246,7 +268,7 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
   fwd_shape(p, &qb, &kvb);
   if (qb > 0 && !dout) return ATTN_ERR_NULL;
   if (kvb > 0 && (!dk || !dv)) return ATTN_ERR_NULL;
-  const int64_t ws_need = p->B * p->Hq * p->Sq * 8;
+  const int64_t ws_need = bwd_layout(p).total;
   if (ws_need > 0 && (!workspace || workspace_bytes < (size_t)ws_need)) return ATTN_ERR_WORKSPACE;
   const void* ptrs[] = {dout, dk, dv, workspace};
   for (const void* ptr : ptrs)
@@ -270,8 +292,8 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   if (st != ATTN_OK) return st;
   if (p->B == 0 || p->Hkv == 0) return ATTN_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int wl = (p->window_left < 0 || p->window_left >= p->Sk) ? -1 : (int)p->window_left;
-  const int wr = (p->window_right < 0 || p->window_right >= p->Sq) ? -1 : (int)p->window_right;
+  const BwdLayout lay = bwd_layout(p);
+  const int wl = lay.wl, wr = lay.wr;
   // 1. the forward's row statistics (LSE, dO . O) into the workspace
   if (p->Hq > 0 && p->Sq > 0) {
     attn::FwdProblem fp;
@@ -318,6 +340,11 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   bp.wr = wr;
   bp.scale = p->softmax_scale;
   bp.softcap = p->softcap;
+  bp.chunk_items = lay.chunk_items;
+  bp.max_chunks = lay.max_chunks;
+  bp.partials = lay.part_bytes > 0
+                    ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.part_offset)
+                    : nullptr;
   return attn::launch_bwd_mfma(bp, p->dtype, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -72,6 +72,10 @@ struct BwdArgs {
   int nbh;       // B * Hq
   int nqb;       // dQ: 128-row query blocks per head
   int heavy_first;
+  int nkb;       // 128-key blocks per KV head
+  int chunk;     // dK/dV items per workgroup (see BwdProblem)
+  int nchunk;    // chunk slots per key block
+  float* part;   // [nbh_kv][nkb][nchunk][2][128][D] float32 partial dK, dV
 };
 
 // XOR swizzle of the 16-byte chunk index of tile row r: the matrix-operand
@@ -158,11 +162,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int g = lane >> 5;
   const int ln = lane & 31;
 
-  // ---- work item: key block kblk of (b, kvh); low key blocks see the most
-  // queries under a causal mask, so they go first
+  // ---- work item: chunk ch of key block kblk of (b, kvh); low key blocks
+  // see the most queries under a causal mask, so they go first
   const int id = blockIdx.x;
-  const int kblk = id / a.nbh_kv;
-  const int bkv = id - kblk * a.nbh_kv;
+  const int kc = id / a.nbh_kv;
+  const int bkv = id - kc * a.nbh_kv;
+  const int kblk = kc / a.nchunk;
+  const int ch = kc - kblk * a.nchunk;
   const int b = bkv / a.Hkv;
   const int kvh = bkv - b * a.Hkv;
   const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
@@ -190,7 +196,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int q_hi = a.wl >= 0 ? min(Sq, k_last - lo - off + 1) : Sq;  // one past
   const int t_lo = q_lo / kBQ;
   const int nt = q_hi > q_lo && k_last >= k0 ? (q_hi + kBQ - 1) / kBQ - t_lo : 0;
-  const int n_items = nt * a.group;
+  const int n_all = nt * a.group;
+  const int n_ch = n_all > 0 ? (n_all + a.chunk - 1) / a.chunk : 1;  // chunks of this block
+  if (ch >= n_ch) return;  // the whole workgroup: an unused chunk slot
+  const int it0 = ch * a.chunk;
+  const int n_items = min(n_all, it0 + a.chunk) - it0;
 
   // per wave: keys [j0, jw_last]
   const int jw_last = min(j0 + kKW, Sk) - 1;
@@ -212,8 +222,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dvt[db] = floatx16{};
   }
 
-  auto item_head = [&](int it) { return kvh * a.group + it / nt; };
-  auto item_q0 = [&](int it) { return (t_lo + it % nt) * kBQ; };
+  // item it of this chunk: flattened index it0 + it over (head, tile)
+  auto item_head = [&](int it) { return kvh * a.group + (it0 + it) / nt; };
+  auto item_q0 = [&](int it) { return (t_lo + (it0 + it) % nt) * kBQ; };
   auto copy_item = [&](int it, u32x4* qd, u32x4* od, float2* sd) {
     const int h = item_head(it), q0 = item_q0(it);
     const size_t row0 = (size_t)(b * a.Hq + h) * Sq + q0;
@@ -299,6 +310,23 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  // ---- a block of several chunks: this chunk's float32 partials (summed by
+  // bwd_reduce_kernel); d = 32 db + 8 jj + 4 g .. + 3 of this lane's key
+  if (n_ch > 1) {
+    float* pk = a.part + ((((size_t)bkv * a.nkb + kblk) * a.nchunk + ch) * 2) * kBK * D +
+                (size_t)(j - k0) * D;
+    float* pv = pk + (size_t)kBK * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        *reinterpret_cast<floatx4*>(pk + 32 * db + 8 * jj + 4 * g) =
+            floatx4{dkt[db][4 * jj], dkt[db][4 * jj + 1], dkt[db][4 * jj + 2], dkt[db][4 * jj + 3]};
+        *reinterpret_cast<floatx4*>(pv + 32 * db + 8 * jj + 4 * g) =
+            floatx4{dvt[db][4 * jj], dvt[db][4 * jj + 1], dvt[db][4 * jj + 2], dvt[db][4 * jj + 3]};
+      }
+    return;
+  }
   // ---- store: this lane's key row; d = 32 db + 8 jj + 4 g .. + 3
   if (j < Sk) {
     T* dkr = reinterpret_cast<T*>(a.dk) + kv_off + (size_t)j * D;
@@ -318,10 +346,52 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// Sum of the chunks' partials of every multi-chunk key block, in chunk
+// order: one thread per 4 d of one key row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+  using E = Elem<T>;
+  constexpr int TPR = D / 4;              // threads per key row
+  constexpr int RPW = 256 / TPR;          // key rows per workgroup
+  const int blk = blockIdx.x / (kBK / RPW);  // (bkv, key block)
+  const int r = (blockIdx.x % (kBK / RPW)) * RPW + threadIdx.x / TPR;
+  const int d4 = (threadIdx.x % TPR) * 4;
+  const int bkv = blk / a.nkb, kblk = blk - bkv * a.nkb;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const int k0 = kblk * kBK;
+  const int j = k0 + r;
+  if (j >= Sk) return;
+  // chunks of this block, as the dK/dV kernel counts them
+  const int lo = a.wl >= 0 ? -a.wl : INT_MIN / 2;
+  const int hi = a.has_hi ? a.dmax : INT_MAX / 2;
+  const int k_last = min(k0 + kBK, Sk) - 1;
+  const int q_lo = a.has_hi ? max(0, k0 - hi - off) : 0;
+  const int q_hi = a.wl >= 0 ? min(Sq, k_last - lo - off + 1) : Sq;
+  const int nt = q_hi > q_lo ? (q_hi + kBQ - 1) / kBQ - q_lo / kBQ : 0;
+  const int n_all = nt * a.group;
+  const int n_ch = n_all > 0 ? (n_all + a.chunk - 1) / a.chunk : 1;
+  if (n_ch < 2) return;
+  const float* base = a.part + (((size_t)bkv * a.nkb + kblk) * a.nchunk) * 2 * kBK * D +
+                      (size_t)r * D + d4;
+  floatx4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < n_ch; ++c) {
+    const floatx4 xk = *reinterpret_cast<const floatx4*>(base + (size_t)c * 2 * kBK * D);
+    const floatx4 xv = *reinterpret_cast<const floatx4*>(base + (size_t)c * 2 * kBK * D + kBK * D);
+    sk += xk;
+    sv += xv;
+  }
+  const int b = bkv / a.Hkv, kvh = bkv - b * a.Hkv;
+  const size_t row = ((size_t)(b * a.Hkv + kvh) * Sk + j) * D + d4;
+  const u32x2 wk = {E::pack2(sk[0] * a.scale, sk[1] * a.scale), E::pack2(sk[2] * a.scale, sk[3] * a.scale)};
+  const u32x2 wv = {E::pack2(sv[0], sv[1]), E::pack2(sv[2], sv[3])};
+  *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.dk) + row) = wk;
+  *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.dv) + row) = wv;
+}
+
 // ---------------------------------------------------------------- dQ
 
 template <typename T, int D, int FLAGS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   constexpr bool MASK = (FLAGS & B_MASK) != 0;
@@ -490,6 +560,13 @@ hipError_t launch_pair(const BwdArgs& a, int grid_kv, int grid_q, hipStream_t st
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (grid_kv > 0 && a.nchunk > 1) {
+    constexpr int RPW = 256 / (ATTN_D / 4);
+    hipLaunchKernelGGL((bwd_reduce_kernel<ATTN_ELEM, ATTN_D>), dim3(a.nbh_kv * a.nkb * (kBK / RPW)),
+                       dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (grid_q > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_q), dim3(kThreads), 0,
                        stream, a);
@@ -525,7 +602,11 @@ hipError_t ATTN_CAT(launch_bwd_mfma_, ATTN_TAG)(const BwdProblem& p, hipStream_t
   a.nbh = p.B * p.Hq;
   a.nqb = (p.Sq + kBM - 1) / kBM;
   a.heavy_first = p.causal;
-  const int grid_kv = a.nbh_kv * ((p.Sk + kBK - 1) / kBK);
+  a.nkb = (p.Sk + kBK - 1) / kBK;
+  a.chunk = p.chunk_items;
+  a.nchunk = p.max_chunks;
+  a.part = p.partials;
+  const int grid_kv = a.nbh_kv * a.nkb * a.nchunk;
   const int grid_q = a.nbh * a.nqb;
   const bool mask = p.causal || p.wl >= 0 || p.wr >= 0 || (p.Sk % kBK) != 0 || (p.Sq % kBM) != 0;
   const int flags = (mask ? B_MASK : 0) | (softcap ? B_SOFTCAP : 0) | (p.alibi ? B_ALIBI : 0);

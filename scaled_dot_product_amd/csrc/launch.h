@@ -80,7 +80,53 @@ struct BwdProblem {
   int wl, wr;
   float scale;
   float softcap;
+  // dK/dV work split: a 128-key block's (head, 32-query tile) items are cut
+  // into chunks of chunk_items; a block of more than one chunk sums float32
+  // partials (`partials`, max_chunks slots per block) in a second pass
+  int chunk_items, max_chunks;
+  float* partials;
 };
+
+// Items (query heads x 32-query tiles) that see key block kb of 128 keys.
+inline int bwd_kv_items(int kb, int Sq, int Sk, int group, int causal, int wl, int wr) {
+  const bool has_hi = causal || wr >= 0;
+  const int dmax = causal ? 0 : wr;  // causal: j <= i' (a right window cannot widen it)
+  const int off = Sk - Sq;
+  const int k0 = kb * 128;
+  const int k_last = (k0 + 128 < Sk ? k0 + 128 : Sk) - 1;
+  if (k_last < k0) return 0;
+  int q_lo = has_hi ? k0 - dmax - off : 0;
+  if (q_lo < 0) q_lo = 0;
+  int q_hi = wl >= 0 ? k_last + wl - off + 1 : Sq;
+  if (q_hi > Sq) q_hi = Sq;
+  if (q_hi <= q_lo) return 0;
+  const int nt = (q_hi + 31) / 32 - q_lo / 32;
+  return nt * group;
+}
+
+// Chunk size: about 1/512 of all dK/dV items (at least 16): about half a
+// compute unit's share on a 256-CU chip, so that the workgroups pack evenly
+// onto the chip even though the causal key blocks differ in work by up to
+// Sq / 32 tiles (chunks of 1/256 packed worse, 1/1024 doubled the partials for
+// 2 % more); and the most chunks any key block needs.
+constexpr long long kBwdChunkDiv = 512;
+inline void bwd_chunking(int B, int Hkv, int Hq, int Sq, int Sk, int causal, int wl, int wr,
+                         int* chunk_items, int* max_chunks) {
+  const int group = Hkv > 0 ? Hq / Hkv : 0;
+  const int nkb = (Sk + 127) / 128;
+  long long total = 0;
+  int most = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int n = bwd_kv_items(kb, Sq, Sk, group, causal, wl, wr);
+    total += n;
+    most = n > most ? n : most;
+  }
+  total *= (long long)B * Hkv;
+  long long L = (total + kBwdChunkDiv - 1) / kBwdChunkDiv;
+  if (L < 16) L = 16;
+  *chunk_items = (int)L;
+  *max_chunks = most > 0 ? (int)((most + L - 1) / L) : 1;
+}
 
 // 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
 hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream);

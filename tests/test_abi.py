@@ -260,3 +260,55 @@ def test_paged_prefill_check():
     lib = sdpa.library()
     p = varlen(D=80)
     assert lib.attn_paged_prefill(Q, KP, VP, TAB, LEN, CU, None, OUT, None, ctypes.byref(p), None) == HEAD_DIM
+
+
+# ------------------------------------------------------------------ backward
+
+DQ, DK, DV, DO, BWS = (0x100000000 * (i + 20) for i in range(5))
+
+
+def check_bwd(p, q=Q, k=K, v=V, do=DO, al=None, dq=DQ, dk=DK, dv=DV, ws=BWS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = sdpa.attn_bwd_workspace_size(p)
+    return sdpa.attn_bwd_check(q, k, v, do, al, dq, dk, dv, ws, ws_bytes, p)
+
+
+def test_bwd_check_accepts_valid_calls():
+    assert check_bwd(fwd()) == OK
+    assert check_bwd(fwd(D=64, dtype=sdpa.ATTN_F16, causal=0, window_left=5, window_right=0,
+                         softcap=30.0), al=AL) == OK
+    assert check_bwd(fwd(Sq=0), q=None, do=None, dq=None, ws=None, ws_bytes=0) == OK
+
+
+def test_bwd_workspace_size():
+    p = fwd(B=2, Hq=8, Hkv=2, Sq=100, Sk=130)
+    # the forward's row statistics: 8 bytes per query row, at least
+    assert sdpa.attn_bwd_workspace_size(p) >= 2 * 8 * 100 * 8
+    assert sdpa.attn_bwd_workspace_size(fwd(D=80)) == 0
+    assert sdpa.attn_bwd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=sdpa.ATTN_F32), UNSUPPORTED), (dict(dtype=sdpa.ATTN_F64), UNSUPPORTED),
+    (dict(dtype=9), DTYPE), (dict(D=256), HEAD_DIM), (dict(Hkv=3), GQA),
+    (dict(softcap=-1.0), PARAM),
+])
+def test_bwd_check_rejects(kw, code):
+    assert check_bwd(fwd(**kw)) == code
+
+
+def test_bwd_check_pointers_and_aliasing():
+    p = fwd()
+    need = sdpa.attn_bwd_workspace_size(p)
+    assert check_bwd(p, do=None) == NULL
+    assert check_bwd(p, dk=None) == NULL
+    assert check_bwd(p, dq=None) == NULL
+    assert check_bwd(p, ws=None) == WORKSPACE
+    assert check_bwd(p, ws_bytes=need - 1) == WORKSPACE
+    assert check_bwd(p, do=DO + 8) == ALIGN
+    assert check_bwd(p, ws=BWS + 4) == ALIGN
+    assert check_bwd(p, dq=Q + 256) == ALIAS        # an output over an input
+    assert check_bwd(p, dk=DO) == ALIAS
+    assert check_bwd(p, dv=DK + 64) == ALIAS        # two outputs overlapping
+    assert check_bwd(p, ws=DQ + 16) == ALIAS        # workspace over an output
+    assert sdpa.attn_bwd_check(Q, K, V, DO, None, DQ, DK, DV, BWS, need, None) == NULL
