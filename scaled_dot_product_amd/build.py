@@ -37,8 +37,8 @@ UNITS = [("attn_api.cpp", [], "attn_api.o"),
          ("fwd_f32.hip", KERNEL_FLAGS, "fwd_f32.o"),
          ("decode.hip", KERNEL_FLAGS, "decode.o")]
 for _elem, _tag in (("__bf16", "bf16"), ("_Float16", "f16")):
-    for _d in (128, 64):
-        for _src in ("fwd_mfma", "bwd_mfma"):
+    for _d in (128, 64, 256):
+        for _src in ("fwd_mfma", "bwd_mfma") if _d <= 128 else ("fwd_mfma",):
             UNITS.append((f"{_src}.hip",
                           KERNEL_FLAGS + [f"-DATTN_ELEM={_elem}", f"-DATTN_D={_d}",
                                           f"-DATTN_TAG={_tag}_d{_d}"],

@@ -18,11 +18,15 @@ hipError_t launch_fwd_mfma_bf16_d128(const FwdProblem& p, hipStream_t stream);
 hipError_t launch_fwd_mfma_bf16_d64(const FwdProblem& p, hipStream_t stream);
 hipError_t launch_fwd_mfma_f16_d128(const FwdProblem& p, hipStream_t stream);
 hipError_t launch_fwd_mfma_f16_d64(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_mfma_bf16_d256(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_mfma_f16_d256(const FwdProblem& p, hipStream_t stream);
 
 hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream) {
   if (dtype == ATTN_BF16)
-    return p.D == 128 ? launch_fwd_mfma_bf16_d128(p, stream) : launch_fwd_mfma_bf16_d64(p, stream);
-  return p.D == 128 ? launch_fwd_mfma_f16_d128(p, stream) : launch_fwd_mfma_f16_d64(p, stream);
+    return p.D == 256 ? launch_fwd_mfma_bf16_d256(p, stream)
+         : p.D == 128 ? launch_fwd_mfma_bf16_d128(p, stream) : launch_fwd_mfma_bf16_d64(p, stream);
+  return p.D == 256 ? launch_fwd_mfma_f16_d256(p, stream)
+       : p.D == 128 ? launch_fwd_mfma_f16_d128(p, stream) : launch_fwd_mfma_f16_d64(p, stream);
 }
 
 hipError_t launch_bwd_mfma_bf16_d128(const BwdProblem& p, hipStream_t stream);
@@ -40,12 +44,15 @@ hipError_t launch_paged_prefill_bf16_d128(const PagedPrefillProblem& p, hipStrea
 hipError_t launch_paged_prefill_bf16_d64(const PagedPrefillProblem& p, hipStream_t stream);
 hipError_t launch_paged_prefill_f16_d128(const PagedPrefillProblem& p, hipStream_t stream);
 hipError_t launch_paged_prefill_f16_d64(const PagedPrefillProblem& p, hipStream_t stream);
+hipError_t launch_paged_prefill_bf16_d256(const PagedPrefillProblem& p, hipStream_t stream);
+hipError_t launch_paged_prefill_f16_d256(const PagedPrefillProblem& p, hipStream_t stream);
 
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream) {
   if (dtype == ATTN_BF16)
-    return p.D == 128 ? launch_paged_prefill_bf16_d128(p, stream)
-                      : launch_paged_prefill_bf16_d64(p, stream);
-  return p.D == 128 ? launch_paged_prefill_f16_d128(p, stream) : launch_paged_prefill_f16_d64(p, stream);
+    return p.D == 256 ? launch_paged_prefill_bf16_d256(p, stream)
+         : p.D == 128 ? launch_paged_prefill_bf16_d128(p, stream) : launch_paged_prefill_bf16_d64(p, stream);
+  return p.D == 256 ? launch_paged_prefill_f16_d256(p, stream)
+       : p.D == 128 ? launch_paged_prefill_f16_d128(p, stream) : launch_paged_prefill_f16_d64(p, stream);
 }
 }  // namespace attn
 
@@ -56,11 +63,11 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
 bool valid_dtype(int32_t d) { return d == ATTN_F32 || d == ATTN_F16 || d == ATTN_BF16 || d == ATTN_F64; }
 int64_t elem_bytes(int32_t d) { return d == ATTN_F64 ? 8 : (d == ATTN_F32 ? 4 : 2); }
-// Dense forward head dims: the matrix-core path (F16, BF16) takes 64 and 128,
-// the vector-ALU path (F32, F64) 32, 64, 128 and 256.
+// Dense forward head dims: the matrix-core path (F16, BF16) takes 64, 128 and
+// 256, the vector-ALU path (F32, F64) 32, 64, 128 and 256.
 bool fwd_head_dim_ok(int32_t dtype, int64_t D) {
   if (dtype == ATTN_F32 || dtype == ATTN_F64) return D == 32 || D == 64 || D == 128 || D == 256;
-  return D == 64 || D == 128;
+  return D == 64 || D == 128 || D == 256;
 }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -264,6 +271,7 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
   // q, k, v, alibi and the parameters as for the forward, with dq in out's place
   attn_status_t st = check_fwd(q, k, v, alibi, dq, p);
   if (st != ATTN_OK) return st;
+  if (p->D > 128) return ATTN_ERR_HEAD_DIM;  // the backward is built for 64 and 128
   int64_t qb, kvb;
   fwd_shape(p, &qb, &kvb);
   if (qb > 0 && !dout) return ATTN_ERR_NULL;
@@ -438,7 +446,7 @@ attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const 
       p->num_blocks < 0 || p->max_blocks_per_seq < 0 || p->block_size < 1)
     return ATTN_ERR_SHAPE;
   if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
-  if (p->D != 64 && p->D != 128) return ATTN_ERR_HEAD_DIM;
+  if (p->D != 64 && p->D != 128 && p->D != 256) return ATTN_ERR_HEAD_DIM;
   if (p->block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
   if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_PARAM;

@@ -6,7 +6,10 @@
 // math up", section 3) and its causal tile early exit (section 4).
 //
 // Compiled once per (element type, head dim): ATTN_ELEM is __bf16 or _Float16,
-// ATTN_D is 64 or 128, ATTN_TAG names the exported launcher.
+// ATTN_D is 64, 128 or 256, ATTN_TAG names the exported launcher.  At head dim
+// 256 the Q fragments and the O accumulator alone take 192 VGPRs: one wave
+// per SIMD, one workgroup per compute unit (128 KiB of K/V tiles), and no key
+// split (it would need twice the tiles).
 //
 // Mapping onto CDNA4 (designed for gfx950, not taken from the gfx942 design):
 //   * A workgroup of 4 waves owns 128 query rows of one (batch, head); each
@@ -90,11 +93,12 @@ struct FwdArgs {
 // 2-4 chunks per 16/32 lanes) hit distinct LDS banks.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
+// (the same for rows r and r + 8, which the transpose read of one step pairs)
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+  return D == 256 ? ((r & 7) << 2) : (D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2));
 }
 
 // Key offset (within a 64-key tile, without the lane-half term 4*g) of
@@ -246,7 +250,7 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
 // LDS buffers, and group 1 hands its (o, m, l) to group 0 at the end.
 template <typename T, int D, int FLAGS>
 __global__ __launch_bounds__((FLAGS & F_SPLIT) ? 2 * kThreads : kThreads)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void fwd_mfma_kernel(FwdArgs a) {
   constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
   constexpr bool PAGED = (FLAGS & F_PAGED) != 0;
@@ -573,6 +577,15 @@ hipError_t launch_flags(const FwdArgs& a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The key split needs two sets of tiles: at head dim 256 they do not fit.
+constexpr bool kCanSplit = ATTN_D <= 128;
+
+template <int FLAGS>
+hipError_t launch_split(const FwdArgs& a, int grid, hipStream_t stream) {
+  if constexpr (kCanSplit) return launch_flags<FLAGS | F_SPLIT>(a, grid, stream);
+  else return launch_flags<FLAGS>(a, grid, stream);  // never taken
+}
+
 // Compute units of the current device (queried once per device).
 int device_cus() {
   static int cus[64] = {};
@@ -617,18 +630,18 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
   // Fewer workgroups than two per compute unit leave SIMDs with a single
   // wave: split the key range of each workgroup over two wave groups instead
   // (only worth it with enough key tiles to share).
-  const bool split = grid < 2 * device_cus() && p.Sk >= 8 * kBN;
+  const bool split = kCanSplit && grid < 2 * device_cus() && p.Sk >= 8 * kBN;
   const int flags = (mask ? F_MASK : 0) | (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0) |
                     (split ? F_SPLIT : 0);
   switch (flags) {
-    case F_SPLIT | 0: return launch_flags<F_SPLIT | 0>(a, grid, stream);
-    case F_SPLIT | 1: return launch_flags<F_SPLIT | 1>(a, grid, stream);
-    case F_SPLIT | 2: return launch_flags<F_SPLIT | 2>(a, grid, stream);
-    case F_SPLIT | 3: return launch_flags<F_SPLIT | 3>(a, grid, stream);
-    case F_SPLIT | 4: return launch_flags<F_SPLIT | 4>(a, grid, stream);
-    case F_SPLIT | 5: return launch_flags<F_SPLIT | 5>(a, grid, stream);
-    case F_SPLIT | 6: return launch_flags<F_SPLIT | 6>(a, grid, stream);
-    case F_SPLIT | 7: return launch_flags<F_SPLIT | 7>(a, grid, stream);
+    case F_SPLIT | 0: return launch_split<0>(a, grid, stream);
+    case F_SPLIT | 1: return launch_split<1>(a, grid, stream);
+    case F_SPLIT | 2: return launch_split<2>(a, grid, stream);
+    case F_SPLIT | 3: return launch_split<3>(a, grid, stream);
+    case F_SPLIT | 4: return launch_split<4>(a, grid, stream);
+    case F_SPLIT | 5: return launch_split<5>(a, grid, stream);
+    case F_SPLIT | 6: return launch_split<6>(a, grid, stream);
+    case F_SPLIT | 7: return launch_split<7>(a, grid, stream);
     case 0: return launch_flags<0>(a, grid, stream);
     case 1: return launch_flags<1>(a, grid, stream);
     case 2: return launch_flags<2>(a, grid, stream);
@@ -674,7 +687,8 @@ hipError_t ATTN_CAT(launch_paged_prefill_, ATTN_TAG)(const PagedPrefillProblem& 
   const int grid = a.nqb * a.nbh;
   // lengths vary per sequence: the masked variants always; the key split on
   // the same rule as the dense launch, with the longest possible key range
-  const bool split = grid < 2 * device_cus() && (long long)p.max_blocks * p.block_size >= 8 * kBN;
+  const bool split = kCanSplit && grid < 2 * device_cus() &&
+                     (long long)p.max_blocks * p.block_size >= 8 * kBN;
   constexpr int PM = F_PAGED | F_MASK;
   const int flags = (softcap ? F_SOFTCAP : 0) | (p.alibi ? F_ALIBI : 0) | (split ? F_SPLIT : 0);
   switch (flags) {
@@ -682,10 +696,10 @@ hipError_t ATTN_CAT(launch_paged_prefill_, ATTN_TAG)(const PagedPrefillProblem& 
     case F_SOFTCAP: return launch_flags<PM | F_SOFTCAP>(a, grid, stream);
     case F_ALIBI: return launch_flags<PM | F_ALIBI>(a, grid, stream);
     case F_SOFTCAP | F_ALIBI: return launch_flags<PM | F_SOFTCAP | F_ALIBI>(a, grid, stream);
-    case F_SPLIT: return launch_flags<PM | F_SPLIT>(a, grid, stream);
-    case F_SPLIT | F_SOFTCAP: return launch_flags<PM | F_SPLIT | F_SOFTCAP>(a, grid, stream);
-    case F_SPLIT | F_ALIBI: return launch_flags<PM | F_SPLIT | F_ALIBI>(a, grid, stream);
-    default: return launch_flags<PM | F_SPLIT | F_SOFTCAP | F_ALIBI>(a, grid, stream);
+    case F_SPLIT: return launch_split<PM>(a, grid, stream);
+    case F_SPLIT | F_SOFTCAP: return launch_split<PM | F_SOFTCAP>(a, grid, stream);
+    case F_SPLIT | F_ALIBI: return launch_split<PM | F_ALIBI>(a, grid, stream);
+    default: return launch_split<PM | F_SOFTCAP | F_ALIBI>(a, grid, stream);
   }
 }
 

@@ -69,13 +69,15 @@ def test_fwd_check_accepts_valid_calls():
                          softcap=30.0), al=AL) == OK
     assert check_fwd(fwd(dtype=sdpa.ATTN_F32)) == OK
     assert check_fwd(fwd(Hkv=8)) == OK
-    # the vector-ALU path (F32, F64) takes head dims 32 .. 256
+    # the matrix-core path takes 64, 128, 256; the vector-ALU path (F32, F64) 32 .. 256
+    for dt in (sdpa.ATTN_BF16, sdpa.ATTN_F16):
+        assert check_fwd(fwd(dtype=dt, D=256)) == OK, dt
     for dt in (sdpa.ATTN_F32, sdpa.ATTN_F64):
         for d in (32, 64, 128, 256):
             assert check_fwd(fwd(dtype=dt, D=d)) == OK, (dt, d)
 
 
-@pytest.mark.parametrize("dt,d", [(sdpa.ATTN_BF16, 32), (sdpa.ATTN_F16, 256), (sdpa.ATTN_F32, 96),
+@pytest.mark.parametrize("dt,d", [(sdpa.ATTN_BF16, 32), (sdpa.ATTN_F16, 512), (sdpa.ATTN_F32, 96),
                                   (sdpa.ATTN_F64, 80), (sdpa.ATTN_F64, 512)])
 def test_fwd_check_head_dim_per_dtype(dt, d):
     assert check_fwd(fwd(dtype=dt, D=d)) == HEAD_DIM
@@ -103,7 +105,7 @@ def test_fwd_check_empty_tensors_may_be_null():
     (dict(B=-1), SHAPE), (dict(Sq=-2), SHAPE), (dict(Sk=-1), SHAPE),
     (dict(Sq=(1 << 30) + 1), SHAPE),
     (dict(Hkv=3), GQA), (dict(Hkv=0), GQA),
-    (dict(D=96), HEAD_DIM), (dict(D=256), HEAD_DIM), (dict(D=32), HEAD_DIM),
+    (dict(D=96), HEAD_DIM), (dict(D=512), HEAD_DIM), (dict(D=32), HEAD_DIM),
     (dict(softmax_scale=float("nan")), PARAM), (dict(softmax_scale=-1.0), PARAM),
     (dict(softcap=-0.5), PARAM), (dict(softcap=float("inf")), PARAM),
     (dict(window_left=-2), PARAM), (dict(window_right=-5), PARAM),
@@ -245,6 +247,8 @@ def test_paged_prefill_check():
     assert check_varlen(varlen(dtype=sdpa.ATTN_F64)) == UNSUPPORTED
     assert check_varlen(varlen(block_size=16)) == UNSUPPORTED
     assert check_varlen(varlen(D=80)) == HEAD_DIM
+    assert check_varlen(varlen(D=256)) == OK
+    assert check_paged(paged(D=256)) == HEAD_DIM     # decode: head dims 64 and 128
     assert check_varlen(varlen(Hq=6, Hkv=4)) == GQA
     assert check_varlen(varlen(window_left=-2)) == PARAM
     assert check_varlen(varlen(softcap=-1.0)) == PARAM

@@ -111,6 +111,14 @@ def test_key_split_parity(gpu_lib, dtype, D, case):
         assert torch.count_nonzero(out[:, :, :Sq - Sk]).item() == 0
 
 
+# Head dim 256 on the matrix cores (one wave per SIMD, no key split).
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", [0, 3, 5, 7, 9, 11])
+def test_d256_parity(gpu_lib, dtype, case):
+    B, Hq, Hkv, Sq, Sk, kw = SMALL[case]
+    run_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, 256, seed=1000 + case, **kw)
+
+
 @pytest.mark.parametrize("case", [
     (1, 4, 4, 128, 128, 64, dict()),
     (1, 4, 2, 200, 250, 128, dict(causal=True)),
@@ -305,6 +313,11 @@ def run_lse_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, w
 def test_lse_parity(gpu_lib, dtype, D, case):
     B, Hq, Hkv, Sq, Sk, kw = SMALL[case]
     run_lse_case(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=300 + case, **kw)
+
+
+def test_lse_parity_d256(gpu_lib):
+    B, Hq, Hkv, Sq, Sk, kw = KEY_SPLIT[7]
+    run_lse_case(gpu_lib, "bf16", B, Hq, Hkv, Sq, Sk, 256, seed=1100, **kw)
 
 
 @pytest.mark.parametrize("case", [2, 4, 7])

@@ -69,7 +69,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("bf16", 256)])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_paged_prefill_parity(gpu_lib, dtype, D, case):
     sq, sk, Hq, Hkv, bs, kw = CASES[case]
