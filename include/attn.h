@@ -82,8 +82,9 @@ typedef struct attn_fwd_params {
   int64_t Sq;            /* query length (0 allowed: nothing to do)             */
   int64_t Sk;            /* key length (0 allowed: output is all zero); one    *
                           * head's K (Sk * D * element size) must be < 2 GiB    */
-  int64_t D;             /* head dim: 64 or 128 for F16/BF16 (matrix cores);    *
-                          * 32, 64, 128 or 256 for F32/F64 (vector ALU)         */
+  int64_t D;             /* head dim: 64, 128 or 256 for F16/BF16 (matrix      *
+                          * cores; the backward 64 or 128); 32, 64, 128 or 256 *
+                          * for F32/F64 (vector ALU)                            */
   int32_t dtype;         /* attn_dtype_t of q, k, v and out                     */
   int32_t causal;        /* nonzero: bottom-right causal mask                   */
   int64_t window_left;   /* -1: unbounded; else keys j >= i' - window_left      */
@@ -138,7 +139,7 @@ typedef struct attn_paged_params {
   int64_t B;                   /* sequences                                      */
   int64_t Hq;                  /* query heads; a multiple of Hkv                 */
   int64_t Hkv;                 /* key/value heads                                */
-  int64_t D;                   /* head dim: 64 or 128                            */
+  int64_t D;                   /* head dim: 64, 128 or 256                       */
   int64_t num_blocks;          /* physical blocks in each pool                   */
   int64_t block_size;          /* tokens per block (>= 1)                        */
   int64_t max_blocks_per_seq;  /* columns of block_table                         */
@@ -194,7 +195,7 @@ typedef struct attn_varlen_params {
   int64_t B;                   /* sequences                                      */
   int64_t Hq;                  /* query heads; a multiple of Hkv                 */
   int64_t Hkv;                 /* key/value heads                                */
-  int64_t D;                   /* head dim: 64 or 128                            */
+  int64_t D;                   /* head dim: 64, 128 or 256                       */
   int64_t total_q;             /* rows of q and out                              */
   int64_t max_seqlen_q;        /* >= cu_seqlens_q[b+1] - cu_seqlens_q[b] for all b */
   int64_t num_blocks;          /* physical blocks in each pool                   */
@@ -249,12 +250,14 @@ attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* 
  * P (times 1 - tanh^2(s_pre / softcap) with a softcap), dQ = scale dS K and
  * dK = scale dS^T Q.  dk and dv are [B, Hkv, Sk, D], summed over the query
  * heads of each KV head's group; dq is [B, Hq, Sq, D].  A row with no
- * admissible key contributes nothing.  F16/BF16 only (matrix cores, float32
- * accumulation, P and dS rounded to the input dtype as matmul operands);
- * F32/F64 give ATTN_ERR_UNSUPPORTED.  Deterministic: no atomics, fixed
+ * admissible key contributes nothing.  F16/BF16 and head dims 64/128 only
+ * (matrix cores, float32 accumulation, P and dS rounded to the input dtype
+ * as matmul operands); F32/F64 give ATTN_ERR_UNSUPPORTED.  Deterministic: no atomics, fixed
  * order. */
 
-/* Workspace bytes attn_bwd needs for p (8 * B * Hq * Sq), 0 for an invalid p. */
+/* Workspace bytes attn_bwd needs for p, 0 for an invalid p: 8 * B * Hq * Sq
+ * for the forward's row statistics, plus float32 partial dK/dV when the
+ * key blocks' work is split (the split depends only on p). */
 size_t attn_bwd_workspace_size(const attn_fwd_params_t* p);
 
 /* Host-only validation of an attn_bwd call (no HIP call is made).

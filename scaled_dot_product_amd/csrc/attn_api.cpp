@@ -146,7 +146,7 @@ attn_status_t paged_shape(const attn_paged_params_t* p) {
     return ATTN_ERR_SHAPE;
   if (p->block_size < 1) return ATTN_ERR_SHAPE;
   if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
-  if (p->D != 64 && p->D != 128) return ATTN_ERR_HEAD_DIM;
+  if (p->D != 64 && p->D != 128 && p->D != 256) return ATTN_ERR_HEAD_DIM;
   if (p->num_splits < 1 || p->num_splits > 256) return ATTN_ERR_PARAM;
   if (p->B > 65535 || p->Hq > 65535) return ATTN_ERR_SHAPE;
   const int64_t hchunks = (p->Hq / p->Hkv + 15) / 16;

@@ -96,7 +96,7 @@ __device__ __forceinline__ floatx4 mma16x16x16<_Float16>(u32x2 a, u32x2 b, float
 // that the transpose reads (4 rows x 2 chunks per 16 lanes) hit distinct banks.
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
+  return D >= 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
 }
 
 // Block copies are issued as global -> LDS copies in inline asm, so that the
@@ -117,7 +117,7 @@ __device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%
 // banks.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
 template <typename T, int D, int PF, bool UNIFORM, int NW>
@@ -475,9 +475,10 @@ hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t st
   a.c_score = a.softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
   a.c_cap = kLog2e * p.softcap;
   if (dtype == 2)
-    return p.D == 128 ? launch_typed<__bf16, 128>(p, a, stream) : launch_typed<__bf16, 64>(p, a, stream);
-  return p.D == 128 ? launch_typed<_Float16, 128>(p, a, stream)
-                    : launch_typed<_Float16, 64>(p, a, stream);
+    return p.D == 256 ? launch_typed<__bf16, 256>(p, a, stream)
+         : p.D == 128 ? launch_typed<__bf16, 128>(p, a, stream) : launch_typed<__bf16, 64>(p, a, stream);
+  return p.D == 256 ? launch_typed<_Float16, 256>(p, a, stream)
+       : p.D == 128 ? launch_typed<_Float16, 128>(p, a, stream) : launch_typed<_Float16, 64>(p, a, stream);
 }
 
 }  // namespace attn

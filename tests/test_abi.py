@@ -248,7 +248,8 @@ def test_paged_prefill_check():
     assert check_varlen(varlen(block_size=16)) == UNSUPPORTED
     assert check_varlen(varlen(D=80)) == HEAD_DIM
     assert check_varlen(varlen(D=256)) == OK
-    assert check_paged(paged(D=256)) == HEAD_DIM     # decode: head dims 64 and 128
+    assert check_paged(paged(D=256)) == OK
+    assert check_paged(paged(D=96)) == HEAD_DIM
     assert check_varlen(varlen(Hq=6, Hkv=4)) == GQA
     assert check_varlen(varlen(window_left=-2)) == PARAM
     assert check_varlen(varlen(softcap=-1.0)) == PARAM

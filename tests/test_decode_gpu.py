@@ -42,6 +42,10 @@ CASES = [
     ("bf16", 2, 32, 1, 128, 16, [333, 129], 4, None, True),
     ("bf16", 2, 24, 8, 64, 64, [700, 64], 8, 30.0, False),
     ("bf16", 3, 10, 5, 128, 48, [1, 480, 481], 16, None, False),
+    # head dim 256
+    ("bf16", 3, 8, 2, 256, 64, [700, 1, 129], 8, None, False),
+    ("f16", 2, 16, 4, 256, 16, [333, 64], 4, 20.0, True),
+    ("bf16", 2, 4, 4, 256, 5, [50, 17], 2, None, False),
 ]
 
 
