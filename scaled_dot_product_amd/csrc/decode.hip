@@ -37,6 +37,8 @@
 // to the input type.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -384,6 +386,299 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(DecArgs a) {
   }
 }
 
+// Four transpose reads of LDS (byte addresses a[0..3]) in one asm statement that
+// also waits for them: the compiler does not see these reads, so it adds no
+// wait of its own for the copies still landing in the other ring slots, and
+// every output is written when the statement ends.
+__device__ __forceinline__ void lds_tr4(u32x2 (&v)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
+// Persistent form for block sizes that are multiples of kTB.  The grid fills
+// the chip once (8 waves per compute unit, the rate at which the pool streams
+// best) and every wave is an independent worker over whole work items, item =
+// (split, KV head, head chunk, sequence), taken in order of decreasing
+// sequence length (ties by index) and dealt in snake order (round k: wave w
+// takes rank k W + w, or k W + W - 1 - w on odd rounds) so that each wave's
+// total is close to the mean; within a sequence the items go split-major, so
+// waves running side by side read the same token rows.
+// Per block the K rows go straight into registers in the A-operand layout and
+// the V rows into the wave's 3-slot LDS ring (two blocks ahead).  A worker
+// ends an item by storing its normalised partial and LSE from registers and
+// goes straight on with the next item, whose Q and first page ids it loaded
+// one item earlier: no wave waits for its stores to be acknowledged, and no
+// item starts cold.  Every load and copy is one the compiler counts, so its
+// waits are exact; only the V transpose reads are inline asm, after an
+// explicit wait for that block's copies.
+constexpr int kOrdMax = 256;   // batches up to this size are ordered longest-first
+constexpr int kStreamWaves = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(DecArgs a) {
+  using E = Elem<T>;
+  constexpr int NW = kStreamWaves;
+  constexpr int KS = D / 32;          // 16x16x32 steps of S^T over d
+  constexpr int NCH = D / 8;          // 16-byte chunks per row
+  constexpr int ROWS = 64 / NCH;      // rows per V copy instruction
+  constexpr int CPB = kTB / ROWS;     // V copy instructions per block
+  constexpr int DB = D / 16;          // 16-row blocks of O^T
+  constexpr int PF = 2;
+  constexpr int NS = PF + 1;
+  constexpr int SLOT = kTB * NCH;
+  static_assert(NS == 3 && kPageWindow % NS == 0 && DB % 4 == 0, "ring and read batches");
+  __shared__ u32x4 vring0[NW][SLOT], vring1[NW][SLOT], vring2[NW][SLOT];
+  __shared__ int ord[kOrdMax], lens_lds[kOrdMax];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, hl = lane & 15;
+
+  // ---- ord[r] = the r-th longest sequence (the launcher guarantees
+  // B <= kOrdMax); the lengths stay in LDS so that no item start waits on a
+  // global load
+  for (int i = tid; i < a.B; i += 64 * NW) lens_lds[i] = a.lens[i];
+  __syncthreads();
+  for (int i = tid; i < a.B; i += 64 * NW) {
+    const int li = lens_lds[i];
+    int r = 0;
+    for (int j = 0; j < a.B; ++j) {
+      const int lj = lens_lds[j];
+      r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+    }
+    ord[r] = i;
+  }
+  __syncthreads();
+
+  const int nhc = a.Hkv * a.hchunks;
+  const int per_seq = nhc * a.splits;
+  const int n_items = a.B * per_seq;
+  const int W = gridDim.x * NW;
+  const int gw = blockIdx.x * NW + wave;
+  const size_t tok_stride = (size_t)a.Hkv * D;
+  const int crow = lane / NCH, cch = lane % NCH;
+  const int cap = a.maxb * a.bs;
+  auto vslot = [&](int u) -> u32x4* { return u == 0 ? vring0[wave] : (u == 1 ? vring1[wave] : vring2[wave]); };
+  auto lds_addr = [](const void* p) { return (uint32_t)(uintptr_t)(const ATTN_LDS void*)p; };
+  bool bad_page = false, bad_len = false;
+
+  // ---- the k-th item of this wave (wave-uniform fields)
+  struct Item { int b, kvh, h0, nh, split, ctx, t0, t1, nj; };
+  auto item_of = [&](int k, Item& it) -> bool {
+    const int base = k * W;
+    if (base >= n_items) return false;
+    const int r = base + ((k & 1) ? (W - 1 - gw) : gw);
+    if (r >= n_items) return false;
+    const int sr = r / per_seq;
+    const int rem = r - sr * per_seq;
+    it.split = rem / nhc;
+    const int y = rem - it.split * nhc;
+    it.b = __builtin_amdgcn_readfirstlane(ord[sr]);
+    it.kvh = y / a.hchunks;
+    const int hc = y - it.kvh * a.hchunks;
+    it.h0 = it.kvh * a.group + hc * 16;
+    it.nh = min(16, a.group - hc * 16);
+    int ctx = __builtin_amdgcn_readfirstlane(lens_lds[it.b]);
+    if (ctx < 0 || ctx > cap) {
+      bad_len = true;
+      ctx = ctx < 0 ? 0 : cap;
+    }
+    it.ctx = ctx;
+    const int per = (ctx + a.splits - 1) / a.splits;
+    const int chunk = (per + kTB - 1) / kTB * kTB;
+    it.t0 = min(ctx, it.split * chunk);
+    it.t1 = min(ctx, it.t0 + chunk);
+    it.nj = (it.t1 - it.t0 + kTB - 1) / kTB;
+    return true;
+  };
+  // Q of an item as the B operand (lane: head hl, d = 32 ks + 8 g .. + 7) and
+  // the physical blocks of its blocks c0 .. c0 + 62 (lane j: block c0 + j)
+  auto load_q = [&](const Item& it, u32x4 (&q)[KS], float& slope) {
+    const T* Qb = reinterpret_cast<const T*>(a.q) + ((size_t)it.b * a.Hq + it.h0) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      q[ks] = hl < it.nh ? load16(Qb + hl * D + 32 * ks + 8 * g) : zero_u32x4();
+    slope = (a.alibi && hl < it.nh) ? a.alibi[it.h0 + hl] * kLog2e : 0.f;
+  };
+  auto load_pages = [&](const Item& it, int c0) -> int {
+    const int j = c0 + lane;
+    return j < it.nj ? a.table[(size_t)it.b * a.maxb + (it.t0 + kTB * j) / a.bs] : 0;
+  };
+
+  Item cur, nxt;
+  bool have = item_of(0, cur);
+  bool have_nxt = have && item_of(1, nxt);
+  u32x4 qf[KS], qn[KS];
+  int page_reg = 0, page_nxt = 0;
+  float slope_l2 = 0.f, slope_nxt = 0.f;
+  if (have) {
+    load_q(cur, qf, slope_l2);
+    page_reg = load_pages(cur, 0);
+  }
+  if (have_nxt) {
+    load_q(nxt, qn, slope_nxt);
+    page_nxt = load_pages(nxt, 0);
+  }
+
+  u32x4 kr[NS][KS];   // K rows of ring slot u
+  uint32_t valid[NS]; // per ring slot: bit t = token t of the block is live
+  for (int k = 0; have; ++k) {
+    const float qpos = (float)(cur.ctx - 1);
+    floatx4 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_part = 0.f;
+    const T* Kp = reinterpret_cast<const T*>(a.kp) + (size_t)cur.kvh * D;
+    const T* Vp = reinterpret_cast<const T*>(a.vp) + (size_t)cur.kvh * D;
+
+    // Copies of block j (window-relative jw for its page id) into ring slot u;
+    // a block that is not `live` is padding: it keeps every block followed by
+    // exactly PF fetches, but reads nothing.
+    auto fetch = [&](int u, int j, int jw, bool live) {
+      const int tb = __builtin_amdgcn_readfirstlane(cur.t0 + kTB * j);
+      const int nvalid = live ? min(kTB, cur.t1 - tb) : 0;
+      const int phys = __builtin_amdgcn_readlane(page_reg, live ? jw : 0);
+      const bool ok = nvalid > 0 && (unsigned)phys < (unsigned)a.num_blocks;
+      bad_page |= nvalid > 0 && !ok;
+      const long long row0 = ok ? ((long long)phys * a.bs + (tb % a.bs)) * (long long)tok_stride : 0;
+      const long long bytes = ok ? (long long)nvalid * tok_stride * sizeof(T) : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp + row0, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp + row0, bytes);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kr[u][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, (int)((hl * tok_stride + 32 * ks + 8 * g) * sizeof(T)), 0, 0);
+      u32x4* vs_ = vslot(u);
+#pragma unroll
+      for (int i = 0; i < CPB; ++i) {
+        const int r = crow + ROWS * i;
+        dma16(rv, vs_ + i * 64, (int)((r * tok_stride + 8 * (cch ^ swz_v<D>(r))) * sizeof(T)));
+      }
+      valid[u] = ok ? (nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u)) : 0u;
+    };
+
+    auto compute = [&](int u, int j) {
+      const int tb = cur.t0 + kTB * j;
+      const T* vs = reinterpret_cast<const T*>(vslot(u));
+      // S^T = K Q^T: A operand lane (g, hl) = K row hl, d = 32 ks + 8 g .. + 7
+      floatx4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sv = E::mma16(kr[u][ks], qf[ks], sv);
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = sv[r];
+        if (a.softcap) {
+          const float ex = fast_exp2(x * a.c_score);
+          x = a.c_cap - 2.f * a.c_cap * fast_rcp(1.f + ex);
+        } else {
+          x *= a.c_score;
+        }
+        const int tok = 4 * g + r;
+        x = __builtin_fmaf(slope_l2, (float)(tb + tok) - qpos, x);
+        sv[r] = ((valid[u] >> tok) & 1u) ? x : kNegInf;
+        mx = __builtin_fmaxf(mx, sv[r]);
+      }
+      mx = groups_max(mx);
+      const bool need = mx > m_run + kRescaleGap;
+      if (wave_any(need)) {
+        const float alpha = need ? fast_exp2(m_run - mx) : 1.f;
+        m_run = need ? mx : m_run;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      const uint32_t p01 = E::pack2(fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use));
+      const uint32_t p23 = E::pack2(fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use));
+      l_part = E::dot2(p01, E::kOnePair, l_part);
+      l_part = E::dot2(p23, E::kOnePair, l_part);
+      const u32x2 pf = {p01, p23};
+      // O^T += V^T P^T: A operand lane (g, hl) = V[4 g + 0..3][16 db + hl];
+      // this block's V copies have landed once at most PF later fetches (KS
+      // loads + CPB copies each) remain in flight
+      wait_vmem_le<PF * (KS + CPB)>();
+      const int tr_row = 4 * g + (hl >> 2);
+      const int sw = swz_v<D>(tr_row);
+#pragma unroll
+      for (int d4 = 0; d4 < DB; d4 += 4) {
+        uint32_t ad[4];
+        u32x2 va[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = 16 * (d4 + q) + 4 * (hl & 3);
+          ad[q] = lds_addr(vs + tr_row * D + ((col >> 3) ^ sw) * 8 + (col & 7));
+        }
+        lds_tr4(va, ad);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[d4 + q] = mma16x16x16<T>(va[q], pf, o[d4 + q]);
+      }
+    };
+
+    for (int c0 = 0; c0 < cur.nj; c0 += kPageWindow) {
+      const int cn = min(kPageWindow, cur.nj - c0);
+      // items of more than one window: the next window's page ids load
+      // while this one streams
+      int page_win = 0;
+      if (c0 + kPageWindow < cur.nj) page_win = load_pages(cur, c0 + kPageWindow);
+#pragma unroll
+      for (int p = 0; p < PF; ++p) fetch(p, c0 + p, p, p < cn);
+      for (int j0 = 0; j0 < cn; j0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const int jw = j0 + u;
+          const int jf = jw + PF;
+          fetch((u + PF) % NS, c0 + jf, jf, jf < cn);
+          if (jw < cn) compute(u, c0 + jw);
+        }
+      }
+      page_reg = page_win;
+    }
+
+    // ---- this item's partial: o / l and its LSE, per head (lane group g
+    // holds d = 16 db + 4 g .. + 3)
+    const float l = groups_sum(l_part);
+    if (hl < cur.nh) {
+      const size_t slot = ((size_t)cur.b * a.Hq + cur.h0 + hl) * a.splits + cur.split;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* dst = a.ws_o + slot * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        floatx4 w = o[db];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[c] *= inv;
+        *reinterpret_cast<floatx4*>(dst + 16 * db) = w;
+      }
+      if (g == 0) a.ws_lse[slot] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+    }
+
+    // ---- next item: its Q and page ids arrived long ago; start those of the
+    // one after it
+    have = have_nxt;
+    if (have) {
+      cur = nxt;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+      page_reg = page_nxt;
+      slope_l2 = slope_nxt;
+      have_nxt = item_of(k + 2, nxt);
+      if (have_nxt) {
+        load_q(nxt, qn, slope_nxt);
+        page_nxt = load_pages(nxt, 0);
+      }
+    }
+  }
+  wait_vmem();  // no copy may still be writing this workgroup's LDS at exit
+  if ((bad_page || bad_len) && a.err && lane == 0) *a.err = 1;
+}
+
 struct MergeArgs {
   const float* ws_o;
   const float* ws_lse;
@@ -432,11 +727,33 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
 #define ATTN_DECODE_WAVES 2
 #endif
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                   ? n : 256;
+  }
+  return cus[dev];
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t stream) {
   constexpr int NW = ATTN_DECODE_WAVES;
   const dim3 grid(p.splits, p.Hkv * a.hchunks, p.B);
-  if (p.block_size % kTB == 0)
+  if (p.block_size % kTB == 0 && p.B <= kOrdMax) {
+    // persistent: as many 4-wave workgroups as are resident at once (two per
+    // compute unit, one at head dim 256), never more than there are items
+    const long long items = (long long)p.B * p.Hkv * a.hchunks * p.splits;
+    const long long per_cu = D <= 128 ? 2 : 1;  // head dim 256: one wave per SIMD
+    const long long wgs = std::min<long long>((items + kStreamWaves - 1) / kStreamWaves,
+                                              per_cu * device_cus());
+    hipLaunchKernelGGL((decode_stream_kernel<T, D>), dim3((unsigned)wgs), dim3(64 * kStreamWaves), 0,
+                       stream, a);
+  } else if (p.block_size % kTB == 0)
     hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, true, NW>), grid, dim3(64 * NW), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, false, NW>), grid, dim3(64 * NW), 0, stream, a);
