@@ -144,7 +144,11 @@ typedef struct attn_paged_params {
   int64_t block_size;          /* tokens per block (>= 1)                        */
   int64_t max_blocks_per_seq;  /* columns of block_table                         */
   int32_t dtype;               /* attn_dtype_t of q, pools and out (F16, BF16)   */
-  int32_t num_splits;          /* key-dimension splits per sequence, 1..256      */
+  int32_t num_splits;          /* key-dimension splits per sequence, 1..256 (a
+                                  tuning value: batches of at least one
+                                  (sequence, KV head, 16-query-head chunk)
+                                  group per compute unit split each group
+                                  over the waves of one workgroup instead)  */
   float softmax_scale;         /* finite, >= 0                                   */
   float softcap;               /* 0: off; > 0: softcap * tanh(s / softcap)       */
 } attn_paged_params_t;
@@ -174,8 +178,14 @@ attn_status_t attn_paged_decode_check(const void* q, const void* k_pool, const v
                                       const attn_paged_params_t* p);
 
 /* Paged split-KV decode: validates as attn_paged_decode_check, then enqueues
- * the partial kernel (one workgroup per sequence, KV head and split) and the
- * merge kernel on `stream` and returns.  Device-side errors do not fault:
+ * the kernels on `stream` and returns: for block sizes that are multiples of
+ * 16 and B <= 256, a persistent kernel (one workgroup per compute unit) that
+ * either merges each group's splits in LDS and writes out directly (batches
+ * with at least one group per compute unit; the workspace is then not
+ * touched) or writes per-split partials for the merge kernel; otherwise a
+ * partial kernel (one workgroup per sequence, KV head and split) and the
+ * merge kernel.  The result is the same up to rounding order in every form.
+ * Device-side errors do not fault:
  * a seq_len outside [0, max_blocks_per_seq * block_size] is clamped into that
  * range and a block_table entry outside [0, num_blocks) masks its keys; both
  * store 1 to *error_flag when error_flag is not NULL (the flag is never

@@ -10,31 +10,36 @@
 // re-bases each part to a common max exactly as the section-3 recurrence
 // re-bases tiles.
 //
-// Partial kernel: one workgroup per (split, KV head [x 16-head chunk], sequence),
-// sequences taken longest first (each workgroup ranks the lengths itself).
-//   * The split's tokens are cut into 16-token blocks dealt round-robin to the
-//     4 waves; every wave keeps its own online-softmax state, so there is no
-//     barrier until the final 4-way merge through LDS.
-//   * Both products run on the matrix cores with the query heads of the KV
-//     head as the N dimension (up to 16 per workgroup, padded):
-//       S^T = K Q^T    16x16x32, gathered key rows as the A operand straight
-//                      from the pool (64 contiguous bytes per 4 lanes);
-//       O^T += V^T P^T 16x16x16, where the S^T accumulator (4 tokens of one
-//                      head per lane) is already the P^T operand and V^T comes
-//                      from a per-wave LDS block through the transpose read.
-//     Every lane therefore owns one head: softmax state, rescale and output
-//     need no cross-lane reduction except the block max over 4 lane groups.
-//   * Loads run PF blocks ahead in a register ring.  When every 16-token block
-//     lies inside one KV block (block_size % 16 == 0) the physical block of a
-//     whole block is one wave-uniform value: a wave reads the page ids of its
-//     next 64 blocks in one load and broadcasts them with readlane, and the
-//     loads go through a buffer descriptor whose size ends at the split's last
-//     live token (later rows read as zero, no branches).  Other block sizes
-//     translate every token separately.
-//   * Output per (sequence, head, split): normalised partial o[D] and its
-//     natural-log LSE, into the caller's workspace.
-// Merge kernel: 4 d per thread, splits combined in fixed order, result cast
-// to the input type.
+// Three forms, chosen by the launcher:
+//   * fused persistent (block_size % 16 == 0, B <= 256, at least one
+//     (sequence, KV head, 16-head chunk) group per compute unit): one
+//     workgroup per compute unit walks whole groups; its waves stream equal
+//     token chunks of a group and merge them through LDS, writing the output;
+//   * split persistent (block_size % 16 == 0, B <= 256, smaller batches):
+//     every wave walks (split, group) items and writes a partial per item,
+//     combined by the merge kernel;
+//   * partial kernel (any block size or batch): one workgroup per (split,
+//     group), then the merge kernel.
+// Common to all: both products run on the matrix cores with the query heads
+// of the KV head as the N dimension (up to 16, padded):
+//     S^T = K Q^T    16x16x32, gathered key rows as the A operand straight
+//                    from the pool (64 contiguous bytes per 4 lanes);
+//     O^T += V^T P^T 16x16x16, where the S^T accumulator (4 tokens of one
+//                    head per lane) is already the P^T operand and V^T comes
+//                    from a per-wave LDS block through the transpose read.
+// Every lane therefore owns one head: softmax state, rescale and output need
+// no cross-lane reduction except the block max over 4 lane groups.  Loads run
+// two 16-token blocks ahead.  When every 16-token block lies inside one KV
+// block (block_size % 16 == 0) the physical block of a whole block is one
+// wave-uniform value: a wave reads the page ids of its next 63 blocks in one
+// load and broadcasts them with readlane, and the loads go through a buffer
+// descriptor whose size ends at the chunk's last live token (later rows read
+// as zero, no branches).  Other block sizes translate every token separately.
+// Sequences are taken longest first (each workgroup ranks the lengths
+// itself).  Partials are the normalised o[D] and its natural-log LSE per
+// (sequence, head, split) in the caller's workspace; the merge kernel takes 4
+// d per thread, combines the splits in fixed order and casts to the input
+// type.
 #include <limits.h>
 
 #include <algorithm>
@@ -59,6 +64,7 @@ struct DecArgs {
   const float* alibi;
   float* ws_o;
   float* ws_lse;
+  void* out;      // [B, Hq, D] (the fused persistent form writes it directly)
   int32_t* err;
   int B, Hq, Hkv, group, hchunks, num_blocks, bs, maxb, splits;
   int softcap;
@@ -418,13 +424,23 @@ __device__ __forceinline__ void lds_tr4(u32x2 (&v)[4], const uint32_t (&a)[4]) {
 // item starts cold.  Every load and copy is one the compiler counts, so its
 // waits are exact; only the V transpose reads are inline asm, after an
 // explicit wait for that block's copies.
+//
+// Fused form (FUSED, when there are at least as many (sequence, KV head, head
+// chunk) groups as compute units): the worker is the whole workgroup and the
+// item is a group; wave w streams the w-th of NW equal token chunks of the
+// group, and at the group's end the NW partial states meet in the waves' ring
+// slots and the workgroup writes the output itself (the same re-basing to a
+// common max as the merge kernel), so there is neither a workspace round trip
+// nor a second launch.
 constexpr int kOrdMax = 256;   // batches up to this size are ordered longest-first
 constexpr int kStreamWaves = 4;
+template <bool FUSED, int D>
+constexpr int stream_waves() { return FUSED ? (D <= 128 ? 8 : 4) : kStreamWaves; }
 
-template <typename T, int D>
-__global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(DecArgs a) {
+template <typename T, int D, bool FUSED>
+__global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream_kernel(DecArgs a) {
   using E = Elem<T>;
-  constexpr int NW = kStreamWaves;
+  constexpr int NW = stream_waves<FUSED, D>();
   constexpr int KS = D / 32;          // 16x16x32 steps of S^T over d
   constexpr int NCH = D / 8;          // 16-byte chunks per row
   constexpr int ROWS = 64 / NCH;      // rows per V copy instruction
@@ -436,6 +452,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(DecArg
   static_assert(NS == 3 && kPageWindow % NS == 0 && DB % 4 == 0, "ring and read batches");
   __shared__ u32x4 vring0[NW][SLOT], vring1[NW][SLOT], vring2[NW][SLOT];
   __shared__ int ord[kOrdMax], lens_lds[kOrdMax];
+  __shared__ float2 ml_x[FUSED ? NW : 1][16];  // fused: per wave and head, (max, sum)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -458,10 +475,11 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(DecArg
   __syncthreads();
 
   const int nhc = a.Hkv * a.hchunks;
-  const int per_seq = nhc * a.splits;
+  const int splits = FUSED ? 1 : a.splits;
+  const int per_seq = nhc * splits;
   const int n_items = a.B * per_seq;
-  const int W = gridDim.x * NW;
-  const int gw = blockIdx.x * NW + wave;
+  const int W = FUSED ? gridDim.x : gridDim.x * NW;    // workers
+  const int gw = FUSED ? blockIdx.x : blockIdx.x * NW + wave;
   const size_t tok_stride = (size_t)a.Hkv * D;
   const int crow = lane / NCH, cch = lane % NCH;
   const int cap = a.maxb * a.bs;
@@ -491,9 +509,10 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(DecArg
       ctx = ctx < 0 ? 0 : cap;
     }
     it.ctx = ctx;
-    const int per = (ctx + a.splits - 1) / a.splits;
+    const int parts = FUSED ? NW : a.splits;
+    const int per = (ctx + parts - 1) / parts;
     const int chunk = (per + kTB - 1) / kTB * kTB;
-    it.t0 = min(ctx, it.split * chunk);
+    it.t0 = min(ctx, (FUSED ? wave : it.split) * chunk);
     it.t1 = min(ctx, it.t0 + chunk);
     it.nj = (it.t1 - it.t0 + kTB - 1) / kTB;
     return true;
@@ -645,7 +664,47 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(DecArg
     // ---- this item's partial: o / l and its LSE, per head (lane group g
     // holds d = 16 db + 4 g .. + 3)
     const float l = groups_sum(l_part);
-    if (hl < cur.nh) {
+    if constexpr (FUSED) {
+      // every copy into this wave's ring has landed; heads 0..7 go to slot 0,
+      // heads 8..15 to slot 1 (8 rows of D floats each)
+      wait_vmem();
+      float* ex = reinterpret_cast<float*>(hl < 8 ? vring0[wave] : vring1[wave]) + (hl & 7) * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<floatx4*>(ex + 16 * db) = o[db];
+      if (g == 0) ml_x[wave][hl] = float2{m_run, l};
+      __syncthreads();
+      constexpr int TPH = D / 4;             // threads per head, 4 d each
+      constexpr int HPP = 64 * NW / TPH;     // heads per pass
+      const int d4 = (tid % TPH) * 4;
+      for (int h = tid / TPH; h < cur.nh; h += HPP) {
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float2 s = ml_x[w][h];
+          M = s.y > 0.f ? __builtin_fmaxf(M, s.x) : M;
+        }
+        floatx4 num = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const float2 s = ml_x[w][h];
+            if (s.y > 0.f) {
+              const float c = fast_exp2(s.x - M);
+              const float* src = reinterpret_cast<const float*>(h < 8 ? vring0[w] : vring1[w]) + (h & 7) * D + d4;
+              const floatx4 v = *reinterpret_cast<const floatx4*>(src);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) num[e] = __builtin_fmaf(c, v[e], num[e]);
+              den = __builtin_fmaf(c, s.y, den);
+            }
+          }
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const u32x2 w2 = {E::pack2(num[0] * inv, num[1] * inv), E::pack2(num[2] * inv, num[3] * inv)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.out) + ((size_t)cur.b * a.Hq + cur.h0 + h) * D + d4) = w2;
+      }
+      __syncthreads();  // the ring slots are free again
+    } else if (hl < cur.nh) {
       const size_t slot = ((size_t)cur.b * a.Hq + cur.h0 + hl) * a.splits + cur.split;
       const float inv = l > 0.f ? 1.f / l : 0.f;
       float* dst = a.ws_o + slot * D + 4 * g;
@@ -744,14 +803,22 @@ template <typename T, int D>
 hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t stream) {
   constexpr int NW = ATTN_DECODE_WAVES;
   const dim3 grid(p.splits, p.Hkv * a.hchunks, p.B);
+  const long long groups = (long long)p.B * p.Hkv * a.hchunks;
+  const int cus = device_cus();
+  if (p.block_size % kTB == 0 && p.B <= kOrdMax && groups >= cus) {
+    // fused persistent form: one workgroup per compute unit (it fills the
+    // unit's registers), the output written directly
+    constexpr int FW = stream_waves<true, D>();
+    hipLaunchKernelGGL((decode_stream_kernel<T, D, true>), dim3((unsigned)cus), dim3(64 * FW), 0, stream, a);
+    return hipGetLastError();
+  }
   if (p.block_size % kTB == 0 && p.B <= kOrdMax) {
     // persistent: as many 4-wave workgroups as are resident at once (two per
     // compute unit, one at head dim 256), never more than there are items
-    const long long items = (long long)p.B * p.Hkv * a.hchunks * p.splits;
+    const long long items = groups * p.splits;
     const long long per_cu = D <= 128 ? 2 : 1;  // head dim 256: one wave per SIMD
-    const long long wgs = std::min<long long>((items + kStreamWaves - 1) / kStreamWaves,
-                                              per_cu * device_cus());
-    hipLaunchKernelGGL((decode_stream_kernel<T, D>), dim3((unsigned)wgs), dim3(64 * kStreamWaves), 0,
+    const long long wgs = std::min<long long>((items + kStreamWaves - 1) / kStreamWaves, per_cu * cus);
+    hipLaunchKernelGGL((decode_stream_kernel<T, D, false>), dim3((unsigned)wgs), dim3(64 * kStreamWaves), 0,
                        stream, a);
   } else if (p.block_size % kTB == 0)
     hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, true, NW>), grid, dim3(64 * NW), 0, stream, a);
@@ -778,6 +845,7 @@ hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t st
   a.alibi = p.alibi;
   a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse;
+  a.out = p.out;
   a.err = p.error_flag;
   a.B = p.B;
   a.Hq = p.Hq;

@@ -67,6 +67,48 @@ def test_paged_parity(gpu_lib, case):
             assert torch.count_nonzero(out[b]).item() == 0
 
 
+def wide_lens(B, hi, seed):
+    """Lengths for the wide batches: empty, single-token, block-edge and long
+    sequences mixed, the rest uniform on [0, hi]."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, hi + 1, size=B)
+    edge = [0, 1, 15, 16, 17, 127, 128, 129, hi]
+    lens[:len(edge)] = edge
+    return rng.permutation(lens).astype(np.int32).tolist()
+
+
+# Batches of at least 256 (sequence, KV head, 16-head chunk) groups: one per
+# compute unit of a 256-CU chip or more, so that every group is a whole
+# workgroup's item and the workgroup merges its chunks itself.
+WIDE_CASES = [
+    # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
+    ("bf16", 64, 8, 4, 128, 16, 700, 8, None, False),
+    ("f16", 128, 4, 2, 64, 32, 300, 4, 15.0, True),
+    ("bf16", 64, 40, 2, 128, 64, 400, 8, None, True),     # 20 heads per KV head: 2 chunks
+    ("bf16", 64, 16, 4, 256, 16, 500, 8, None, False),
+    ("f16", 256, 2, 1, 128, 48, 200, 2, 30.0, False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE_CASES)))
+def test_paged_parity_wide_batch(gpu_lib, case):
+    dtype, B, Hq, Hkv, D, bs, hi, splits, cap, use_alibi = WIDE_CASES[case]
+    lens = wide_lens(B, hi, 300 + case)
+    maxb = (max(lens) + bs - 1) // bs + 1
+    w = W.Paged("t", dtype, B, Hq, Hkv, D, bs, 0, 0, splits, maxb, seed=310 + case)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    alibi = torch.from_numpy(W.alibi_slopes(Hq)) if use_alibi else None
+    scale = D ** -0.5
+    announce(f"paged decode wide case {case}: {WIDE_CASES[case]}")
+    out = gpu_decode(gpu_lib, q, kp, vp, table, sl, alibi, softmax_scale=scale, softcap=cap,
+                     num_splits=splits)
+    ref = oracle_decode(q, kp, vp, table, sl, alibi, scale=scale, softcap=cap)
+    compare(out, ref, DT[dtype], f"paged wide case {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
 def test_paged_decode_workload(gpu_lib):
     w = W.PAGED_DECODE
     q, kp, vp, table, lens, _ = W.paged_inputs(w)
@@ -77,28 +119,34 @@ def test_paged_decode_workload(gpu_lib):
     compare(out, ref, torch.bfloat16, w.name)
 
 
-@pytest.mark.parametrize("bs,splits", [(64, 8), (16, 3), (5, 1)])
-def test_paging_is_bit_exact(gpu_lib, bs, splits):
+@pytest.mark.parametrize("bs,splits,B,Hkv", [(64, 8, 4, 2), (16, 3, 4, 2), (5, 1, 4, 2),
+                                             (16, 8, 64, 4), (32, 2, 128, 2)])
+def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
     """One-hot scores: q = 1024 e0 in every head and a single key row equal to
     8 e0 give that key a score of 1024 * 8 / sqrt(128) ~ 724 and every other
     key 0, so exp underflows to exactly 0 elsewhere and the output is exactly
     the V row of that logical token.  V rows hold (sequence, position % 128,
     position // 128, kv head) as bf16-exact integers; slots no table entry
-    points at hold a finite sentinel so that a stray read is visible."""
-    B, Hq, Hkv, D = 4, 8, 2, 128
-    lens = [130, 64, 7, 200]
+    points at hold a finite sentinel so that a stray read is visible.  The
+    last two cases have 256 (sequence, KV head) groups."""
+    Hq, D = 8, 128
+    lens = [130, 64, 7, 200] if B == 4 else np.random.default_rng(6).integers(1, 260, size=B).tolist()
     rng = np.random.default_rng(5)
     maxb = (max(lens) + bs - 1) // bs + 1
     table_np, nb = W.paged_layout(np.array(lens), bs, maxb, rng)
     nb_pool = nb + 3                        # three blocks nobody references
     kp = torch.zeros(nb_pool, bs, Hkv, D, dtype=torch.bfloat16)
-    vp = torch.full((nb_pool, bs, Hkv, D), 1e4, dtype=torch.bfloat16)
+    vp_np = np.full((nb_pool, bs, Hkv, D), 1e4, dtype=np.float32)
     for b, n in enumerate(lens):
-        for t in range(n):
-            blk, slot = table_np[b, t // bs], t % bs
-            for g in range(Hkv):
-                vp[blk, slot, g, :4] = torch.tensor([b, t % 128, t // 128, g], dtype=torch.bfloat16)
-                vp[blk, slot, g, 4:] = 0
+        t = np.arange(n)
+        blk, slot = table_np[b, t // bs], t % bs
+        row = np.zeros((n, Hkv, D), dtype=np.float32)
+        row[:, :, 0] = b
+        row[:, :, 1] = (t % 128)[:, None]
+        row[:, :, 2] = (t // 128)[:, None]
+        row[:, :, 3] = np.arange(Hkv)[None, :]
+        vp_np[blk, slot] = row
+    vp = torch.from_numpy(vp_np).to(torch.bfloat16)
     q = torch.zeros(B, Hq, 1, D, dtype=torch.bfloat16)
     q[..., 0] = 1024.0
     table = torch.from_numpy(table_np)
