@@ -6,8 +6,9 @@ One step = one pass of the whole path over one batch of synthetic input:
     scale 1/sqrt(128) -- causal-effective TFLOP/s (4 * D * admissible pairs);
   * decode: attn_paged_decode, bf16, B=64, Hq=32, Hkv=8, D=128, context
     lengths uniform on [512, 8192], 64-token blocks randomly permuted in one
-    pool, 8 key splits -- HBM GB/s over the live K/V bytes plus Q, out and the
-    block-table entries read.
+    pool, num_splits 8 (the fused form splits each (sequence, KV head) over
+    the 8 waves of a workgroup) -- HBM GB/s over the live K/V bytes plus Q,
+    out and the block-table entries read.
 
 Inputs are generated (seeded) and resident in device memory before the timed
 region.  Kernel durations come from HIP events recorded on the stream the
@@ -285,7 +286,7 @@ def bench(args):
                 "work_per_launch": flops, "ms_per_launch": t_pre * 1e3}
     roof_dec = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": traffic.get("decode_bytes"),
-                "kernel": "decode_partial_kernel<bf16, D=128, 4 heads> + decode_merge_kernel",
+                "kernel": "decode_stream_kernel<bf16, D=128, fused> (one launch: 512 groups >= 256 CUs)",
                 "work_per_launch": nbytes, "ms_per_launch": t_dec * 1e3}
     dominant = roof_pre if t_pre >= t_dec else roof_dec
     result = {
@@ -387,14 +388,15 @@ def _counter_means(path, counter):
     files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         sys.exit(f"no rocprofv3 counter output under {path}")
-    vals = {"prefill": [], "decode_partial": [], "decode_merge": [], "copy": []}
+    vals = {"prefill": [], "decode_main": [], "decode_merge": [], "copy": []}
     for fn in files:
         with open(fn) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
                 n = r["Kernel_Name"]
-                key = ("prefill" if "fwd_mfma_kernel" in n else "decode_partial" if "decode_partial" in n
+                key = ("prefill" if "fwd_mfma_kernel" in n
+                       else "decode_main" if ("decode_partial" in n or "decode_stream" in n)
                        else "decode_merge" if "decode_merge" in n else "copy" if "neg_kernel" in n else None)
                 if key:
                     vals[key].append(float(r["Counter_Value"]))
@@ -411,8 +413,8 @@ def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):
     f_fac = copy_bytes / 1024.0 / fe["copy"]
     w_fac = copy_bytes / 1024.0 / wr["copy"]
     pre = (fe["prefill"] * f_fac + wr["prefill"] * w_fac) * 1024.0
-    dec_f = (fe["decode_partial"] + fe["decode_merge"]) * f_fac * 1024.0
-    dec_w = (wr["decode_partial"] + wr["decode_merge"]) * w_fac * 1024.0
+    dec_f = (fe["decode_main"] + fe["decode_merge"]) * f_fac * 1024.0
+    dec_w = (wr["decode_main"] + wr["decode_merge"]) * w_fac * 1024.0
     print("# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),")
     print("# each scaled by the factor that makes the copy kernel (torch.neg over 256 MiB float32,")
     print("# 256 MiB read + 256 MiB written) read its known size.")
@@ -422,8 +424,8 @@ def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):
     print(f"copy_write_kib_raw = {wr['copy']:.1f}")
     print(f"prefill_fetch_kib_raw = {fe['prefill']:.1f}")
     print(f"prefill_write_kib_raw = {wr['prefill']:.1f}")
-    print(f"decode_fetch_kib_raw = {fe['decode_partial']:.1f} + {fe['decode_merge']:.1f} (partial + merge)")
-    print(f"decode_write_kib_raw = {wr['decode_partial']:.1f} + {wr['decode_merge']:.1f} (partial + merge)")
+    print(f"decode_fetch_kib_raw = {fe['decode_main']:.1f} + {fe['decode_merge']:.1f} (decode + merge kernel, if any)")
+    print(f"decode_write_kib_raw = {wr['decode_main']:.1f} + {wr['decode_merge']:.1f} (decode + merge kernel, if any)")
     print(f"prefill_bytes = {pre:.0f}")
     print(f"decode_bytes = {dec_f + dec_w:.0f}")
     print(f"decode_read_bytes = {dec_f:.0f}")
