@@ -29,6 +29,8 @@
 //     operand of O^T = V^T P^T; V^T comes from row-major V in LDS through the
 //     gfx950 LDS transpose read.  The output accumulator therefore also has
 //     one query per lane, matching the softmax state.
+//   * K fragments are read from LDS kKPF MFMAs ahead of their use, the first
+//     ones before the softmax of the previous tile.
 //   * Tiles wholly outside a wave's admissible key range are skipped (causal
 //     and window early exit, per wave); masks are evaluated only on tiles that
 //     straddle a mask boundary.
@@ -130,6 +132,37 @@ __device__ __forceinline__ void qk_tile(const u32x4* Ks, const u32x4* qf, int ln
     const int c = 2 * s + g;
     sc[0] = E::mma32(Ks[ln * NC + (c ^ swz_k<D>(ln))], qf[s], sc[0]);
     sc[1] = E::mma32(Ks[(32 + ln) * NC + (c ^ swz_k<D>(32 + ln))], qf[s], sc[1]);
+  }
+}
+
+// One K fragment (A operand of S^T = K Q^T): fragment f = 2 s + kb is key
+// block kb (rows 32 kb .. + 31), contraction step s.
+template <typename T, int D>
+__device__ __forceinline__ u32x4 kfrag(const u32x4* Ks, int f, int ln, int g) {
+  constexpr int NC = D / 8;
+  const int row = 32 * (f & 1) + ln;
+  const int c = 2 * (f >> 1) + g;
+  return Ks[row * NC + (c ^ swz_k<D>(row))];
+}
+#ifndef ATTN_KPF
+#define ATTN_KPF 8
+#endif
+// K fragments kept in flight ahead of their MFMA: the first kKPF are read
+// before the softmax of the previous tile, so that their LDS latency hides
+// behind it (8 is 32 VGPRs; it fits the two-waves-per-SIMD budget at D = 128)
+constexpr int kKPF = ATTN_KPF;
+template <typename T, int D>
+__device__ __forceinline__ void qk_tile_pf(const u32x4* Ks, const u32x4* qf, int ln, int g,
+                                           u32x4 (&kf)[kKPF], floatx16 (&sc)[2]) {
+  using E = Elem<T>;
+  constexpr int NF = 2 * (D / 16);
+  sc[0] = floatx16{};
+  sc[1] = floatx16{};
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const u32x4 a = kf[f % kKPF];
+    if (f + kKPF < NF) kf[f % kKPF] = kfrag<T, D>(Ks, f + kKPF, ln, g);
+    sc[f & 1] = E::mma32(a, qf[f >> 1], sc[f & 1]);
   }
 }
 
@@ -458,6 +491,9 @@ void fwd_mfma_kernel(FwdArgs a) {
     }
     if (i + 2 < n) dma_k(kload, t + 2, ok_load);
     if (i + 1 < n) dma_v(vload, t + 1);
+    u32x4 kf[kKPF];
+#pragma unroll
+    for (int p = 0; p < kKPF; ++p) kf[p] = kfrag<T, D>(kread, p, ln, g);
     if (live(t))
       softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a, Sk, t * kBN, ip, ipa_w,
                               ipb_w, slope_l2, lane, g);
@@ -467,7 +503,7 @@ void fwd_mfma_kernel(FwdArgs a) {
     // over the one in its softmax (vector) phase.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
-    if (i + 1 < n && live(t + 1)) qk_tile<T, D>(kread, qf, ln, g, sc);
+    if (i + 1 < n && live(t + 1)) qk_tile_pf<T, D>(kread, qf, ln, g, kf, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     if (i + 1 < n && live(t + 1)) mask_bad(ok_read);
