@@ -168,8 +168,10 @@ def backward_flops(w) -> int:
 
 
 def extra_backward(torch, sdpa, W, dev, stream, launches=10):
-    """attn_bwd on the 2048-token causal GQA workload (the forward's row
-    statistics, dK/dV and dQ), timed on its own after the timed steps."""
+    """The backward on the 2048-token causal GQA workload, timed on its own
+    after the timed steps: attn_bwd (the forward's row statistics recomputed,
+    dK/dV, dQ) and attn_bwd_lse (row statistics from a saved forward's output
+    and LSE, then the same dK/dV and dQ)."""
     w = W.GQA_CAUSAL_2K
     q, k, v, _ = W.dense_inputs(w)
     do = W.random_dense(w.dtype, w.B, w.Hq, w.Hkv, w.Sq, 1, w.D, 4242, 1.0)[0]
@@ -179,26 +181,39 @@ def extra_backward(torch, sdpa, W, dev, stream, launches=10):
     p = sdpa.attn_fwd_params(tuple(q.shape), tuple(k.shape), q.dtype, softmax_scale=w.scale,
                              causal=True)
     ws = torch.empty(sdpa.attn_bwd_workspace_size(p), dtype=torch.uint8, device=dev)
+    t["out"], t["lse"] = sdpa.attn_fwd_lse(t["q"], t["k"], t["v"], None, softmax_scale=w.scale,
+                                           causal=True, stream=stream)
 
-    def run():
+    def recompute():
         sdpa.attn_bwd(t["q"], t["k"], t["v"], t["do"], None, softmax_scale=w.scale, causal=True,
                       dq=t["dq"], dk=t["dk"], dv=t["dv"], workspace=ws, stream=stream)
-    for _ in range(3):
-        run()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(launches):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) * 1e-3 / launches
-    tf = backward_flops(w) / sec / 1e12
-    return {w.name: {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype,
-                     "work_per_launch": backward_flops(w), "ms_per_launch": sec * 1e3,
-                     "launches": launches,
-                     "kernels": "forward statistics + bwd_dkdv_kernel + bwd_dq_kernel"}}
+
+    def saved():
+        sdpa.attn_bwd_lse(t["q"], t["k"], t["v"], t["out"], t["lse"], t["do"], None,
+                          softmax_scale=w.scale, causal=True, dq=t["dq"], dk=t["dk"], dv=t["dv"],
+                          workspace=ws, stream=stream)
+
+    out = {}
+    for label, run, kernels in (
+            (w.name, recompute, "forward statistics + bwd_dkdv_kernel + bwd_dq_kernel"),
+            (w.name + " (from the saved forward)", saved,
+             "bwd_rowstats_kernel + bwd_dkdv_kernel + bwd_dq_kernel")):
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(launches):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / launches
+        tf = backward_flops(w) / sec / 1e12
+        out[label] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype,
+                      "work_per_launch": backward_flops(w), "ms_per_launch": sec * 1e3,
+                      "launches": launches, "kernels": kernels}
+    return out
 
 
 def run_prefill(sdpa, wp, pre, stream):

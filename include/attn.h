@@ -292,6 +292,33 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        const float* alibi, void* dq, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, const attn_fwd_params_t* p, void* stream);
 
+/* Host-only validation of an attn_bwd_lse call (no HIP call is made): the
+ * rules of attn_bwd_check, and
+ *   out  [B, Hq, Sq, D] dtype    the output attn_fwd_lse returned for q, k, v,
+ *                                alibi and p;
+ *   lse  [B, Hq, Sq] float32     its natural-log LSE (-inf for a row without
+ *                                keys), 4-byte aligned;
+ * both required when B * Hq * Sq > 0, both read only, neither overlapping
+ * dq, dk, dv or the workspace. */
+attn_status_t attn_bwd_lse_check(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, const void* dout, const float* alibi,
+                                 const void* dq, const void* dk, const void* dv,
+                                 const void* workspace, size_t workspace_bytes,
+                                 const attn_fwd_params_t* p);
+
+/* The gradients of attn_bwd (kernel-contract page, attention_flash_backward)
+ * for a caller that kept the forward's output and LSE (attn_fwd_lse): S and P
+ * are still recomputed per key block as in attn_bwd, but the two per-row
+ * quantities that attn_bwd gets by re-running the forward -- the softmax
+ * normaliser and sum_j P dP = dO . O -- come from lse and from the rounded
+ * out, so that pass is skipped.  Same workspace, outputs and determinism as
+ * attn_bwd; the gradients agree with attn_bwd's to rounding (dO . O from the
+ * rounded output here, from the float32 accumulator there). */
+attn_status_t attn_bwd_lse(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, const float* alibi, void* dq,
+                           void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                           const attn_fwd_params_t* p, void* stream);
+
 /* Static string naming a status code. */
 const char* attn_status_str(attn_status_t status);
 

@@ -33,7 +33,7 @@ __all__ = [
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
     "attn_paged_params", "attn_status_str", "attn_version",
     "attn_paged_prefill", "attn_paged_prefill_check", "attn_varlen_params",
-    "attn_bwd", "attn_bwd_check", "attn_bwd_workspace_size",
+    "attn_bwd", "attn_bwd_check", "attn_bwd_workspace_size", "attn_bwd_lse", "attn_bwd_lse_check",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_F64",
 ]
 
@@ -124,6 +124,10 @@ def library():
     lib.attn_bwd_check.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [_VP] * 9 + [ctypes.c_size_t, fwd_p, _VP]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_lse_check.argtypes = [_VP] * 11 + [ctypes.c_size_t, fwd_p]
+    lib.attn_bwd_lse_check.restype = ctypes.c_int
+    lib.attn_bwd_lse.argtypes = [_VP] * 11 + [ctypes.c_size_t, fwd_p, _VP]
+    lib.attn_bwd_lse.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -282,6 +286,48 @@ def attn_bwd(q, k, v, dout, alibi=None, *, softmax_scale=None, causal=False, win
                       ctypes.byref(p), _stream_handle(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_lse_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, do_ptr, alibi_ptr, dq_ptr, dk_ptr,
+                       dv_ptr, ws_ptr, ws_bytes, params) -> int:
+    """Host-only validation of an attn_bwd_lse call on raw pointers (see attn.h)."""
+    return int(library().attn_bwd_lse_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, do_ptr, alibi_ptr,
+                                            dq_ptr, dk_ptr, dv_ptr, ws_ptr, ws_bytes,
+                                            None if params is None else ctypes.byref(params)))
+
+
+def attn_bwd_lse(q, k, v, out, lse, dout, alibi=None, *, softmax_scale=None, causal=False,
+                 window_left=None, window_right=None, softcap=None, dq=None, dk=None, dv=None,
+                 workspace=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` from a saved forward: ``out`` and ``lse`` are what
+    :func:`attn_fwd_lse` returned for the same inputs and options (see attn.h)."""
+    lib = library()
+    dev, _, p = _fwd_args(q, k, v, alibi, q, softmax_scale, causal, window_left,
+                          window_right, softcap)
+    for name, t in (("out", out), ("lse", lse), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv),
+                    ("workspace", workspace)):
+        _need_device(name, t, dev)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its input")
+    need = attn_bwd_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.attn_bwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(alibi),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), ctypes.byref(p),
+                          _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_lse")
     return dq, dk, dv
 
 

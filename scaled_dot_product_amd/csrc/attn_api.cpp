@@ -40,6 +40,20 @@ hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream) {
   return p.D == 128 ? launch_bwd_mfma_f16_d128(p, stream) : launch_bwd_mfma_f16_d64(p, stream);
 }
 
+hipError_t launch_bwd_rowstats_bf16_d128(const void*, const void*, const float*, float*, long long, hipStream_t);
+hipError_t launch_bwd_rowstats_bf16_d64(const void*, const void*, const float*, float*, long long, hipStream_t);
+hipError_t launch_bwd_rowstats_f16_d128(const void*, const void*, const float*, float*, long long, hipStream_t);
+hipError_t launch_bwd_rowstats_f16_d64(const void*, const void*, const float*, float*, long long, hipStream_t);
+
+hipError_t launch_bwd_rowstats(const void* out, const void* dout, const float* lse, float* stats,
+                               long long rows, int D, int dtype, hipStream_t stream) {
+  if (dtype == ATTN_BF16)
+    return D == 128 ? launch_bwd_rowstats_bf16_d128(out, dout, lse, stats, rows, stream)
+                    : launch_bwd_rowstats_bf16_d64(out, dout, lse, stats, rows, stream);
+  return D == 128 ? launch_bwd_rowstats_f16_d128(out, dout, lse, stats, rows, stream)
+                  : launch_bwd_rowstats_f16_d64(out, dout, lse, stats, rows, stream);
+}
+
 hipError_t launch_paged_prefill_bf16_d128(const PagedPrefillProblem& p, hipStream_t stream);
 hipError_t launch_paged_prefill_bf16_d64(const PagedPrefillProblem& p, hipStream_t stream);
 hipError_t launch_paged_prefill_f16_d128(const PagedPrefillProblem& p, hipStream_t stream);
@@ -292,18 +306,23 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
   return ATTN_OK;
 }
 
-attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* dout,
-                       const float* alibi, void* dq, void* dk, void* dv, void* workspace,
-                       size_t workspace_bytes, const attn_fwd_params_t* p, void* stream) {
-  const attn_status_t st =
-      attn_bwd_check(q, k, v, dout, alibi, dq, dk, dv, workspace, workspace_bytes, p);
-  if (st != ATTN_OK) return st;
+// The backward after validation: the row statistics into the workspace
+// (recomputed by the forward kernel, or from a saved forward's out and lse
+// when those are given), then dK/dV and dQ.
+static attn_status_t run_bwd(const void* q, const void* k, const void* v, const void* out,
+                             const float* lse, const void* dout, const float* alibi, void* dq,
+                             void* dk, void* dv, void* workspace, const attn_fwd_params_t* p,
+                             void* stream) {
   if (p->B == 0 || p->Hkv == 0) return ATTN_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const BwdLayout lay = bwd_layout(p);
   const int wl = lay.wl, wr = lay.wr;
-  // 1. the forward's row statistics (LSE, dO . O) into the workspace
-  if (p->Hq > 0 && p->Sq > 0) {
+  // 1. the row statistics (LSE, dO . O) into the workspace
+  if (p->Hq > 0 && p->Sq > 0 && out) {
+    if (attn::launch_bwd_rowstats(out, dout, lse, static_cast<float*>(workspace), p->B * p->Hq * p->Sq,
+                                  (int)p->D, p->dtype, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+  } else if (p->Hq > 0 && p->Sq > 0) {
     attn::FwdProblem fp;
     fp.q = q;
     fp.k = k;
@@ -354,6 +373,47 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                     ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.part_offset)
                     : nullptr;
   return attn::launch_bwd_mfma(bp, p->dtype, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                       const float* alibi, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, const attn_fwd_params_t* p, void* stream) {
+  const attn_status_t st =
+      attn_bwd_check(q, k, v, dout, alibi, dq, dk, dv, workspace, workspace_bytes, p);
+  if (st != ATTN_OK) return st;
+  return run_bwd(q, k, v, nullptr, nullptr, dout, alibi, dq, dk, dv, workspace, p, stream);
+}
+
+attn_status_t attn_bwd_lse_check(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, const void* dout, const float* alibi,
+                                 const void* dq, const void* dk, const void* dv,
+                                 const void* workspace, size_t workspace_bytes,
+                                 const attn_fwd_params_t* p) {
+  attn_status_t st = attn_bwd_check(q, k, v, dout, alibi, dq, dk, dv, workspace, workspace_bytes, p);
+  if (st != ATTN_OK) return st;
+  const int64_t rows = p->B * p->Hq * p->Sq;
+  const int64_t qb = rows * p->D * elem_bytes(p->dtype);
+  if (rows > 0 && (!out || !lse)) return ATTN_ERR_NULL;
+  if ((out && !aligned16(out)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3) != 0)) return ATTN_ERR_ALIGN;
+  // out and lse are read only: they may alias each other's inputs, never what is written
+  const Span ins[] = {{out, qb}, {lse, rows * 4}};
+  const int64_t kvb = p->B * p->Hkv * p->Sk * p->D * elem_bytes(p->dtype);
+  const Span outs[] = {{dq, qb}, {dk, kvb}, {dv, kvb}, {workspace, bwd_layout(p).total}};
+  for (const Span& x : ins)
+    for (const Span& o : outs)
+      if (overlaps(x, o)) return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd_lse(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, const float* alibi, void* dq,
+                           void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                           const attn_fwd_params_t* p, void* stream) {
+  const attn_status_t st = attn_bwd_lse_check(q, k, v, out, lse, dout, alibi, dq, dk, dv, workspace,
+                                              workspace_bytes, p);
+  if (st != ATTN_OK) return st;
+  return run_bwd(q, k, v, p->B * p->Hq * p->Sq > 0 ? out : nullptr, lse, dout, alibi, dq, dk, dv,
+                 workspace, p, stream);
 }
 
 size_t attn_paged_decode_workspace_size(const attn_paged_params_t* p) {

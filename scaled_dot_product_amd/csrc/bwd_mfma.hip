@@ -573,7 +573,47 @@ hipError_t launch_pair(const BwdArgs& a, int grid_kv, int grid_q, hipStream_t st
   return hipGetLastError();
 }
 
+// Row statistics of the backward from the forward's saved output and LSE:
+// stats[row] = (lse in log2 units, or +inf for a row without keys; dO . O).
+// D / 8 lanes per row, one 16-byte load of O and of dO each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_rowstats_kernel(const T* out, const T* dout, const float* lse,
+                                                           float2* stats, long long rows) {
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPW = 64 / LPR;    // rows per wave
+  const int lane = threadIdx.x & 63;
+  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int c = lane % LPR;
+  float part = 0.f;
+  if (row < rows) {
+    const u32x4 o = load16(out + row * D + 8 * c);
+    const u32x4 d = load16(dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t ho = (o[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const uint32_t hd = (d[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      part = __builtin_fmaf(Elem<T>::to_float(ho), Elem<T>::to_float(hd), part);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+  if (row < rows && c == 0) {
+    const float l = lse[row];
+    stats[row] = float2{l == kNegInf ? __builtin_inff() : l * kLog2e, part};
+  }
+}
+
 }  // namespace
+
+hipError_t ATTN_CAT(launch_bwd_rowstats_, ATTN_TAG)(const void* out, const void* dout, const float* lse,
+                                                    float* stats, long long rows, hipStream_t stream) {
+  constexpr int RPB = 4 * (64 / (ATTN_D / 8));  // rows per workgroup
+  const long long grid = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((bwd_rowstats_kernel<ATTN_ELEM, ATTN_D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const ATTN_ELEM*>(out), reinterpret_cast<const ATTN_ELEM*>(dout), lse,
+                     reinterpret_cast<float2*>(stats), rows);
+  return hipGetLastError();
+}
 
 hipError_t ATTN_CAT(launch_bwd_mfma_, ATTN_TAG)(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a;

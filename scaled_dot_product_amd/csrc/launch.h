@@ -134,5 +134,9 @@ hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream);
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream);
+// Backward row statistics (BwdProblem::stats) from a saved forward: out and
+// dout [rows, D] of the dtype, lse [rows] float32 natural-log LSE.
+hipError_t launch_bwd_rowstats(const void* out, const void* dout, const float* lse, float* stats,
+                               long long rows, int D, int dtype, hipStream_t stream);
 
 }  // namespace attn

@@ -317,3 +317,34 @@ def test_bwd_check_pointers_and_aliasing():
     assert check_bwd(p, dv=DK + 64) == ALIAS        # two outputs overlapping
     assert check_bwd(p, ws=DQ + 16) == ALIAS        # workspace over an output
     assert sdpa.attn_bwd_check(Q, K, V, DO, None, DQ, DK, DV, BWS, need, None) == NULL
+
+
+BO, BL = (0x100000000 * (i + 30) for i in range(2))   # saved forward output and LSE
+
+
+def check_bwd_lse(p, out=BO, lse=BL, ws_bytes=None, **kw):
+    if ws_bytes is None:
+        ws_bytes = sdpa.attn_bwd_workspace_size(p)
+    a = dict(q=Q, k=K, v=V, do=DO, al=None, dq=DQ, dk=DK, dv=DV, ws=BWS)
+    a.update(kw)
+    return sdpa.attn_bwd_lse_check(a["q"], a["k"], a["v"], out, lse, a["do"], a["al"], a["dq"],
+                                   a["dk"], a["dv"], a["ws"], ws_bytes, p)
+
+
+def test_bwd_lse_check():
+    p = fwd()
+    assert check_bwd_lse(p) == OK
+    assert check_bwd_lse(p, out=None) == NULL
+    assert check_bwd_lse(p, lse=None) == NULL
+    assert check_bwd_lse(fwd(Sq=0), out=None, lse=None, q=None, do=None, dq=None, ws=None,
+                         ws_bytes=0) == OK
+    assert check_bwd_lse(p, out=BO + 8) == ALIGN
+    assert check_bwd_lse(p, lse=BL + 2) == ALIGN
+    assert check_bwd_lse(p, out=DQ) == ALIAS         # the saved output under a gradient
+    assert check_bwd_lse(p, lse=BWS + 16) == ALIAS   # the LSE inside the workspace
+    assert check_bwd_lse(p, out=Q) == OK             # read-only inputs may share memory
+    # attn_bwd_check's rules come first
+    assert check_bwd_lse(fwd(dtype=sdpa.ATTN_F32)) == UNSUPPORTED
+    assert check_bwd_lse(p, do=None) == NULL
+    assert check_bwd_lse(p, ws_bytes=1) == WORKSPACE
+    assert sdpa.attn_bwd_lse_check(Q, K, V, BO, BL, DO, None, DQ, DK, DV, BWS, 1 << 30, None) == NULL

@@ -144,3 +144,99 @@ def test_bwd_gqa_causal_2k_workload(gpu_lib):
         compare_grad(dq[b:b + 1, hs], ref[0], w.dtype, f"{w.name} dq b{b} heads {hs}")
         compare_grad(dk[b:b + 1, g:g + 1], ref[1], w.dtype, f"{w.name} dk b{b} kv {g}")
         compare_grad(dv[b:b + 1, g:g + 1], ref[2], w.dtype, f"{w.name} dv b{b} kv {g}")
+
+
+def run_bwd_lse(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None, softcap=None,
+                alibi=False, amp=1.0, seed=0):
+    """attn_bwd_lse from attn_fwd_lse's saved output and LSE, against the oracle."""
+    name = (f"attn_bwd_lse {dtype} B{B} H{Hq}/{Hkv} Sq{Sq} Sk{Sk} D{D} causal={causal} "
+            f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
+    q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
+    do = W.random_dense(dtype, B, Hq, Hkv, Sq, 1, D, seed + 7919, 1.0)[0]
+    sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    announce(name)
+    kw = dict(softmax_scale=scale, causal=causal, window_left=wl, window_right=wr, softcap=softcap)
+    dsl = None if sl is None else sl.to(DEV)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = gpu_fwd_lse(sdpa, qd, kd, vd, dsl, kw)
+    dq, dk, dv = sdpa.attn_bwd_lse(qd, kd, vd, out, lse, dod, dsl, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do),
+                                   scale=scale, causal=causal, window_left=wl, window_right=wr,
+                                   softcap=softcap, alibi=None if sl is None else W.to_f64(sl))
+    for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        compare_grad(got, r, dtype, f"{name} {nm}")
+    return (qd, kd, vd, out, lse, dod, dsl, kw), (dq, dk, dv)
+
+
+def gpu_fwd_lse(sdpa, q, k, v, alibi, kw):
+    return sdpa.attn_fwd_lse(q, k, v, alibi, **kw)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_bwd_lse_parity(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = CASES[case]
+    run_bwd_lse(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=1700 + case, **kw)
+
+
+def test_bwd_lse_deterministic_and_close_to_recompute(gpu_lib):
+    """Reruns are bitwise equal; the gradients from the saved forward agree
+    with attn_bwd's (recomputed statistics) to a few units of rounding."""
+    args, first = run_bwd_lse(gpu_lib, "bf16", 1, 4, 2, 200, 333, 128, causal=True, seed=1900)
+    qd, kd, vd, out, lse, dod, dsl, kw = args
+    again = gpu_lib.attn_bwd_lse(qd, kd, vd, out, lse, dod, dsl, **kw)
+    rec = gpu_lib.attn_bwd(qd, kd, vd, dod, dsl, **kw)
+    torch.cuda.synchronize()
+    for a, b, r in zip(first, again, rec):
+        assert torch.equal(a, b)
+        rf = r.double().cpu().numpy()
+        compare_grad(a, rf, "bf16", "attn_bwd_lse vs attn_bwd")
+
+
+def test_bwd_lse_no_queries_or_keys(gpu_lib):
+    """Sq = 0: dk = dv = 0 (out and lse may be empty).  Sk = 0: dq = 0, every
+    row's LSE is -inf."""
+    q, k, v = W.random_dense("bf16", 1, 2, 2, 0, 70, 64, 3, 1.0)
+    announce("attn_bwd_lse Sq=0")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = gpu_lib.attn_fwd_lse(qd, kd, vd, None)
+    dk0 = torch.full_like(kd, 7.0)
+    dv0 = torch.full_like(vd, 7.0)
+    _, dk, dv = gpu_lib.attn_bwd_lse(qd, kd, vd, out, lse, torch.empty_like(qd), None, dk=dk0, dv=dv0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
+    q, k, v = W.random_dense("bf16", 1, 2, 2, 90, 0, 64, 4, 1.0)
+    announce("attn_bwd_lse Sk=0")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = gpu_lib.attn_fwd_lse(qd, kd, vd, None)
+    torch.cuda.synchronize()
+    assert torch.isinf(lse).all() and (lse < 0).all()
+    dq0 = torch.full_like(qd, 7.0)
+    dq, _, _ = gpu_lib.attn_bwd_lse(qd, kd, vd, out, lse, torch.ones_like(qd), None, dq=dq0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq).item() == 0
+
+
+def test_bwd_lse_gqa_causal_2k_workload(gpu_lib):
+    """The 2048-token causal GQA workload from its saved forward: dQ of one
+    group of query heads and dK/dV of their KV head against the oracle."""
+    w = W.GQA_CAUSAL_2K
+    q, k, v, _ = W.dense_inputs(w)
+    do = W.random_dense(w.dtype, w.B, w.Hq, w.Hkv, w.Sq, 1, w.D, 4243, 1.0)[0]
+    announce(f"attn_bwd_lse {w.name}")
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = gpu_lib.attn_fwd_lse(qd, kd, vd, None, softmax_scale=w.scale, causal=True)
+    dq, dk, dv = gpu_lib.attn_bwd_lse(qd, kd, vd, out, lse, dod, None, softmax_scale=w.scale,
+                                      causal=True)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    b, g = 0, 3
+    hs = slice(g * G, (g + 1) * G)
+    ref = oracle.sdpa_backward_f64(W.to_f64(q[b:b + 1, hs]), W.to_f64(k[b:b + 1, g:g + 1]),
+                                   W.to_f64(v[b:b + 1, g:g + 1]), W.to_f64(do[b:b + 1, hs]),
+                                   scale=w.scale, causal=True)
+    compare_grad(dq[b:b + 1, hs], ref[0], w.dtype, f"{w.name} dq b{b} heads {hs}")
+    compare_grad(dk[b:b + 1, g:g + 1], ref[1], w.dtype, f"{w.name} dk b{b} kv {g}")
+    compare_grad(dv[b:b + 1, g:g + 1], ref[2], w.dtype, f"{w.name} dv b{b} kv {g}")
