@@ -229,3 +229,43 @@ def test_decode_equals_dense_prefill_path(gpu_lib):
     ref = oracle.sdpa_naive_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale=D ** -0.5)
     compare(dec, ref, torch.bfloat16, "decode")
     compare(dense, ref, torch.bfloat16, "dense")
+
+
+def test_wide_batch_error_flag_and_determinism(gpu_lib):
+    """The fused form (256 groups): a block id outside the pool masks its keys
+    and sets the flag, a length beyond the table's capacity is clamped and
+    sets it, the other sequences are unaffected, and reruns are bitwise equal."""
+    B, Hq, Hkv, D, bs, maxb = 64, 8, 4, 128, 16, 20
+    w = W.Paged("ew", "bf16", B, Hq, Hkv, D, bs, 0, 0, 4, maxb, seed=77)
+    lens = wide_lens(B, 300, 78)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce("wide batch: valid call, rerun")
+    a = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag)
+    b = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag)
+    assert flag.item() == 0
+    assert torch.equal(a, b)
+    ref = oracle_decode(q, kp, vp, table, sl, scale=D ** -0.5)
+    compare(a, ref, torch.bfloat16, "wide batch")
+    victim = int(np.argmax(np.array(lens) > 2 * bs))       # a sequence with at least 3 blocks
+    bad = table.clone()
+    bad[victim, 1] = 10 ** 6                                # keys 16..31 of that sequence are masked
+    announce("wide batch: block id out of range")
+    out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag)
+    assert flag.item() == 1
+    assert torch.isfinite(out.float()).all()
+    others = [i for i in range(B) if i != victim]
+    compare(out[others], ref[others], torch.bfloat16, "wide batch, unaffected sequences")
+    n = lens[victim]
+    keep = [t for t in range(n) if not bs <= t < 2 * bs]
+    kb = oracle.paged_gather(W.to_f64(kp), table.numpy(), n, victim, bs)[keep]
+    vb = oracle.paged_gather(W.to_f64(vp), table.numpy(), n, victim, bs)[keep]
+    r1 = oracle.sdpa_naive_f64(W.to_f64(q[victim:victim + 1]), kb.transpose(1, 0, 2)[None],
+                               vb.transpose(1, 0, 2)[None], scale=D ** -0.5)
+    compare(out[victim:victim + 1], r1, torch.bfloat16, "wide batch, masked keys")
+    flag.zero_()
+    long = sl.clone()
+    long[3] = maxb * bs + 5
+    announce("wide batch: seq_len beyond capacity")
+    gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag)
+    assert flag.item() == 1

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 def test_graph_replay_matches_eager(gpu_lib):
     sdpa = gpu_lib
     dev = torch.device("cuda:0")
-    announce("graph capture: attn_fwd + attn_fwd_lse + attn_paged_decode")
+    announce("graph capture: attn_fwd + attn_fwd_lse + attn_paged_decode (split and fused forms)")
     q, k, v = W.random_dense("bf16", 1, 8, 2, 200, 300, 128, 41, 1.0)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(q)
@@ -31,6 +31,11 @@ def test_graph_replay_matches_eager(gpu_lib):
     dout = torch.empty_like(dq)
     p = sdpa.attn_paged_params(tuple(dq.shape), tuple(kp.shape), table.shape[1], dq.dtype, num_splits=8)
     ws = torch.zeros(sdpa.attn_paged_decode_workspace_size(p), dtype=torch.uint8, device=dev)
+    # a batch of 64 sequences x 4 KV heads = 256 groups: the fused persistent decode
+    ww = W.Paged("g", "bf16", 64, 8, 4, 128, 16, 1, 500, 8, 40, seed=43)
+    wq, wkp, wvp, wtab, wlens, _ = W.paged_inputs(ww)
+    wq, wkp, wvp, wtab, wlens = (t.to(dev) for t in (wq, wkp, wvp, wtab, wlens))
+    wout = torch.empty_like(wq)
     scale = 1.0 / np.sqrt(128)
 
     def work():
@@ -38,10 +43,11 @@ def test_graph_replay_matches_eager(gpu_lib):
         sdpa.attn_fwd_lse(q, k, v, None, out2, lse, softmax_scale=scale, causal=True, window_left=64)
         sdpa.attn_paged_decode(dq, kp, vp, table, lens, None, dout, softmax_scale=scale,
                                num_splits=8, workspace=ws)
+        sdpa.attn_paged_decode(wq, wkp, wvp, wtab, wlens, None, wout, softmax_scale=scale)
 
     work()
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (out, out2, lse, dout)]
+    eager = [t.clone() for t in (out, out2, lse, dout, wout)]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -54,10 +60,11 @@ def test_graph_replay_matches_eager(gpu_lib):
         work()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (out, out2, lse, dout):
+        for t in (out, out2, lse, dout, wout):
             t.fill_(7.0)                  # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, got, want in zip(("out", "out_lse", "lse", "decode"), (out, out2, lse, dout), eager):
+        for name, got, want in zip(("out", "out_lse", "lse", "decode", "decode_wide"),
+                                   (out, out2, lse, dout, wout), eager):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from eager"
