@@ -357,8 +357,9 @@ def profile(args):
 
 
 def profile_backward(args):
-    """Fixed launches of attn_bwd on the 2048-token causal GQA workload for
-    rocprofv3 (its three kernels: the forward's row statistics, dK/dV, dQ)."""
+    """Fixed launches on the 2048-token causal GQA workload for rocprofv3:
+    attn_bwd (the forward's row statistics, dK/dV, dQ), then one attn_fwd_lse
+    and attn_bwd_lse from its saved output (row statistics kernel, dK/dV, dQ)."""
     import torch
     import scaled_dot_product_amd as sdpa
     import workloads as W
@@ -370,6 +371,10 @@ def profile_backward(args):
     q, k, v, do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
     for _ in range(2 + args.launches):
         sdpa.attn_bwd(q, k, v, do, None, softmax_scale=w.scale, causal=True, stream=stream)
+    out, lse = sdpa.attn_fwd_lse(q, k, v, None, softmax_scale=w.scale, causal=True, stream=stream)
+    for _ in range(2 + args.launches):
+        sdpa.attn_bwd_lse(q, k, v, out, lse, do, None, softmax_scale=w.scale, causal=True,
+                          stream=stream)
     torch.cuda.synchronize()
     print(json.dumps({"profile_launches": args.launches, "backward_flops": backward_flops(w)}),
           flush=True)
