@@ -139,11 +139,15 @@ typedef struct attn_paged_params {
   int64_t B;                   /* sequences                                      */
   int64_t Hq;                  /* query heads; a multiple of Hkv                 */
   int64_t Hkv;                 /* key/value heads                                */
-  int64_t D;                   /* head dim: 64, 128 or 256                       */
+  int64_t D;                   /* head dim: 64, 128 or 256 (F16/BF16); 32, 64,
+                                  128 or 256 (F32/F64)                           */
   int64_t num_blocks;          /* physical blocks in each pool                   */
   int64_t block_size;          /* tokens per block (>= 1)                        */
   int64_t max_blocks_per_seq;  /* columns of block_table                         */
-  int32_t dtype;               /* attn_dtype_t of q, pools and out (F16, BF16)   */
+  int32_t dtype;               /* attn_dtype_t of q, pools and out: F16/BF16 on
+                                  the matrix cores, F32/F64 on the vector ALU
+                                  (one workgroup per (sequence, head); the
+                                  workspace is then not touched)                 */
   int32_t num_splits;          /* key-dimension splits per sequence, 1..256 (a
                                   tuning value: batches of at least one
                                   (sequence, KV head, 16-query-head chunk)
@@ -205,13 +209,15 @@ typedef struct attn_varlen_params {
   int64_t B;                   /* sequences                                      */
   int64_t Hq;                  /* query heads; a multiple of Hkv                 */
   int64_t Hkv;                 /* key/value heads                                */
-  int64_t D;                   /* head dim: 64, 128 or 256                       */
+  int64_t D;                   /* head dim: 64, 128 or 256 (F16/BF16); 32, 64,
+                                  128 or 256 (F32/F64)                           */
   int64_t total_q;             /* rows of q and out                              */
   int64_t max_seqlen_q;        /* >= cu_seqlens_q[b+1] - cu_seqlens_q[b] for all b */
   int64_t num_blocks;          /* physical blocks in each pool                   */
-  int64_t block_size;          /* tokens per block: a multiple of 64             */
+  int64_t block_size;          /* tokens per block: a multiple of 64 for F16/BF16,
+                                  any for F32/F64                                */
   int64_t max_blocks_per_seq;  /* columns of block_table                         */
-  int32_t dtype;               /* attn_dtype_t of q, pools and out (F16, BF16)   */
+  int32_t dtype;               /* attn_dtype_t of q, pools and out               */
   int32_t causal;              /* nonzero: key t admissible iff t <= i'          */
   int64_t window_left;         /* -1: unbounded; else keys t >= i' - window_left */
   int64_t window_right;        /* -1: unbounded; else keys t <= i' + window_right*/
@@ -230,8 +236,9 @@ typedef struct attn_varlen_params {
  *   alibi         [Hq] float32 or NULL (ALiBi distance t - i')
  *   out           [total_q, Hq, D] dtype
  *   error_flag    NULL or one device int32.
- * block_size must be a multiple of 64 (ATTN_ERR_UNSUPPORTED otherwise), as
- * must be F32 (ATTN_ERR_UNSUPPORTED). */
+ * For F16/BF16 (matrix cores) block_size must be a multiple of 64
+ * (ATTN_ERR_UNSUPPORTED otherwise); F32/F64 run on the vector ALU, computing
+ * in that type throughout, with any block size. */
 attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const void* v_pool,
                                        const int32_t* block_table, const int32_t* seq_lens,
                                        const int32_t* cu_seqlens_q, const float* alibi,

@@ -160,7 +160,7 @@ attn_status_t paged_shape(const attn_paged_params_t* p) {
     return ATTN_ERR_SHAPE;
   if (p->block_size < 1) return ATTN_ERR_SHAPE;
   if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
-  if (p->D != 64 && p->D != 128 && p->D != 256) return ATTN_ERR_HEAD_DIM;
+  if (!fwd_head_dim_ok(p->dtype, p->D)) return ATTN_ERR_HEAD_DIM;
   if (p->num_splits < 1 || p->num_splits > 256) return ATTN_ERR_PARAM;
   if (p->B > 65535 || p->Hq > 65535) return ATTN_ERR_SHAPE;
   const int64_t hchunks = (p->Hq / p->Hkv + 15) / 16;
@@ -429,7 +429,6 @@ attn_status_t attn_paged_decode_check(const void* q, const void* k_pool, const v
                                       const attn_paged_params_t* p) {
   if (!p) return ATTN_ERR_NULL;
   if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
-  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t st = paged_shape(p);
   if (st != ATTN_OK) return st;
   if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
@@ -469,6 +468,35 @@ attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v
                                                    out, workspace, workspace_bytes, error_flag, p);
   if (st != ATTN_OK) return st;
   if (p->B == 0 || p->Hq == 0) return ATTN_OK;
+  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) {
+    // vector-ALU path: the paged forward with one query per sequence at the
+    // sequence's last position (bottom-right causal admits every live key)
+    attn::PagedPrefillProblem pp;
+    pp.q = q;
+    pp.k_pool = k_pool;
+    pp.v_pool = v_pool;
+    pp.block_table = block_table;
+    pp.seq_lens = seq_lens;
+    pp.cu_seqlens_q = nullptr;
+    pp.alibi = alibi;
+    pp.out = out;
+    pp.error_flag = error_flag;
+    pp.B = (int)p->B;
+    pp.Hq = (int)p->Hq;
+    pp.Hkv = (int)p->Hkv;
+    pp.D = (int)p->D;
+    pp.total_q = (int)p->B;
+    pp.max_sq = 1;
+    pp.num_blocks = p->num_blocks > INT32_MAX ? INT32_MAX : (int)p->num_blocks;
+    pp.block_size = (int)p->block_size;
+    pp.max_blocks = (int)p->max_blocks_per_seq;
+    pp.causal = 1;
+    pp.wl = pp.wr = -1;
+    pp.scale = p->softmax_scale;
+    pp.softcap = p->softcap;
+    const hipError_t e = attn::launch_paged_valu(pp, p->dtype == ATTN_F64, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
   attn::DecodeProblem dp;
   dp.q = q;
   dp.k_pool = k_pool;
@@ -501,13 +529,13 @@ attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const 
                                        const attn_varlen_params_t* p) {
   if (!p) return ATTN_ERR_NULL;
   if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
-  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) return ATTN_ERR_UNSUPPORTED;
+  const bool valu = p->dtype == ATTN_F32 || p->dtype == ATTN_F64;
   if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->D < 0 || p->total_q < 0 || p->max_seqlen_q < 0 ||
       p->num_blocks < 0 || p->max_blocks_per_seq < 0 || p->block_size < 1)
     return ATTN_ERR_SHAPE;
   if (p->Hkv == 0 || p->Hq % p->Hkv != 0) return ATTN_ERR_GQA;
-  if (p->D != 64 && p->D != 128 && p->D != 256) return ATTN_ERR_HEAD_DIM;
-  if (p->block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!fwd_head_dim_ok(p->dtype, p->D)) return ATTN_ERR_HEAD_DIM;
+  if (!valu && p->block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;  // matrix-core path
   if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_PARAM;
   if (p->total_q > kMaxLen || p->max_seqlen_q > kMaxLen) return ATTN_ERR_SHAPE;
@@ -515,7 +543,8 @@ attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const 
   int64_t cap, bh, grid, q_bytes, pool_bytes;
   if (!mul(p->max_blocks_per_seq, p->block_size, &cap) || cap > kMaxLen) return ATTN_ERR_SHAPE;
   if (!mul(p->B, p->Hq, &bh) || bh > kMaxLen) return ATTN_ERR_SHAPE;
-  if (!mul(bh, (p->max_seqlen_q + 127) / 128, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
+  // query blocks of 128 rows (matrix cores) or at least 32 (vector ALU)
+  if (!mul(bh, (p->max_seqlen_q + 31) / 32, &grid) || grid > kMaxGrid) return ATTN_ERR_SHAPE;
   if (!mul4(p->total_q, p->Hq, p->D, es, &q_bytes)) return ATTN_ERR_SHAPE;
   if (!mul4(p->num_blocks, p->block_size, p->Hkv, p->D * es, &pool_bytes)) return ATTN_ERR_SHAPE;
   // one 64-key tile spans 64 token rows of the pool: its offsets must fit int32
@@ -578,7 +607,10 @@ attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* 
   pp.wr = (p->window_right < 0 || p->window_right >= p->max_seqlen_q) ? -1 : (int)p->window_right;
   pp.scale = p->softmax_scale;
   pp.softcap = p->softcap;
-  const hipError_t e = attn::launch_paged_prefill(pp, p->dtype, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      (p->dtype == ATTN_F32 || p->dtype == ATTN_F64)
+          ? attn::launch_paged_valu(pp, p->dtype == ATTN_F64, static_cast<hipStream_t>(stream))
+          : attn::launch_paged_prefill(pp, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

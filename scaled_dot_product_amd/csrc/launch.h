@@ -131,6 +131,9 @@ inline void bwd_chunking(int B, int Hkv, int Hq, int Sq, int Sk, int causal, int
 // 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
 hipError_t launch_fwd_mfma(const FwdProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream);
+// Vector-ALU paged forward (F32/F64): packed queries with a prefix sum, or,
+// with cu_seqlens_q == nullptr, one query per sequence (row b: decode).
+hipError_t launch_paged_valu(const PagedPrefillProblem& p, bool f64, hipStream_t stream);
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream);

@@ -190,11 +190,13 @@ def test_paged_check_accepts_valid_calls():
                              softcap=20.0), al=AL, err=ERR) == OK
     assert check_paged(paged(Hkv=32, num_splits=256)) == OK
     assert check_paged(paged(B=0), q=None, out=None, tab=None, lens=None, ws=None) == OK
+    # F32 / F64 (vector-ALU path): any block size, head dims 32 to 256
+    assert check_paged(paged(dtype=sdpa.ATTN_F32)) == OK
+    assert check_paged(paged(dtype=sdpa.ATTN_F64, D=32, block_size=7)) == OK
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=5), DTYPE), (dict(dtype=sdpa.ATTN_F32), UNSUPPORTED),
-    (dict(dtype=sdpa.ATTN_F64), UNSUPPORTED),
+    (dict(dtype=5), DTYPE), (dict(dtype=sdpa.ATTN_F64, D=80), HEAD_DIM),
     (dict(B=-1), SHAPE), (dict(block_size=0), SHAPE), (dict(B=70000), SHAPE),
     (dict(max_blocks_per_seq=1 << 30), SHAPE),
     (dict(Hkv=5), GQA), (dict(D=32), HEAD_DIM),
@@ -243,9 +245,10 @@ def check_varlen(p, **kw):
 def test_paged_prefill_check():
     assert check_varlen(varlen()) == OK
     assert check_varlen(varlen(block_size=128)) == OK
-    assert check_varlen(varlen(dtype=sdpa.ATTN_F32)) == UNSUPPORTED
-    assert check_varlen(varlen(dtype=sdpa.ATTN_F64)) == UNSUPPORTED
-    assert check_varlen(varlen(block_size=16)) == UNSUPPORTED
+    assert check_varlen(varlen(dtype=sdpa.ATTN_F32)) == OK
+    assert check_varlen(varlen(dtype=sdpa.ATTN_F64, block_size=16, D=32)) == OK  # vector-ALU path
+    assert check_varlen(varlen(dtype=sdpa.ATTN_F32, D=80)) == HEAD_DIM
+    assert check_varlen(varlen(block_size=16)) == UNSUPPORTED    # matrix cores: multiples of 64
     assert check_varlen(varlen(D=80)) == HEAD_DIM
     assert check_varlen(varlen(D=256)) == OK
     assert check_paged(paged(D=256)) == OK

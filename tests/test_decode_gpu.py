@@ -269,3 +269,60 @@ def test_wide_batch_error_flag_and_determinism(gpu_lib):
     announce("wide batch: seq_len beyond capacity")
     gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag)
     assert flag.item() == 1
+
+
+# F32 / F64: the vector-ALU paged kernel with one query per sequence
+VALU_DECODE = [
+    # dtype, B, Hq, Hkv, D, block_size, lens, softcap, alibi
+    ("f32", 4, 8, 2, 128, 16, [0, 1, 77, 300], None, False),
+    ("f64", 3, 4, 4, 64, 7, [50, 123, 13], 15.0, True),
+    ("f32", 2, 16, 1, 32, 64, [9, 400], None, True),
+    ("f64", 2, 6, 2, 256, 5, [40, 2], None, False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(VALU_DECODE)))
+def test_paged_decode_valu_parity(gpu_lib, case):
+    dtype, B, Hq, Hkv, D, bs, lens, cap, use_alibi = VALU_DECODE[case]
+    maxb = max((max(lens) + bs - 1) // bs, 1) + 1
+    w = W.Paged("v", "f32", B, Hq, Hkv, D, bs, 0, 0, 4, maxb, seed=260 + case)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    if dtype == "f64":
+        q, kp, vp = q.double(), kp.double(), vp.double()
+    alibi = torch.from_numpy(W.alibi_slopes(Hq)) if use_alibi else None
+    scale = float(np.float32(D ** -0.5))
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce(f"paged decode vector-ALU case {case}: {VALU_DECODE[case]}")
+    out = gpu_decode(gpu_lib, q, kp, vp, table, sl, alibi, softmax_scale=scale, softcap=cap,
+                     error_flag=flag)
+    assert flag.item() == 0
+    ref = oracle_decode(q, kp, vp, table, sl, alibi, scale=scale, softcap=cap)
+    compare(out, ref, {"f32": torch.float32, "f64": torch.float64}[dtype], f"valu decode {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
+def test_paged_decode_valu_error_flag(gpu_lib):
+    w = W.Paged("ve", "f32", 3, 8, 2, 64, 16, 0, 0, 4, 8, seed=9)
+    lens = [40, 100, 33]
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad = table.clone()
+    bad[1, 2] = 10 ** 6                      # keys 32..47 of sequence 1 are masked
+    announce("paged decode vector-ALU: block id out of range")
+    out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag, softmax_scale=0.125)
+    assert flag.item() == 1
+    ref = oracle_decode(q, kp, vp, table, sl, scale=0.125)
+    compare(out[[0, 2]], ref[[0, 2]], torch.float32, "valu decode, unaffected sequences")
+    keep = [t for t in range(100) if not 32 <= t < 48]
+    kb = oracle.paged_gather(W.to_f64(kp), table.numpy(), 100, 1, 16)[keep]
+    vb = oracle.paged_gather(W.to_f64(vp), table.numpy(), 100, 1, 16)[keep]
+    r1 = oracle.sdpa_naive_f64(W.to_f64(q[1:2]), kb.transpose(1, 0, 2)[None],
+                               vb.transpose(1, 0, 2)[None], scale=0.125)
+    compare(out[1:2], r1, torch.float32, "valu decode, masked keys")
+    flag.zero_()
+    long = sl.clone()
+    long[2] = 8 * 16 + 5                     # beyond the table's capacity: clamped
+    gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag)
+    assert flag.item() == 1

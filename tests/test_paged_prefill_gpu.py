@@ -13,7 +13,12 @@ from gpu_util import announce, compare
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "f64": torch.float64}
+
+
+def cast(x, dtype):
+    """float32 draws in the test dtype (float64: the exact float32 values)."""
+    return W.cast(x, "f32").double() if dtype == "f64" else W.cast(x, dtype)
 DEV = torch.device("cuda:0")
 
 
@@ -31,9 +36,9 @@ def make_case(dtype, sq, sk, Hq, Hkv, D, bs, seed, amp=1.0):
         pos += n
     cu = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
     tq = int(cu[-1])
-    q = W.cast(rng.standard_normal((tq, Hq, D), dtype=np.float32) * np.float32(amp), dtype)
-    kp = W.cast(rng.standard_normal((nb, bs, Hkv, D), dtype=np.float32) * np.float32(amp), dtype)
-    vp = W.cast(rng.standard_normal((nb, bs, Hkv, D), dtype=np.float32), dtype)
+    q = cast(rng.standard_normal((tq, Hq, D), dtype=np.float32) * np.float32(amp), dtype)
+    kp = cast(rng.standard_normal((nb, bs, Hkv, D), dtype=np.float32) * np.float32(amp), dtype)
+    vp = cast(rng.standard_normal((nb, bs, Hkv, D), dtype=np.float32), dtype)
     return dict(q=q, kp=kp, vp=vp, table=torch.from_numpy(table),
                 lens=torch.from_numpy(np.asarray(sk, dtype=np.int32)), cu=torch.from_numpy(cu))
 
@@ -182,3 +187,48 @@ def test_error_flag_and_masking(gpu_lib):
     err.zero_()
     gpu_run(gpu_lib, c, err=err, scale=0.088, max_sq=50)
     assert err.item() == 1
+
+
+# F32 / F64: the vector-ALU paged kernel (any block size, head dims 32 to 256)
+VALU_CASES = [
+    # (sq per sequence, sk per sequence, Hq, Hkv, bs, kwargs)
+    ((70, 1, 33, 0), (70, 200, 120, 30), 4, 2, 16, dict()),
+    ((50, 20), (300, 20), 4, 1, 7, dict(wl=40, wr=0)),
+    ((40, 61), (20, 90), 2, 2, 64, dict(softcap=30.0, alibi=True, amp=1.5)),   # Sk < Sq: early rows empty
+    ((33, 45), (33, 100), 2, 1, 5, dict(causal=False, wl=10, wr=3)),
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 128), ("f64", 64), ("f32", 32), ("f64", 256)])
+@pytest.mark.parametrize("case", range(len(VALU_CASES)))
+def test_paged_prefill_valu_parity(gpu_lib, dtype, D, case):
+    sq, sk, Hq, Hkv, bs, kw = VALU_CASES[case]
+    kw = dict(kw)
+    amp = kw.pop("amp", 1.0)
+    c = make_case(dtype, sq, sk, Hq, Hkv, D, bs, 540 + case, amp)
+    kw["scale"] = float(np.float32(1.0 / math.sqrt(D)))
+    if kw.pop("alibi", False):
+        kw["alibi"] = torch.from_numpy(W.alibi_slopes(Hq))
+    name = f"attn_paged_prefill {dtype} D{D} sq={sq} sk={sk} H{Hq}/{Hkv} bs{bs} {sorted(kw)}"
+    announce(name)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = gpu_run(gpu_lib, c, err=err, **kw)
+    assert err.item() == 0, f"{name}: error flag set"
+    compare(got, oracle_run(c, **kw), DT[dtype], name)
+
+
+def test_paged_prefill_valu_error_flag(gpu_lib):
+    """Vector-ALU path: a block id outside the pool masks its keys and sets the
+    flag; the other sequence is unaffected."""
+    c = make_case("f32", (40, 30), (100, 60), 4, 2, 64, 16, 77)
+    kw = dict(scale=0.125)
+    ref = oracle_run(c, **kw)
+    bad = c["table"].clone()
+    bad[0, 2] = 10 ** 6                          # keys 32..47 of sequence 0
+    c2 = dict(c, table=bad)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce("attn_paged_prefill f32: block id out of range")
+    got = gpu_run(gpu_lib, c2, err=err, **kw)
+    assert err.item() == 1
+    assert torch.isfinite(got).all()
+    compare(got[40:], ref[40:], torch.float32, "f32 paged prefill, unaffected sequence")
