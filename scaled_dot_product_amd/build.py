@@ -35,7 +35,8 @@ KERNEL_FLAGS = ["-fno-honor-nans"]
 # (source, extra flags, object)
 UNITS = [("attn_api.cpp", [], "attn_api.o"),
          ("fwd_f32.hip", KERNEL_FLAGS, "fwd_f32.o"),
-         ("decode.hip", KERNEL_FLAGS, "decode.o")]
+         ("decode.hip", KERNEL_FLAGS, "decode.o"),
+         ("bwd_valu.hip", KERNEL_FLAGS, "bwd_valu.o")]
 for _elem, _tag in (("__bf16", "bf16"), ("_Float16", "f16")):
     for _d in (128, 64, 256):
         for _src in ("fwd_mfma", "bwd_mfma") if _d <= 128 else ("fwd_mfma",):

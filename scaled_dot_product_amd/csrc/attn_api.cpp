@@ -258,9 +258,16 @@ static BwdLayout bwd_layout(const attn_fwd_params_t* p) {
   BwdLayout L;
   L.wl = (p->window_left < 0 || p->window_left >= p->Sk) ? -1 : (int)p->window_left;
   L.wr = (p->window_right < 0 || p->window_right >= p->Sq) ? -1 : (int)p->window_right;
-  attn::bwd_chunking((int)p->B, (int)p->Hkv, (int)p->Hq, (int)p->Sq, (int)p->Sk, p->causal != 0,
-                     L.wl, L.wr, &L.chunk_items, &L.max_chunks);
-  L.stats_bytes = p->B * p->Hq * p->Sq * 8;
+  const bool valu = p->dtype == ATTN_F32 || p->dtype == ATTN_F64;
+  if (valu) {
+    L.chunk_items = 1;
+    L.max_chunks = 1;
+  } else {
+    attn::bwd_chunking((int)p->B, (int)p->Hkv, (int)p->Hq, (int)p->Sq, (int)p->Sk, p->causal != 0,
+                       L.wl, L.wr, &L.chunk_items, &L.max_chunks);
+  }
+  // per query row: two floats (matrix cores) or two values of the element type
+  L.stats_bytes = p->B * p->Hq * p->Sq * (valu ? 2 * elem_bytes(p->dtype) : 8);
   L.part_offset = (L.stats_bytes + 255) / 256 * 256;
   const int64_t nkb = (p->Sk + 127) / 128;
   L.part_bytes = L.max_chunks > 1 ? p->B * p->Hkv * nkb * L.max_chunks * 2 * 128 * p->D * 4 : 0;
@@ -281,11 +288,11 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
                              const attn_fwd_params_t* p) {
   if (!p) return ATTN_ERR_NULL;
   if (!valid_dtype(p->dtype)) return ATTN_ERR_DTYPE;
-  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) return ATTN_ERR_UNSUPPORTED;
   // q, k, v, alibi and the parameters as for the forward, with dq in out's place
   attn_status_t st = check_fwd(q, k, v, alibi, dq, p);
   if (st != ATTN_OK) return st;
-  if (p->D > 128) return ATTN_ERR_HEAD_DIM;  // the backward is built for 64 and 128
+  const bool valu = p->dtype == ATTN_F32 || p->dtype == ATTN_F64;
+  if (!valu && p->D > 128) return ATTN_ERR_HEAD_DIM;  // the matrix-core backward: 64 and 128
   int64_t qb, kvb;
   fwd_shape(p, &qb, &kvb);
   if (qb > 0 && !dout) return ATTN_ERR_NULL;
@@ -317,6 +324,32 @@ static attn_status_t run_bwd(const void* q, const void* k, const void* v, const 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const BwdLayout lay = bwd_layout(p);
   const int wl = lay.wl, wr = lay.wr;
+  if (p->dtype == ATTN_F32 || p->dtype == ATTN_F64) {
+    // vector-ALU path: recomputes the row statistics itself (a saved out and
+    // lse are not read)
+    attn::BwdProblem bp = {};
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.dout = dout;
+    bp.alibi = alibi;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.B = (int)p->B;
+    bp.Hq = (int)p->Hq;
+    bp.Hkv = (int)p->Hkv;
+    bp.Sq = (int)p->Sq;
+    bp.Sk = (int)p->Sk;
+    bp.D = (int)p->D;
+    bp.causal = p->causal != 0;
+    bp.wl = wl;
+    bp.wr = wr;
+    bp.scale = p->softmax_scale;
+    bp.softcap = p->softcap;
+    return attn::launch_bwd_valu(bp, p->dtype == ATTN_F64, workspace, s) == hipSuccess ? ATTN_OK
+                                                                                     : ATTN_ERR_HIP;
+  }
   // 1. the row statistics (LSE, dO . O) into the workspace
   if (p->Hq > 0 && p->Sq > 0 && out) {
     if (attn::launch_bwd_rowstats(out, dout, lse, static_cast<float*>(workspace), p->B * p->Hq * p->Sq,

@@ -137,6 +137,9 @@ hipError_t launch_paged_valu(const PagedPrefillProblem& p, bool f64, hipStream_t
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream);
+// Vector-ALU backward (F32/F64): `stats` holds two values of the element type
+// per query row; the chunking fields of p are not used.
+hipError_t launch_bwd_valu(const BwdProblem& p, bool f64, void* stats, hipStream_t stream);
 // Backward row statistics (BwdProblem::stats) from a saved forward: out and
 // dout [rows, D] of the dtype, lse [rows] float32 natural-log LSE.
 hipError_t launch_bwd_rowstats(const void* out, const void* dout, const float* lse, float* stats,

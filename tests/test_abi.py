@@ -286,6 +286,10 @@ def test_bwd_check_accepts_valid_calls():
     assert check_bwd(fwd(D=64, dtype=sdpa.ATTN_F16, causal=0, window_left=5, window_right=0,
                          softcap=30.0), al=AL) == OK
     assert check_bwd(fwd(Sq=0), q=None, do=None, dq=None, ws=None, ws_bytes=0) == OK
+    # F32 / F64 (vector-ALU backward): head dims 32 to 256
+    assert check_bwd(fwd(dtype=sdpa.ATTN_F32)) == OK
+    assert check_bwd(fwd(dtype=sdpa.ATTN_F64, D=256)) == OK
+    assert check_bwd(fwd(dtype=sdpa.ATTN_F64, D=32)) == OK
 
 
 def test_bwd_workspace_size():
@@ -293,11 +297,13 @@ def test_bwd_workspace_size():
     # the forward's row statistics: 8 bytes per query row, at least
     assert sdpa.attn_bwd_workspace_size(p) >= 2 * 8 * 100 * 8
     assert sdpa.attn_bwd_workspace_size(fwd(D=80)) == 0
+    # F64: two float64 values per query row, no partials
+    assert sdpa.attn_bwd_workspace_size(fwd(B=2, Hq=8, Hkv=2, Sq=100, Sk=130, dtype=sdpa.ATTN_F64)) == 2 * 8 * 100 * 16
     assert sdpa.attn_bwd_workspace_size(None) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=sdpa.ATTN_F32), UNSUPPORTED), (dict(dtype=sdpa.ATTN_F64), UNSUPPORTED),
+    (dict(dtype=sdpa.ATTN_F64, D=80), HEAD_DIM),
     (dict(dtype=9), DTYPE), (dict(D=256), HEAD_DIM), (dict(Hkv=3), GQA),
     (dict(softcap=-1.0), PARAM),
 ])
@@ -347,7 +353,7 @@ def test_bwd_lse_check():
     assert check_bwd_lse(p, lse=BWS + 16) == ALIAS   # the LSE inside the workspace
     assert check_bwd_lse(p, out=Q) == OK             # read-only inputs may share memory
     # attn_bwd_check's rules come first
-    assert check_bwd_lse(fwd(dtype=sdpa.ATTN_F32)) == UNSUPPORTED
+    assert check_bwd_lse(fwd(dtype=sdpa.ATTN_F32)) == OK
     assert check_bwd_lse(p, do=None) == NULL
     assert check_bwd_lse(p, ws_bytes=1) == WORKSPACE
     assert sdpa.attn_bwd_lse_check(Q, K, V, BO, BL, DO, None, DQ, DK, DV, BWS, 1 << 30, None) == NULL

@@ -240,3 +240,66 @@ def test_bwd_lse_gqa_causal_2k_workload(gpu_lib):
     compare_grad(dq[b:b + 1, hs], ref[0], w.dtype, f"{w.name} dq b{b} heads {hs}")
     compare_grad(dk[b:b + 1, g:g + 1], ref[1], w.dtype, f"{w.name} dk b{b} kv {g}")
     compare_grad(dv[b:b + 1, g:g + 1], ref[2], w.dtype, f"{w.name} dv b{b} kv {g}")
+
+
+# F32 / F64: the vector-ALU backward, computing in the element type throughout.
+# Bar: each gradient element is a sum of up to Sk (or group * Sq) products
+# formed and accumulated in the element type, so its error is a modest multiple
+# of that type's unit roundoff times the magnitudes involved: tensor rel-L2 at
+# most 1e-5 (f32) / 1e-12 (f64), and every element within 1e-4 / 1e-10 of the
+# tensor's largest element.
+VALU_BAR = {"f32": (1e-5, 1e-4), "f64": (1e-12, 1e-10)}
+
+
+def compare_grad_valu(got, ref, dtype, what):
+    g = got.detach().to("cpu", torch.float64).numpy()
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    rel_bar, el_bar = VALU_BAR[dtype]
+    err = np.abs(g - ref)
+    scale = np.abs(ref).max(initial=0.0)
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(g - ref) / nref if nref > 0 else np.linalg.norm(g)
+    announce(f"{what}: rel L2 {rel:.3g}, max err {err.max(initial=0):.3g} of max |ref| {scale:.3g}")
+    assert rel <= rel_bar, f"{what}: relative L2 {rel:.3g} > {rel_bar}"
+    assert err.max(initial=0.0) <= el_bar * scale + 1e-300, f"{what}: max err {err.max():.3g}"
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 128), ("f64", 64), ("f32", 32), ("f64", 256)])
+@pytest.mark.parametrize("case", [0, 1, 2, 3, 4, 5])
+def test_bwd_valu_parity(gpu_lib, dtype, D, case):
+    B, Hq, Hkv, Sq, Sk, kw = CASES[case]
+    kw = dict(kw)
+    q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, 2700 + case, kw.pop("amp", 1.0))
+    do = W.random_dense(dtype, B, Hq, Hkv, Sq, 1, D, 2800 + case, 1.0)[0]
+    sl = torch.from_numpy(W.alibi_slopes(Hq)) if kw.pop("alibi", False) else None
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    opts = dict(causal=kw.get("causal", False), window_left=kw.get("wl"),
+                window_right=kw.get("wr"), softcap=kw.get("softcap"))
+    name = f"attn_bwd {dtype} D{D} case {case} {CASES[case]}"
+    announce(name)
+    dq, dk, dv = gpu_lib.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV),
+                                  None if sl is None else sl.to(DEV), softmax_scale=scale, **opts)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), scale=scale,
+                                   causal=opts["causal"], window_left=opts["window_left"],
+                                   window_right=opts["window_right"], softcap=opts["softcap"],
+                                   alibi=None if sl is None else W.to_f64(sl))
+    for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        compare_grad_valu(got, r, dtype, f"{name} {nm}")
+
+
+def test_bwd_valu_deterministic_and_saved_forward(gpu_lib):
+    """F64: reruns are bitwise equal, and attn_bwd_lse (whose saved output and
+    LSE the vector-ALU path does not need) gives the same gradients."""
+    q, k, v = W.random_dense("f64", 1, 4, 2, 90, 130, 64, 2900, 1.0)
+    do = W.random_dense("f64", 1, 4, 2, 90, 1, 64, 2901, 1.0)[0]
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    announce("attn_bwd f64 determinism")
+    a = gpu_lib.attn_bwd(qd, kd, vd, dod, None, causal=True)
+    b = gpu_lib.attn_bwd(qd, kd, vd, dod, None, causal=True)
+    out, lse = gpu_lib.attn_fwd_lse(qd, kd, vd, None, causal=True)
+    c = gpu_lib.attn_bwd_lse(qd, kd, vd, out, lse, dod, None, causal=True)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y) and torch.equal(x, z)
