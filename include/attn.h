@@ -267,14 +267,16 @@ attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* 
  * P (times 1 - tanh^2(s_pre / softcap) with a softcap), dQ = scale dS K and
  * dK = scale dS^T Q.  dk and dv are [B, Hkv, Sk, D], summed over the query
  * heads of each KV head's group; dq is [B, Hq, Sq, D].  A row with no
- * admissible key contributes nothing.  F16/BF16 and head dims 64/128 only
- * (matrix cores, float32 accumulation, P and dS rounded to the input dtype
- * as matmul operands); F32/F64 give ATTN_ERR_UNSUPPORTED.  Deterministic: no atomics, fixed
+ * admissible key contributes nothing.  F16/BF16 with head dims 64/128 run on
+ * the matrix cores (float32 accumulation, P and dS rounded to the input dtype
+ * as matmul operands); F32/F64 with head dims 32 to 256 on the vector ALU,
+ * computing in that type throughout.  Deterministic: no atomics, fixed
  * order. */
 
-/* Workspace bytes attn_bwd needs for p, 0 for an invalid p: 8 * B * Hq * Sq
- * for the forward's row statistics, plus float32 partial dK/dV when the
- * key blocks' work is split (the split depends only on p). */
+/* Workspace bytes attn_bwd needs for p, 0 for an invalid p: for F16/BF16,
+ * 8 * B * Hq * Sq for the forward's row statistics plus float32 partial
+ * dK/dV when the key blocks' work is split (the split depends only on p);
+ * for F32/F64, two values of the element type per query row. */
 size_t attn_bwd_workspace_size(const attn_fwd_params_t* p);
 
 /* Host-only validation of an attn_bwd call (no HIP call is made).
@@ -320,7 +322,9 @@ attn_status_t attn_bwd_lse_check(const void* q, const void* k, const void* v, co
  * normaliser and sum_j P dP = dO . O -- come from lse and from the rounded
  * out, so that pass is skipped.  Same workspace, outputs and determinism as
  * attn_bwd; the gradients agree with attn_bwd's to rounding (dO . O from the
- * rounded output here, from the float32 accumulator there). */
+ * rounded output here, from the float32 accumulator there).  F32/F64
+ * recompute the statistics in the element type as attn_bwd does (out and
+ * lse are validated but not read), so their gradients equal attn_bwd's. */
 attn_status_t attn_bwd_lse(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, const float* alibi, void* dq,
                            void* dk, void* dv, void* workspace, size_t workspace_bytes,
