@@ -473,7 +473,7 @@ def main():
         return traffic(*args.traffic)
     if args.gpus != 1:
         sys.exit(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the attention "
-                 "kernels here are single-GPU, and multi-GPU sharding is not part of this build")
+                 "kernels here run on one GPU and the library has no multi-GPU path")
     if args.mode == "profile":
         return profile(args)
     if args.mode == "profile_backward":
