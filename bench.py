@@ -435,6 +435,12 @@ def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):
     pre = (fe["prefill"] * f_fac + wr["prefill"] * w_fac) * 1024.0
     dec_f = (fe["decode_main"] + fe["decode_merge"]) * f_fac * 1024.0
     dec_w = (wr["decode_main"] + wr["decode_merge"]) * w_fac * 1024.0
+    print("# commands (from the repository root, on one MI355X; $REPO is the repository root; "
+          "cd /tmp && export TMPDIR=/tmp first):")
+    for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        print(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $REPO/{os.path.basename(d.rstrip('/'))} "
+              "-- python $REPO/bench.py --mode profile")
+    print(f"#   python bench.py --traffic {fetch_dir} {write_dir} > profiles/hbm_traffic.txt")
     print("# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),")
     print("# each scaled by the factor that makes the copy kernel (torch.neg over 256 MiB float32,")
     print("# 256 MiB read + 256 MiB written) read its known size.")
