@@ -440,7 +440,8 @@ def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):
     for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         print(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $REPO/{os.path.basename(d.rstrip('/'))} "
               "-- python $REPO/bench.py --mode profile")
-    print(f"#   python bench.py --traffic {fetch_dir} {write_dir} > profiles/hbm_traffic.txt")
+    names = [os.path.basename(d.rstrip("/")) for d in (fetch_dir, write_dir)]
+    print(f"#   python bench.py --traffic $REPO/{names[0]} $REPO/{names[1]} > profiles/hbm_traffic.txt")
     print("# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),")
     print("# each scaled by the factor that makes the copy kernel (torch.neg over 256 MiB float32,")
     print("# 256 MiB read + 256 MiB written) read its known size.")
