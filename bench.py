@@ -380,6 +380,73 @@ def profile_backward(args):
           flush=True)
 
 
+PREFILL_CONFIGS = ("GQA_CAUSAL_2K", "LONG_MASKED_8K", "CHUNKED_PREFILL")
+
+
+def profile_prefill(args):
+    """Fixed launches of the three prefill workloads, one after the other
+    (the 2048-token causal GQA one, the long masked 8192-token one, chunked
+    f16 prefill), for the MFMA-utilisation counter pass."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for name in PREFILL_CONFIGS:
+        w = getattr(W, name)
+        q, k, v, alibi = W.dense_inputs(w)
+        t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
+        t["out"] = torch.empty_like(t["q"])
+        al = alibi.to(dev) if alibi is not None else None
+        for _ in range(2 + args.launches):
+            run_dense(sdpa, w, t, al, stream)
+        torch.cuda.synchronize()
+        del t
+    print(json.dumps({"profile_launches": args.launches, "workloads": list(PREFILL_CONFIGS)}), flush=True)
+
+
+def mfma_util(path):
+    """MFMA utilisation of each prefill launch class from a rocprofv3 counter
+    run of --mode profile_prefill with SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES
+    and GRBM_GUI_ACTIVE: busy cycles per SIMD over the kernel's GPU cycles (per
+    XCD), and the clock the GPU ran at (GPU cycles over the dispatch time)."""
+    import workloads as W
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no rocprofv3 counter output under {path}")
+    rows = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if "fwd_mfma_kernel" not in r["Kernel_Name"]:
+                    continue
+                d = rows.setdefault(int(r["Dispatch_Id"]), {"t": (int(r["End_Timestamp"]) -
+                                                                  int(r["Start_Timestamp"])) * 1e-9})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted(rows)
+    per = len(ids) // len(PREFILL_CONFIGS)
+    simds, xcds = 1024, 8
+    print("# commands (from the repository root, on one MI355X; $REPO is the repository root; "
+          "cd /tmp && export TMPDIR=/tmp first):")
+    print(f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+          f"-d $REPO/{os.path.basename(path.rstrip('/'))} -- python $REPO/bench.py --mode profile_prefill")
+    print(f"#   python bench.py --mfma-util $REPO/{os.path.basename(path.rstrip('/'))} "
+          "> profiles/mfma_util_prefill.txt")
+    print("# MFMA utilisation per prefill workload (rocprofv3 counters, one pass; the first 2 launches of "
+          "each workload are warm-up and skipped)")
+    print("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs); "
+          "clock = GPU cycles per XCD / dispatch time")
+    for i, name in enumerate(PREFILL_CONFIGS):
+        w = getattr(W, name)
+        sel = [rows[k] for k in ids[i * per:(i + 1) * per]][2:]
+        busy = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) for d in sel) / simds
+        gpu = sum(d.get("GRBM_GUI_ACTIVE", 0) for d in sel) / xcds
+        t = sum(d["t"] for d in sel)
+        flops = prefill_flops(w) * len(sel)
+        print(f"{w.name}: launches={len(sel)} mfma_busy={busy / gpu:.3f} clock_ghz={gpu / t / 1e9:.2f} "
+              f"avg_us={t / len(sel) * 1e6:.1f} tflops={flops / t / 1e12:.1f}")
+
+
 def summarize(path):
     """Print the per-kernel duration table of a rocprofv3 kernel-trace run
     (its SQLite database, or the CSV stats when it wrote those)."""
@@ -465,7 +532,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=["bench", "profile", "profile_backward"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "profile", "profile_backward", "profile_prefill"],
+                    default="bench")
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
@@ -473,11 +541,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--mfma-util", metavar="DIR")
     args = ap.parse_args()
     if args.summarize:
         return summarize(args.summarize)
     if args.traffic:
         return traffic(*args.traffic)
+    if args.mfma_util:
+        return mfma_util(args.mfma_util)
     if args.gpus != 1:
         sys.exit(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the attention "
                  "kernels here run on one GPU and the library has no multi-GPU path")
@@ -485,6 +556,8 @@ def main():
         return profile(args)
     if args.mode == "profile_backward":
         return profile_backward(args)
+    if args.mode == "profile_prefill":
+        return profile_prefill(args)
     return bench(args)
 
 
