@@ -533,7 +533,9 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
 
   Item cur, nxt;
   bool have = item_of(0, cur);
-  bool have_nxt = have && item_of(1, nxt);
+  // the fused form ends every item with two barriers: it loads an item's Q
+  // and page ids when it starts it; the split form loads them one item ahead
+  bool have_nxt = !FUSED && have && item_of(1, nxt);
   u32x4 qf[KS], qn[KS];
   int page_reg = 0, page_nxt = 0;
   float slope_l2 = 0.f, slope_nxt = 0.f;
@@ -718,8 +720,16 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
       if (g == 0) a.ws_lse[slot] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
     }
 
-    // ---- next item: its Q and page ids arrived long ago; start those of the
-    // one after it
+    // ---- next item.  Fused form: load its Q and page ids now.  Split form:
+    // they arrived long ago; start those of the one after it.
+    if constexpr (FUSED) {
+      have = item_of(k + 1, cur);
+      if (have) {
+        load_q(cur, qf, slope_l2);
+        page_reg = load_pages(cur, 0);
+      }
+      continue;
+    }
     have = have_nxt;
     if (have) {
       cur = nxt;
