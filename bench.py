@@ -160,6 +160,52 @@ def extra_prefill(torch, sdpa, W, dev, stream, launches=10):
     return out
 
 
+def extra_paged_prefill(torch, sdpa, W, dev, stream, launches=10, block_size=64):
+    """The chunked f16 prefill workload run through the paged pool: the same
+    q, k, v, with K/V scattered over 64-token blocks in a randomly permuted
+    pool, the queries packed with a prefix sum; timed like the other
+    workloads, after the timed steps."""
+    w = W.CHUNKED_PREFILL
+    q, k, v, _ = W.dense_inputs(w)
+    nb_seq = (w.Sk + block_size - 1) // block_size
+    rng = np.random.default_rng(w.seed + 77)
+    perm = torch.from_numpy(rng.permutation(w.B * nb_seq).astype(np.int64))
+    table = perm.reshape(w.B, nb_seq).to(torch.int32)
+    # pool[block, slot, kv head, d]: block table[b, n] holds keys n*bs .. of sequence b
+    kk = k.permute(0, 2, 1, 3).reshape(w.B, nb_seq, block_size, w.Hkv, w.D)
+    vv = v.permute(0, 2, 1, 3).reshape(w.B, nb_seq, block_size, w.Hkv, w.D)
+    kp = torch.empty((w.B * nb_seq, block_size, w.Hkv, w.D), dtype=k.dtype)
+    vp = torch.empty_like(kp)
+    kp[perm] = kk.reshape(-1, block_size, w.Hkv, w.D)
+    vp[perm] = vv.reshape(-1, block_size, w.Hkv, w.D)
+    qp = q.permute(0, 2, 1, 3).reshape(w.B * w.Sq, w.Hq, w.D).contiguous()
+    cu = torch.arange(0, (w.B + 1) * w.Sq, w.Sq, dtype=torch.int32)
+    lens = torch.full((w.B,), w.Sk, dtype=torch.int32)
+    t = dict(q=qp.to(dev), kp=kp.to(dev), vp=vp.to(dev), table=table.to(dev), lens=lens.to(dev),
+             cu=cu.to(dev))
+    t["out"] = torch.empty_like(t["q"])
+
+    def run():
+        sdpa.attn_paged_prefill(t["q"], t["kp"], t["vp"], t["table"], t["lens"], t["cu"], None,
+                                t["out"], max_seqlen_q=w.Sq, softmax_scale=w.scale, causal=True,
+                                stream=stream)
+    for _ in range(3):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(launches):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / launches
+    tf = prefill_flops(w) / sec / 1e12
+    return {w.name + " over the paged pool (64-token blocks)": {
+        "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype, "work_per_launch": prefill_flops(w),
+        "ms_per_launch": sec * 1e3, "launches": launches}}
+
+
 def backward_flops(w) -> int:
     """Algorithmic work of the backward: the five matmuls per admissible
     (query, key) pair (S = Q K^T, dP = dO V^T, dV, dQ, dK), 2 D FLOP each."""
@@ -322,6 +368,7 @@ def bench(args):
     }
     if not args.no_extra:
         result["other_prefill"] = extra_prefill(torch, sdpa, W, dev, stream)
+        result["other_prefill"].update(extra_paged_prefill(torch, sdpa, W, dev, stream))
         result["backward"] = extra_backward(torch, sdpa, W, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
