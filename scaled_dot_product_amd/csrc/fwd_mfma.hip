@@ -408,25 +408,38 @@ void fwd_mfma_kernel(FwdArgs a) {
     page_reg = j < a.maxb ? a.table[(size_t)b * a.maxb + j] : 0;
   };
   bool bad_page = false;  // a table entry outside the pool was used (wave-uniform)
-  // Buffer resource of tile t; `ok` is false for a tile whose block is outside
-  // the pool (its keys are masked, its copies read nothing).
-  auto tile_rsrc = [&](const T* base_t, int t, bool& ok) -> __amdgpu_buffer_rsrc_t {
+  // Paged: a cursor (logical block lb, tile sub within it) per tensor for the
+  // tile its next copy reads, advanced one tile per step instead of dividing.
+  struct Cursor {
+    int lb, sub;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.sub == m_tiles) {
+      c.sub = 0;
+      ++c.lb;
+    }
+  };
+  // Buffer resource of tile t (at cursor c when paged); `ok` is false for a
+  // tile whose block is outside the pool (its keys are masked, its copies read
+  // nothing).  Every field is wave-uniform; the read-first-lane calls say so to
+  // the compiler, which otherwise computes the clamped size on the vector unit
+  // and wraps each copy in a loop over the distinct descriptors of the wave.
+  auto tile_rsrc = [&](const T* base_t, int t, Cursor c, bool& ok) -> __amdgpu_buffer_rsrc_t {
     if constexpr (PAGED) {
-      const int lb = t / m_tiles;
-      const int phys = __builtin_amdgcn_readlane(page_reg, lb - pbase);
-      const int rows = min(max(Sk - t * kBN, 0), kBN);
+      const int phys = __builtin_amdgcn_readlane(page_reg, c.lb - pbase);
+      const int rows = __builtin_amdgcn_readfirstlane(min(max(Sk - t * kBN, 0), kBN));
       ok = rows == 0 || (unsigned)phys < (unsigned)a.num_blocks;
       bad_page |= !ok;
-      const long long row0 = ok ? (long long)phys * a.bs + (t - lb * m_tiles) * kBN : 0;
-      return make_rsrc32(base_t + row0 * kv_row, ok ? rows * kv_row * (int)sizeof(T) : 0);
+      const long long row0 = ok ? (long long)phys * a.bs + c.sub * kBN : 0;
+      const int bytes = __builtin_amdgcn_readfirstlane(ok ? rows * kv_row * (int)sizeof(T) : 0);
+      return make_rsrc32(base_t + row0 * kv_row, bytes);
     } else {
       ok = true;
       const int base = t * kBN * D * (int)sizeof(T);
       return make_rsrc32(reinterpret_cast<const char*>(base_t) + base, kv_bytes - base);
     }
   };
-  auto dma_k = [&](u32x4* dst, int t, bool& ok) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(K, t, ok);
+  auto dma_k = [&](u32x4* dst, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kThreads + tid;
@@ -434,9 +447,7 @@ void fwd_mfma_kernel(FwdArgs a) {
       dma16(rs, dst + i * kThreads + wave * 64, (r * kv_row + (pc ^ swz_k<D>(r)) * 8) * (int)sizeof(T));
     }
   };
-  auto dma_v = [&](u32x4* dst, int t) {
-    bool ok_unused;
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(V, t, ok_unused);
+  auto dma_v = [&](u32x4* dst, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kThreads + tid;
@@ -451,7 +462,8 @@ void fwd_mfma_kernel(FwdArgs a) {
   //   while K(i+2) and V(i+1) stream into the buffers freed by step i-1.
   // K(i) lives in kbuf[i % 2], V(i) in vbuf[i % 2].
   // Paged: kok0 / kok1 say whether the tile in kbuf0 / kbuf1 lies in the pool;
-  // a tile that does not has its scores set to -inf right after its QK.
+  // the softmax of a tile that does not sees a key bound at its first key, so
+  // all of its keys are masked.
   const int n = t_end - t_begin;
   // steps every wave of the workgroup runs (barriers must match): group 0 of a
   // split workgroup has at least as many tiles as group 1
@@ -462,43 +474,66 @@ void fwd_mfma_kernel(FwdArgs a) {
   u32x4* const vb1 = vbuf1 + grp * TC;
   floatx16 sc[2];
   bool kok0 = true, kok1 = true;
-  auto mask_bad = [&](bool ok) {
-    if (PAGED && !ok) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = kNegInf;
-    }
-  };
-  if constexpr (PAGED) load_pages(t_begin / m_tiles);
+  Cursor kc{0, 0}, vc{0, 0};  // paged: tiles of the next K and V copies
+  if constexpr (PAGED) {
+    kc.lb = t_begin / m_tiles;
+    kc.sub = t_begin - kc.lb * m_tiles;
+    vc = kc;
+    load_pages(kc.lb);
+  }
+  bool ok_unused;
   if (n_steps > 0) {
-    if (n > 0) {
-      dma_k(kb0, t_begin, kok0);
-      dma_v(vb0, t_begin);
+    // descriptors first, copies after: the page ids may still be in flight,
+    // and a wait for them placed between copies would wait for the copies too
+    if constexpr (PAGED) {
+      const __amdgpu_buffer_rsrc_t rk0 = n > 0 ? tile_rsrc(K, t_begin, kc, kok0) : make_rsrc32(K, 0);
+      const __amdgpu_buffer_rsrc_t rv0 = n > 0 ? tile_rsrc(V, t_begin, vc, ok_unused) : make_rsrc32(V, 0);
+      advance(kc);
+      advance(vc);
+      const __amdgpu_buffer_rsrc_t rk1 = n > 1 ? tile_rsrc(K, t_begin + 1, kc, kok1) : make_rsrc32(K, 0);
+      advance(kc);
+      if (n > 0) {
+        dma_k(kb0, rk0);
+        dma_v(vb0, rv0);
+      }
+      if (n > 1) dma_k(kb1, rk1);
+    } else {
+      if (n > 0) {
+        dma_k(kb0, tile_rsrc(K, t_begin, kc, kok0));
+        dma_v(vb0, tile_rsrc(V, t_begin, vc, ok_unused));
+      }
+      if (n > 1) dma_k(kb1, tile_rsrc(K, t_begin + 1, kc, kok1));
     }
-    if (n > 1) dma_k(kb1, t_begin + 1, kok1);
     wait_vmem();
     __syncthreads();
-    if (n > 0 && live(t_begin)) {
-      qk_tile<T, D>(kb0, qf, ln, g, sc);
-      mask_bad(kok0);
-    }
+    if (n > 0 && live(t_begin)) qk_tile<T, D>(kb0, qf, ln, g, sc);
   }
   auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload,
-                  const bool& ok_read, bool& ok_load) {
+                  bool& ok_load) {
     const int t = t_begin + i;
+    const bool ok_t = ok_load;  // tile t, whose K buffer this step refills
     wait_vmem();
     __syncthreads();  // K(i+1), V(i) landed; everyone is done with step i-1's buffers
     if constexpr (PAGED) {
-      // the copies below read blocks (t + 1) / m and (t + 2) / m
-      if (i + 2 < n && (t + 2) / m_tiles - pbase >= 64) load_pages((t + 1) / m_tiles);
+      // the copies below read tiles t + 2 (K, at kc) and t + 1 (V, at vc)
+      if (i + 2 < n && kc.lb - pbase >= 64) load_pages(vc.lb);
+      const __amdgpu_buffer_rsrc_t rk = i + 2 < n ? tile_rsrc(K, t + 2, kc, ok_load) : make_rsrc32(K, 0);
+      const __amdgpu_buffer_rsrc_t rv = i + 1 < n ? tile_rsrc(V, t + 1, vc, ok_unused) : make_rsrc32(V, 0);
+      advance(kc);
+      advance(vc);
+      if (i + 2 < n) dma_k(kload, rk);
+      if (i + 1 < n) dma_v(vload, rv);
+    } else {
+      if (i + 2 < n) dma_k(kload, tile_rsrc(K, t + 2, kc, ok_load));
+      if (i + 1 < n) dma_v(vload, tile_rsrc(V, t + 1, vc, ok_unused));
     }
-    if (i + 2 < n) dma_k(kload, t + 2, ok_load);
-    if (i + 1 < n) dma_v(vload, t + 1);
     u32x4 kf[kKPF];
 #pragma unroll
     for (int p = 0; p < kKPF; ++p) kf[p] = kfrag<T, D>(kread, p, ln, g);
     if (live(t))
-      softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a, Sk, t * kBN, ip, ipa_w,
-                              ipb_w, slope_l2, lane, g);
+      softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a,
+                              PAGED && !ok_t ? t * kBN : Sk, t * kBN, ip, ipa_w, ipb_w, slope_l2,
+                              lane, g);
     // S(i+1) overwrites S(i), already consumed: one score buffer per wave.
     // This matrix phase runs at raised wave priority so that, of the two waves
     // sharing a SIMD, the one with matrix work ready wins instruction issue
@@ -508,11 +543,10 @@ void fwd_mfma_kernel(FwdArgs a) {
     if (i + 1 < n && live(t + 1)) qk_tile_pf<T, D>(kread, qf, ln, g, kf, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    if (i + 1 < n && live(t + 1)) mask_bad(ok_read);
   };
   for (int i = 0; i < n_steps; i += 2) {
-    step(i, kb1, vb0, kb0, vb1, kok1, kok0);
-    if (i + 1 < n_steps) step(i + 1, kb0, vb1, kb1, vb0, kok0, kok1);
+    step(i, kb1, vb0, kb0, vb1, kok0);
+    if (i + 1 < n_steps) step(i + 1, kb0, vb1, kb1, vb0, kok1);
   }
   if (PAGED && bad_page && a.err && lane == 0) *a.err = 1;
 
