@@ -181,7 +181,15 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
   constexpr int DB = D / 32;
   const int rb = n0 + 4 * g - ip;            // j - i' of element offset 0
 
+  // With a softcap or ALiBi the scores are turned into log2-unit logits
+  // relative to the current reference max m_ref (0 before any key): the
+  // per-tile constant base = c_cap + slope * (j0 - i') - m_ref carries the
+  // softcap offset, the ALiBi term of the tile's first key and m_ref, so each
+  // score costs its softcap (or scale) and one fused multiply-add for ALiBi.
   if constexpr (!kRaw) {
+    float base = (SOFTCAP ? a.c_cap : 0.f) - (st.m_run == kNegInf ? 0.f : st.m_run);
+    if constexpr (ALIBI) base = __builtin_fmaf(slope_l2, (float)rb, base);
+    const float m2cap = -2.f * a.c_cap;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -189,11 +197,13 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
         float x = sc[kb][r];
         if constexpr (SOFTCAP) {
           const float e = fast_exp2(x * a.c_score);
-          x = a.c_cap - 2.f * a.c_cap * fast_rcp(1.f + e);
+          x = __builtin_fmaf(m2cap, fast_rcp(1.f + e), base);
         } else {
-          x *= a.c_score;
+          x = __builtin_fmaf(x, a.c_score, base);
         }
-        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(rb + key_of(kb, r)), x);
+        // (the ALiBi term of key j0 + k added last: computed ahead of the
+        // scores, the 32 terms would hold 32 registers)
+        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)key_of(kb, r), x);
         sc[kb][r] = x;
       }
   }
@@ -225,18 +235,37 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
     const int kb = q >> 3, r = 2 * (q & 7);
     mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[kb][r]), sc[kb][r + 1]);
   }
+  // (with a softcap or ALiBi, mt is the tile max relative to m_ref)
   float mt = mx;
   if constexpr (kRaw) mt = mx == kNegInf ? kNegInf : mx * a.c_score;
   mt = halves_max(mt);
 
   // raise the reference max only when the tile exceeds it by > 2^8
-  const bool need = mt > st.m_run + kRescaleGap;
-  if (wave_any(need)) {
-    const float alpha = need ? fast_exp2(st.m_run - mt) : 1.f;
-    st.m_run = need ? mt : st.m_run;
-    st.l_part *= alpha;
+  if constexpr (kRaw) {
+    const bool need = mt > st.m_run + kRescaleGap;
+    if (wave_any(need)) {
+      const float alpha = need ? fast_exp2(st.m_run - mt) : 1.f;
+      st.m_run = need ? mt : st.m_run;
+      st.l_part *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
+      for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
+    }
+  } else {
+    // m_ref + mt > m_run + 8: above the gap, or the first admissible keys
+    const bool need = st.m_run == kNegInf ? mt != kNegInf : mt > kRescaleGap;
+    if (wave_any(need)) {
+      const float m_new = (st.m_run == kNegInf ? 0.f : st.m_run) + mt;
+      const float alpha = need ? fast_exp2(st.m_run - m_new) : 1.f;
+      const float shift = need ? mt : 0.f;  // logits relative to the new reference
+      st.m_run = need ? m_new : st.m_run;
+      st.l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][r] -= shift;
+    }
   }
   const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
 
@@ -251,8 +280,8 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
         p0 = fast_exp2(__builtin_fmaf(sc[kb][r], a.c_score, -m_use));
         p1 = fast_exp2(__builtin_fmaf(sc[kb][r + 1], a.c_score, -m_use));
       } else {
-        p0 = fast_exp2(sc[kb][r] - m_use);
-        p1 = fast_exp2(sc[kb][r + 1] - m_use);
+        p0 = fast_exp2(sc[kb][r]);
+        p1 = fast_exp2(sc[kb][r + 1]);
       }
       const uint32_t pk = E::pack2(p0, p1);
       pp[kb * 8 + r / 2] = pk;
