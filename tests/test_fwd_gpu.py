@@ -340,3 +340,49 @@ def test_lse_parity_f32(gpu_lib, case):
 def test_lse_parity_f64(gpu_lib, D):
     B, Hq, Hkv, Sq, Sk, kw = VALU_CASES[2]
     run_lse_case(gpu_lib, "f64", B, Hq, Hkv, Sq, Sk, D, seed=11, **kw)
+
+
+# ------------------------------------------- a reference max raised every tile
+
+RISING = [
+    # (S, D, kwargs): S = Sq = Sk; 700 keys take the key split (two wave groups)
+    (700, 128, dict(causal=True, softcap=1000.0, alibi=True)),
+    (700, 128, dict(causal=True, alibi=True)),
+    (700, 128, dict(softcap=1000.0)),
+    (400, 128, dict(causal=True, softcap=1000.0, alibi=True)),
+    (400, 64, dict(causal=True, alibi=True)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(RISING)))
+def test_rising_scores_rescale_every_tile(gpu_lib, dtype, case):
+    """Scores that grow by about 32 log2 units per 64-key tile (q and k_j
+    aligned along d = 0 with k_j[0] = j), so every tile raises the running
+    max far past the rescale gap: the logits of every tile are re-based to the
+    new reference inside the rescale branch (softcap / ALiBi), or the raw-score
+    rescale runs every tile (neither).  Output and LSE against the oracle."""
+    S, D, kw = RISING[case]
+    kw = dict(kw)
+    alibi = kw.pop("alibi", False)
+    rng = np.random.default_rng(1500 + case)
+    q = 0.1 * rng.standard_normal((1, 2, S, D), dtype=np.float32)
+    k = 0.1 * rng.standard_normal((1, 1, S, D), dtype=np.float32)
+    v = rng.standard_normal((1, 1, S, D), dtype=np.float32)
+    q[..., 0] = 4.0
+    k[0, 0, :, 0] = np.arange(S, dtype=np.float32)
+    q, k, v = W.cast(q, dtype), W.cast(k, dtype), W.cast(v, dtype)
+    sl = torch.from_numpy(W.alibi_slopes(2)) if alibi else None
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    name = f"rising scores {dtype} S{S} D{D} {kw} alibi={alibi}"
+    announce(name)
+    dev = torch.device("cuda:0")
+    out, lse = gpu_lib.attn_fwd_lse(q.to(dev), k.to(dev), v.to(dev), None if sl is None else sl.to(dev),
+                                    softmax_scale=scale, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_naive_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale=scale,
+                                alibi=None if sl is None else W.to_f64(sl), **kw)
+    compare(out, ref, DT[dtype], name)
+    ref_lse = oracle.sdpa_lse_f64(W.to_f64(q), W.to_f64(k), scale=scale,
+                                  alibi=None if sl is None else W.to_f64(sl), **kw)
+    check_lse(lse, ref_lse, dtype, name)
