@@ -132,6 +132,22 @@ def run_dense(sdpa, w, t, alibi, stream):
                   stream=stream)
 
 
+def time_launches(torch, run, stream, launches, warm=3):
+    """Median per-launch time (seconds) of ``run`` from HIP events recorded
+    on ``stream`` around each launch, after ``warm`` untimed launches."""
+    for _ in range(warm):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+
+
 def extra_prefill(torch, sdpa, W, dev, stream, launches=10):
     """The other prefill workloads, timed on their own after the timed steps
     (not part of a step): the long masked 8k prefill (causal + window 4096,
@@ -142,16 +158,7 @@ def extra_prefill(torch, sdpa, W, dev, stream, launches=10):
         t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
         t["out"] = torch.empty_like(t["q"])
         al = alibi.to(dev) if alibi is not None else None
-        for _ in range(3):
-            run_dense(sdpa, w, t, al, stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(launches):
-            run_dense(sdpa, w, t, al, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) * 1e-3 / launches
+        sec = time_launches(torch, lambda: run_dense(sdpa, w, t, al, stream), stream, launches)
         tf = prefill_flops(w) / sec / 1e12
         out[w.name] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype, "work_per_launch": prefill_flops(w),
@@ -189,16 +196,7 @@ def extra_paged_prefill(torch, sdpa, W, dev, stream, launches=10, block_size=64)
         sdpa.attn_paged_prefill(t["q"], t["kp"], t["vp"], t["table"], t["lens"], t["cu"], None,
                                 t["out"], max_seqlen_q=w.Sq, softmax_scale=w.scale, causal=True,
                                 stream=stream)
-    for _ in range(3):
-        run()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(launches):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) * 1e-3 / launches
+    sec = time_launches(torch, run, stream, launches)
     tf = prefill_flops(w) / sec / 1e12
     return {w.name + " over the paged pool (64-token blocks)": {
         "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -244,16 +242,7 @@ def extra_backward(torch, sdpa, W, dev, stream, launches=10):
             (w.name, recompute, "forward statistics + bwd_dkdv_kernel + bwd_dq_kernel"),
             (w.name + " (from the saved forward)", saved,
              "bwd_rowstats_kernel + bwd_dkdv_kernel + bwd_dq_kernel")):
-        for _ in range(3):
-            run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(launches):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) * 1e-3 / launches
+        sec = time_launches(torch, run, stream, launches)
         tf = backward_flops(w) / sec / 1e12
         out[label] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": tf / PEAK_BF16_TFLOPS, "dtype": w.dtype,
@@ -273,6 +262,81 @@ def run_decode(sdpa, wd, dec, stream):
                            num_splits=wd.num_splits, workspace=dec["workspace"], stream=stream)
 
 
+DECODE_SPLIT_USED = ("fused form: each (sequence, KV head) group is split over the 8 waves of "
+                     "one workgroup and merged in LDS; num_splits does not apply to this form")
+
+
+def clock_warm(torch, step, seconds):
+    """Runs ``step`` untimed until ``seconds`` of wall time have passed (at
+    least once), so that the timed steps see the sustained clock rather than
+    the ramp from idle; returns (seconds spent, steps run)."""
+    if seconds <= 0:
+        return 0.0, 0
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return time.perf_counter() - t0, n
+
+
+def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
+    """Per-call cost of a launch that the caller waits for, in two modes: eager
+    (the binding marshals the arguments and launches, host + kernel) and HIP
+    graph replay of the same call (kernel only, no host marshalling), both as
+    wall time per call with a synchronisation after each call; and the
+    kernel's own median event time.  For the paged decode workload and the
+    chunked f16 prefill (512 queries, a short prefill)."""
+    w = W.CHUNKED_PREFILL
+    q, k, v, _ = W.dense_inputs(w)
+    t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
+    t["out"] = torch.empty_like(t["q"])
+    cases = {
+        W.PAGED_DECODE.name: lambda s: run_decode(sdpa, wd, dec, s),
+        w.name: lambda s: run_dense(sdpa, w, t, None, s),
+    }
+    res = {}
+    for name, fn in cases.items():
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn(side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        kern = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            kern.append(e0.elapsed_time(e1) * 1e3)
+        modes = {}
+        for mode, call in (("eager", lambda: fn(stream)), ("graph", g.replay)):
+            for _ in range(10):
+                call()
+                torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(calls):
+                call()
+                torch.cuda.synchronize()
+            modes[mode] = (time.perf_counter() - t0) / calls * 1e6
+        res[name] = {"kernel_us": float(np.median(kern)), "eager_us_per_call": modes["eager"],
+                     "graph_us_per_call": modes["graph"],
+                     "note": "wall time per call with a synchronisation after each call"}
+        del g
+    del t
+    return res
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(W, budget_s: float):
@@ -280,11 +344,16 @@ def cpu_baseline(W, budget_s: float):
     workload, cycling over them until about ``budget_s`` seconds of CPU work
     have been spent (at least one slice)."""
     import oracle
+    affinity = len(os.sched_getaffinity(0))
+    # the host cores this process may use, capped by the thread count the
+    # environment grants it (a shared host sets OMP_NUM_THREADS to its share)
+    threads = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity))
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
+        pass
     w = W.GQA_CAUSAL_2K
     q, k, v, _ = W.dense_inputs(w)
     q64, k64, v64 = W.to_f64(q), W.to_f64(k), W.to_f64(v)
@@ -300,9 +369,11 @@ def cpu_baseline(W, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     flops = 4 * w.D * pairs * heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "affinity_cpus": affinity, "kind": "oracle",
             "sample": f"{heads} (batch, head) slices of the prefill workload, cycling over its "
                       f"{len(order)} (all {w.Sq} rows each), float64 NumPy, {dt:.1f} s"}
 
@@ -319,6 +390,8 @@ def bench(args):
     sdpa.library()
     wp, wd, pre, dec, lens = setup(torch, sdpa, W, dev)
     stream = torch.cuda.current_stream(dev)
+    warm_s, warm_steps = clock_warm(torch, lambda: (run_prefill(sdpa, wp, pre, stream),
+                                                    run_decode(sdpa, wd, dec, stream)), args.clock_warm)
     for _ in range(args.warmup):
         run_prefill(sdpa, wp, pre, stream)
         run_decode(sdpa, wd, dec, stream)
@@ -333,8 +406,9 @@ def bench(args):
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    # median of the per-launch event times (kernel time on the launch stream)
+    t_pre = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_dec = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
 
     flops = prefill_flops(wp)
     nbytes = decode_bytes(wd, lens)
@@ -360,13 +434,17 @@ def bench(args):
                                "D": wp.D, "causal": wp.causal},
                    "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D,
                               "block_size": wd.block_size, "ctx": [wd.ctx_lo, wd.ctx_hi],
-                              "num_splits": wd.num_splits, "live_tokens": int(lens.sum())}},
+                              "num_splits_arg": wd.num_splits, "split_used": DECODE_SPLIT_USED,
+                              "live_tokens": int(lens.sum())}},
+        "timing": {"statistic": "median of per-launch HIP event times on the launch stream",
+                   "clock_warm_s": round(warm_s, 3), "clock_warm_steps": warm_steps},
         "decode": {"value": gbs, "unit": "GB/s", "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
                    "ms": t_dec * 1e3},
         "roofline": dominant,
         "rooflines": {"prefill": roof_pre, "decode": roof_dec},
     }
     if not args.no_extra:
+        result["host_overhead"] = host_overhead(torch, sdpa, W, dev, wd, dec)
         result["other_prefill"] = extra_prefill(torch, sdpa, W, dev, stream)
         result["other_prefill"].update(extra_paged_prefill(torch, sdpa, W, dev, stream))
         result["backward"] = extra_backward(torch, sdpa, W, dev, stream)
@@ -586,6 +664,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip timing the other prefill workloads and the backward")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--clock-warm", type=float, default=1.0,
+                    help="seconds of untimed steps before the warm-up steps, so that the GPU "
+                         "clocks have ramped to their sustained level")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--mfma-util", metavar="DIR")

@@ -707,6 +707,20 @@ hipError_t launch_split(const FwdArgs& a, int grid, hipStream_t stream) {
   else return launch_flags<FLAGS>(a, grid, stream);  // never taken
 }
 
+// Factor from a raw score (q . k) to the exponent of the weight: log2(e) *
+// scale, or 2 log2(e) scale / cap for the softcap's exponential.  Without a
+// softcap or ALiBi the kernel masks raw scores with -inf and folds this factor
+// into the exponent, where a zero scale would turn a masked score into
+// -inf * 0 = NaN; a zero scale therefore enters as the smallest normal float
+// instead: every finite score times it is below 2^-100 in magnitude, so every
+// admissible weight is still exactly 1 (uniform attention, as for scale 0)
+// while a masked score keeps weight 0.
+float score_factor(float scale, float softcap, bool alibi) {
+  if (softcap > 0.f) return 2.f * kLog2e * scale / softcap;
+  const float c = kLog2e * scale;
+  return (c == 0.f && !alibi) ? __FLT_MIN__ : c;
+}
+
 // Compute units of the current device (queried once per device).
 int device_cus() {
   static int cus[64] = {};
@@ -744,7 +758,7 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
   a.has_hi = p.causal || p.wr >= 0;
   a.dmax = p.causal ? (p.wr >= 0 ? min(p.wr, 0) : 0) : p.wr;
   const bool softcap = p.softcap > 0.f;
-  a.c_score = softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
+  a.c_score = score_factor(p.scale, p.softcap, p.alibi != nullptr);
   a.c_cap = kLog2e * p.softcap;
   const int grid = a.nqb * a.nbh;
   const bool mask = p.causal || p.wl >= 0 || p.wr >= 0 || (p.Sk % kBN) != 0;
@@ -803,7 +817,7 @@ hipError_t ATTN_CAT(launch_paged_prefill_, ATTN_TAG)(const PagedPrefillProblem& 
   a.has_hi = p.causal || p.wr >= 0;
   a.dmax = p.causal ? (p.wr >= 0 ? min(p.wr, 0) : 0) : p.wr;
   const bool softcap = p.softcap > 0.f;
-  a.c_score = softcap ? 2.f * kLog2e * p.scale / p.softcap : kLog2e * p.scale;
+  a.c_score = score_factor(p.scale, p.softcap, p.alibi != nullptr);
   a.c_cap = kLog2e * p.softcap;
   const int grid = a.nqb * a.nbh;
   // lengths vary per sequence: the masked variants always; the key split on

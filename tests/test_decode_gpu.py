@@ -109,6 +109,87 @@ def test_paged_parity_wide_batch(gpu_lib, case):
             assert torch.count_nonzero(out[b]).item() == 0
 
 
+# Batches above 256 sequences with block sizes that are multiples of 16: the
+# partial kernel over uniform 16-token blocks (one 2-wave workgroup per split
+# and group, the longest sequences first) plus the merge kernel.  The last two
+# cases exceed the batch size up to which each workgroup ranks the lengths in
+# LDS (2048 at head dim 128, 1024 at 64), so those take sequences in index
+# order.
+PARTIAL_CASES = [
+    # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
+    ("bf16", 300, 8, 4, 128, 16, 300, 3, None, False),
+    ("bf16", 512, 8, 8, 128, 64, 260, 8, None, False),
+    ("f16", 300, 4, 2, 64, 64, 400, 1, 20.0, True),
+    ("bf16", 320, 16, 4, 256, 16, 150, 8, 30.0, True),
+    ("f16", 512, 8, 2, 128, 16, 250, 8, None, True),
+    ("bf16", 400, 32, 8, 128, 32, 200, 5, None, False),
+    ("bf16", 2100, 2, 1, 128, 16, 40, 2, None, False),
+    ("f16", 1100, 4, 2, 64, 32, 70, 3, 25.0, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PARTIAL_CASES)))
+def test_paged_parity_partial_kernel(gpu_lib, case):
+    dtype, B, Hq, Hkv, D, bs, hi, splits, cap, use_alibi = PARTIAL_CASES[case]
+    lens = wide_lens(B, hi, 400 + case)
+    maxb = (max(lens) + bs - 1) // bs + 1
+    w = W.Paged("t", dtype, B, Hq, Hkv, D, bs, 0, 0, splits, maxb, seed=410 + case)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    alibi = torch.from_numpy(W.alibi_slopes(Hq)) if use_alibi else None
+    scale = D ** -0.5
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce(f"paged decode partial-kernel case {case}: {PARTIAL_CASES[case]}")
+    out = gpu_decode(gpu_lib, q, kp, vp, table, sl, alibi, softmax_scale=scale, softcap=cap,
+                     num_splits=splits, error_flag=flag)
+    assert flag.item() == 0
+    ref = oracle_decode(q, kp, vp, table, sl, alibi, scale=scale, softcap=cap)
+    compare(out, ref, DT[dtype], f"paged partial-kernel case {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
+def test_partial_kernel_error_flag_and_determinism(gpu_lib):
+    """The partial kernel (B = 300, 16-token blocks): a block id outside the
+    pool masks its keys and sets the flag, a length beyond the table's
+    capacity is clamped and sets it, the other sequences are unaffected, and
+    reruns are bitwise equal."""
+    B, Hq, Hkv, D, bs, maxb = 300, 8, 2, 128, 16, 20
+    w = W.Paged("ep", "bf16", B, Hq, Hkv, D, bs, 0, 0, 4, maxb, seed=91)
+    lens = wide_lens(B, 300, 92)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce("partial kernel: valid call, rerun")
+    a = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
+    b = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
+    assert flag.item() == 0
+    assert torch.equal(a, b)
+    ref = oracle_decode(q, kp, vp, table, sl, scale=D ** -0.5)
+    compare(a, ref, torch.bfloat16, "partial kernel")
+    victim = int(np.argmax(np.array(lens) > 2 * bs))
+    bad = table.clone()
+    bad[victim, 1] = 10 ** 6                                # keys 16..31 of that sequence are masked
+    announce("partial kernel: block id out of range")
+    out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag, num_splits=4)
+    assert flag.item() == 1
+    assert torch.isfinite(out.float()).all()
+    others = [i for i in range(B) if i != victim]
+    compare(out[others], ref[others], torch.bfloat16, "partial kernel, unaffected sequences")
+    n = lens[victim]
+    keep = [t for t in range(n) if not bs <= t < 2 * bs]
+    kb = oracle.paged_gather(W.to_f64(kp), table.numpy(), n, victim, bs)[keep]
+    vb = oracle.paged_gather(W.to_f64(vp), table.numpy(), n, victim, bs)[keep]
+    r1 = oracle.sdpa_naive_f64(W.to_f64(q[victim:victim + 1]), kb.transpose(1, 0, 2)[None],
+                               vb.transpose(1, 0, 2)[None], scale=D ** -0.5)
+    compare(out[victim:victim + 1], r1, torch.bfloat16, "partial kernel, masked keys")
+    flag.zero_()
+    long = sl.clone()
+    long[3] = maxb * bs + 5
+    announce("partial kernel: seq_len beyond capacity")
+    gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag, num_splits=4)
+    assert flag.item() == 1
+
+
 def test_paged_decode_workload(gpu_lib):
     w = W.PAGED_DECODE
     q, kp, vp, table, lens, _ = W.paged_inputs(w)
@@ -120,7 +201,8 @@ def test_paged_decode_workload(gpu_lib):
 
 
 @pytest.mark.parametrize("bs,splits,B,Hkv", [(64, 8, 4, 2), (16, 3, 4, 2), (5, 1, 4, 2),
-                                             (16, 8, 64, 4), (32, 2, 128, 2)])
+                                             (16, 8, 64, 4), (32, 2, 128, 2),
+                                             (16, 3, 300, 2), (64, 8, 300, 1)])
 def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
     """One-hot scores: q = 1024 e0 in every head and a single key row equal to
     8 e0 give that key a score of 1024 * 8 / sqrt(128) ~ 724 and every other
@@ -128,7 +210,8 @@ def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
     the V row of that logical token.  V rows hold (sequence, position % 128,
     position // 128, kv head) as bf16-exact integers; slots no table entry
     points at hold a finite sentinel so that a stray read is visible.  The
-    last two cases have 256 (sequence, KV head) groups."""
+    cases with B = 64 and 128 have 256 (sequence, KV head) groups (the fused
+    form); those with B = 300 run the partial kernel over 16-token blocks."""
     Hq, D = 8, 128
     lens = [130, 64, 7, 200] if B == 4 else np.random.default_rng(6).integers(1, 260, size=B).tolist()
     rng = np.random.default_rng(5)

@@ -1,8 +1,8 @@
 """Parity of attn_fwd (HIP, through the C ABI) with the float64 oracle.
 
 Small cases span several 128-row / 64-key tiles with ragged tails and every
-mask combination; the full-size workloads are checked on sampled heads (all
-rows of each sampled head), in the launch configuration the benchmark times.
+mask combination; the full-size workloads are checked on their whole output,
+in the launch configuration the benchmark times.
 """
 import math
 
@@ -40,14 +40,17 @@ def oracle_heads(q, k, v, alibi, heads, **kw):
 
 
 def run_case(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None,
-             softcap=None, alibi=False, amp=1.0, seed=0, heads=None):
+             softcap=None, alibi=False, amp=1.0, seed=0, heads=None, scale=None,
+             window_left=None, window_right=None):
+    wl = window_left if window_left is not None else wl
+    wr = window_right if window_right is not None else wr
     name = (f"attn_fwd {dtype} B{B} H{Hq}/{Hkv} Sq{Sq} Sk{Sk} D{D} causal={causal} "
             f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
     q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
     sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
     # the ABI takes the scale as float32: both sides get that value
-    kw = dict(scale=float(np.float32(1.0 / math.sqrt(D))), causal=causal, window_left=wl, window_right=wr,
-              softcap=softcap)
+    kw = dict(scale=float(np.float32(1.0 / math.sqrt(D) if scale is None else scale)), causal=causal,
+              window_left=wl, window_right=wr, softcap=softcap)
     announce(name)
     out = gpu_fwd(sdpa, q, k, v, sl, softmax_scale=kw["scale"], causal=causal,
                   window_left=wl, window_right=wr, softcap=softcap)
@@ -163,36 +166,51 @@ def test_tiny_f32_workload(gpu_lib):
     compare(out, ref, torch.float32, w.name)
 
 
-def _workload_heads(sdpa, w, sample):
+def _workload_full(sdpa, w):
+    """The whole output of a full-size workload, in the launch configuration
+    the benchmark times, against the oracle's whole output."""
     q, k, v, sl = W.dense_inputs(w)
     announce(w.name)
     out = gpu_fwd(sdpa, q, k, v, sl, softmax_scale=w.scale, causal=w.causal,
                   window_left=w.window_left, window_right=w.window_right, softcap=w.softcap)
-    ref = oracle_heads(q, k, v, sl, sample, scale=w.scale, causal=w.causal,
-                       window_left=w.window_left, window_right=w.window_right, softcap=w.softcap)
-    compare(torch.stack([out[b, h] for b, h in sample]), ref, DT[w.dtype], w.name)
+    ref = oracle.sdpa_naive_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v),
+                                alibi=None if sl is None else W.to_f64(sl), scale=w.scale,
+                                causal=w.causal, window_left=w.window_left,
+                                window_right=w.window_right, softcap=w.softcap)
+    compare(out, ref, DT[w.dtype], w.name)
     return out
 
 
 def test_gqa_causal_2k_workload(gpu_lib):
-    _workload_heads(gpu_lib, W.GQA_CAUSAL_2K, [(0, 0), (0, 5), (0, 31), (1, 12), (1, 27)])
+    _workload_full(gpu_lib, W.GQA_CAUSAL_2K)
 
 
 def test_masked_rows_workload(gpu_lib):
     w = W.GQA_MASKED_ROWS
-    out = _workload_heads(gpu_lib, w, [(0, 0), (1, 30)])
+    out = _workload_full(gpu_lib, w)
     # Rows 0..63 have no admissible key in every head: exactly zero.
     assert torch.count_nonzero(out[:, :, :64]).item() == 0
     assert torch.count_nonzero(out[:, :, 64:].float().abs().sum(-1) == 0).item() == 0
 
 
 def test_long_masked_8k_workload(gpu_lib):
-    _workload_heads(gpu_lib, W.LONG_MASKED_8K, [(0, 0), (0, 17), (0, 31)])
+    _workload_full(gpu_lib, W.LONG_MASKED_8K)
 
 
 def test_chunked_prefill_workload(gpu_lib):
-    w = W.CHUNKED_PREFILL
-    _workload_heads(gpu_lib, w, [(b, h) for b in range(w.B) for h in (0, 7, 15)])
+    _workload_full(gpu_lib, W.CHUNKED_PREFILL)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("mask", ["causal", "window", "ragged"])
+def test_zero_scale_is_uniform_attention(gpu_lib, dtype, mask):
+    """softmax_scale = 0 makes every admissible weight 1: each row is the mean
+    of its admissible V rows, also where masked keys share a tile with
+    admissible ones (causal diagonal, window edge, a ragged key tail)."""
+    Sk = 200 if mask == "ragged" else 256
+    kw = {"causal": dict(causal=True), "window": dict(window_left=40, window_right=3),
+          "ragged": dict()}[mask]
+    run_case(gpu_lib, dtype, 1, 4, 2, 256, Sk, 128, seed=31, scale=0.0, **kw)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])

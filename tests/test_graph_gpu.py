@@ -4,14 +4,16 @@ Host launch overhead dominates short decode and prefill calls (derivation
 page, the section on host overhead and graph replay), so callers capture them.
 Every buffer is allocated before capture and the library issues no memset or
 allocation of its own; each replay is checked bitwise against the eager
-result, with eager work and synchronisation between replays.
+result, with eager work and synchronisation between replays, and the first
+replay's outputs are checked against the float64 oracle.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
-from gpu_util import announce
+from gpu_util import announce, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +70,25 @@ def test_graph_replay_matches_eager(gpu_lib):
         for name, got, want in zip(("out", "out_lse", "lse", "decode", "decode_wide"),
                                    (out, out2, lse, dout, wout), eager):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from eager"
+        if rep == 0:
+            check_against_oracle(q, k, v, out, out2, lse, scale, (dq, kp, vp, table, lens, dout),
+                                 (wq, wkp, wvp, wtab, wlens, wout))
+
+
+def check_against_oracle(q, k, v, out, out2, lse, scale, dec, wide):
+    """The replayed outputs against the float64 oracle, at the parity bars of
+    the eager tests (bf16 outputs; LSE within 2^-8 + 1e-4)."""
+    f = float(np.float32(scale))
+    q64, k64, v64 = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    compare(out, oracle.sdpa_naive_f64(q64, k64, v64, scale=f, causal=True), torch.bfloat16,
+            "graph replay: attn_fwd")
+    compare(out2, oracle.sdpa_naive_f64(q64, k64, v64, scale=f, causal=True, window_left=64),
+            torch.bfloat16, "graph replay: attn_fwd_lse output")
+    want = oracle.sdpa_lse_f64(q64, k64, scale=f, causal=True, window_left=64)
+    err = np.abs(W.to_f64(lse) - want)
+    assert np.all(err <= 2.0 ** -8 + 1e-4 + 1e-5 * np.abs(want)), \
+        f"graph replay: lse max abs err {err.max():.3g}"
+    for what, (dq, kp, vp, table, lens, dout) in (("split", dec), ("fused", wide)):
+        ref = oracle.paged_decode_f64(W.to_f64(dq), W.to_f64(kp), W.to_f64(vp), table.cpu().numpy(),
+                                      lens.cpu().numpy(), scale=f)
+        compare(dout, ref, torch.bfloat16, f"graph replay: paged decode ({what} form)")
