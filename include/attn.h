@@ -201,6 +201,30 @@ attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v
                                 int32_t* error_flag,
                                 const attn_paged_params_t* p, void* stream);
 
+/* Bytes of the device-resident workspace behind attn_paged_decode_noalloc
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define ATTN_DECODE_SCRATCH_BYTES (32u << 20)
+
+/* attn_paged_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, validation, kernels and results (bitwise) as
+ * attn_paged_decode, except that no workspace is passed: the split forms
+ * keep their partials in a file-scope device array of
+ * ATTN_DECODE_SCRATCH_BYTES bytes inside the library.  A call whose
+ * attn_paged_decode_workspace_size(p) exceeds that returns
+ * ATTN_ERR_WORKSPACE before anything is launched.  The library allocates
+ * nothing and calls no allocating routine here; on the first call on a
+ * device it looks up that device's copy of the array (hipGetSymbolAddress;
+ * ATTN_ERR_HIP if that fails).  Every call on one GPU shares that GPU's
+ * array, whatever the stream: calls that overlap in time on one GPU race on
+ * it, so callers serialise them (one stream, or events).  Nothing in the
+ * array needs clearing between calls: every call writes each partial it
+ * reads. */
+attn_status_t attn_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const float* alibi, void* out, int32_t* error_flag,
+                                        const attn_paged_params_t* p, void* stream);
+
 /* Parameters of attn_paged_prefill: variable-length prefill over the paged
  * pool (kernel-contract page, attention_paged_naive, with the packed query
  * layout of the derivation page, section 5: queries [total_q, Hq, D] with a

@@ -17,6 +17,9 @@ fails to load, every call raises.
     attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
                       out=None, *, softmax_scale=None, softcap=None,
                       num_splits=8, workspace=None, error_flag=None, stream=None)
+    attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
+                              out=None, *, softmax_scale=None, softcap=None,
+                              num_splits=8, error_flag=None, stream=None)
 """
 from __future__ import annotations
 
@@ -31,6 +34,7 @@ __all__ = [
     "AttnError", "library", "LIB_PATH",
     "attn_fwd", "attn_fwd_check", "attn_fwd_params", "attn_fwd_lse", "attn_fwd_lse_check",
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
+    "attn_paged_decode_noalloc", "DECODE_SCRATCH_BYTES",
     "attn_paged_params", "attn_status_str", "attn_version",
     "attn_paged_prefill", "attn_paged_prefill_check", "attn_varlen_params",
     "attn_bwd", "attn_bwd_check", "attn_bwd_workspace_size", "attn_bwd_lse", "attn_bwd_lse_check",
@@ -113,6 +117,8 @@ def library():
     lib.attn_paged_decode_check.restype = ctypes.c_int
     lib.attn_paged_decode.argtypes = [_VP] * 8 + [ctypes.c_size_t, _VP, pag_p, _VP]
     lib.attn_paged_decode.restype = ctypes.c_int
+    lib.attn_paged_decode_noalloc.argtypes = [_VP] * 8 + [pag_p, _VP]
+    lib.attn_paged_decode_noalloc.restype = ctypes.c_int
     var_p = ctypes.POINTER(attn_varlen_params_t)
     lib.attn_paged_prefill_check.argtypes = [_VP] * 9 + [var_p]
     lib.attn_paged_prefill_check.restype = ctypes.c_int
@@ -356,11 +362,10 @@ def attn_paged_decode_check(q_ptr, k_ptr, v_ptr, table_ptr, lens_ptr, alibi_ptr,
                                                  None if params is None else ctypes.byref(params)))
 
 
-def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
-                      softmax_scale=None, softcap=None, num_splits=8, workspace=None,
-                      error_flag=None, stream=None):
-    """Paged split-KV decode, one query per sequence (see attn.h)."""
-    lib = library()
+def _paged_decode_args(q, k_pool, v_pool, block_table, seq_lens, alibi, out, workspace, error_flag,
+                       softmax_scale, softcap, num_splits):
+    """Shared marshalling of the two decode entry points: device, dtype and
+    shape agreement of the tensors, the params struct, and `out`."""
     dev = q.device
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
                     ("block_table", block_table), ("seq_lens", seq_lens), ("alibi", alibi),
@@ -384,19 +389,52 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=
         raise ValueError("error_flag must be one int32")
     p = attn_paged_params(tuple(q.shape), tuple(k_pool.shape), block_table.shape[1], q.dtype,
                           softmax_scale=softmax_scale, softcap=softcap, num_splits=num_splits)
-    need = attn_paged_decode_workspace_size(p)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
+    return p, out
+
+
+def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
+                      softmax_scale=None, softcap=None, num_splits=8, workspace=None,
+                      error_flag=None, stream=None):
+    """Paged split-KV decode, one query per sequence (see attn.h)."""
+    lib = library()
+    dev = q.device
+    p, out = _paged_decode_args(q, k_pool, v_pool, block_table, seq_lens, alibi, out, workspace,
+                                error_flag, softmax_scale, softcap, num_splits)
+    need = attn_paged_decode_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.attn_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                _ptr(seq_lens), _ptr(alibi), _ptr(out), _ptr(workspace), ws_bytes,
                                _ptr(error_flag), ctypes.byref(p), _stream_handle(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_paged_decode")
+    return out
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # ATTN_DECODE_SCRATCH_BYTES in attn.h
+
+
+def attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
+                              softmax_scale=None, softcap=None, num_splits=8, error_flag=None,
+                              stream=None):
+    """attn_paged_decode without a workspace argument: the library's
+    device-resident scratch array (DECODE_SCRATCH_BYTES per GPU) serves as it,
+    so the call allocates nothing when `out` is given (see attn.h; calls that
+    overlap in time on one GPU race on that array)."""
+    lib = library()
+    dev = q.device
+    p, out = _paged_decode_args(q, k_pool, v_pool, block_table, seq_lens, alibi, out, None,
+                                error_flag, softmax_scale, softcap, num_splits)
+    st = lib.attn_paged_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                       _ptr(seq_lens), _ptr(alibi), _ptr(out), _ptr(error_flag),
+                                       ctypes.byref(p), _stream_handle(stream, dev))
+    if st != 0:
+        raise AttnError(st, "attn_paged_decode_noalloc")
     return out
 
 

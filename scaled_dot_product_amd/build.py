@@ -36,6 +36,7 @@ KERNEL_FLAGS = ["-fno-honor-nans"]
 UNITS = [("attn_api.cpp", [], "attn_api.o"),
          ("fwd_f32.hip", KERNEL_FLAGS, "fwd_f32.o"),
          ("decode.hip", KERNEL_FLAGS, "decode.o"),
+         ("scratch.hip", [], "scratch.o"),
          ("bwd_valu.hip", KERNEL_FLAGS, "bwd_valu.o")]
 for _elem, _tag in (("__bf16", "bf16"), ("_Float16", "f16")):
     for _d in (128, 64, 256):

@@ -555,6 +555,25 @@ attn_status_t attn_paged_decode(const void* q, const void* k_pool, const void* v
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status_t attn_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const float* alibi, void* out, int32_t* error_flag,
+                                        const attn_paged_params_t* p, void* stream) {
+  if (!p) return ATTN_ERR_NULL;
+  // the size check comes first and makes no HIP call (sizes beyond the array
+  // are rejected before the device is touched); invalid parameters are
+  // reported by attn_paged_decode_check below
+  if (attn_paged_decode_workspace_size(p) > (size_t)ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+  const attn_status_t st = attn_paged_decode_check(q, k_pool, v_pool, block_table, seq_lens, alibi,
+                                                   out, nullptr, 0, error_flag, p);
+  // (the check reports a missing workspace when one is needed; here it is the scratch array)
+  if (st != ATTN_OK && st != ATTN_ERR_WORKSPACE) return st;
+  void* ws = attn::decode_scratch();
+  if (!ws) return ATTN_ERR_HIP;
+  return attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi, out, ws,
+                           (size_t)ATTN_DECODE_SCRATCH_BYTES, error_flag, p, stream);
+}
+
 attn_status_t attn_paged_prefill_check(const void* q, const void* k_pool, const void* v_pool,
                                        const int32_t* block_table, const int32_t* seq_lens,
                                        const int32_t* cu_seqlens_q, const float* alibi,

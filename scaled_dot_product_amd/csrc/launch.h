@@ -136,6 +136,9 @@ hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream);
 hipError_t launch_paged_valu(const PagedPrefillProblem& p, bool f64, hipStream_t stream);
 hipError_t launch_paged_prefill(const PagedPrefillProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeProblem& p, int dtype, hipStream_t stream);
+// Device address of the current device's copy of the allocation-free decode
+// workspace (ATTN_DECODE_SCRATCH_BYTES), or nullptr if it cannot be found.
+void* decode_scratch();
 hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream);
 // Vector-ALU backward (F32/F64): `stats` holds two values of the element type
 // per query row; the chunking fields of p are not used.

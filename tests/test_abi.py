@@ -357,3 +357,20 @@ def test_bwd_lse_check():
     assert check_bwd_lse(p, do=None) == NULL
     assert check_bwd_lse(p, ws_bytes=1) == WORKSPACE
     assert sdpa.attn_bwd_lse_check(Q, K, V, BO, BL, DO, None, DQ, DK, DV, BWS, 1 << 30, None) == NULL
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch_array():
+    """attn_paged_decode_noalloc refuses, before touching the device, a call
+    whose split partials would not fit the library's scratch array; the
+    pointers here are never dereferenced."""
+    lib = sdpa.library()
+    fake = ctypes.c_void_p(1 << 20)
+    # 512 sequences x 64 heads x 16 splits x (128 + 1) floats = 270 MB > 32 MiB
+    p = sdpa.attn_paged_params((512, 64, 1, 128), (9000, 16, 8, 128), 600, sdpa.ATTN_BF16,
+                               num_splits=16)
+    assert sdpa.attn_paged_decode_workspace_size(p) > sdpa.DECODE_SCRATCH_BYTES
+    st = lib.attn_paged_decode_noalloc(fake, fake, fake, fake, fake, None, fake, None,
+                                       ctypes.byref(p), None)
+    assert st == 9  # ATTN_ERR_WORKSPACE
+    assert lib.attn_paged_decode_noalloc(fake, fake, fake, fake, fake, None, fake, None, None,
+                                         None) == 1  # ATTN_ERR_NULL: no params
