@@ -91,6 +91,16 @@ typedef struct attn_fwd_params {
   int64_t window_right;  /* -1: unbounded; else keys j <= i' + window_right     */
   float softmax_scale;   /* finite, >= 0 (1/sqrt(D) is the usual value)         */
   float softcap;         /* 0: off; > 0: s <- softcap * tanh(s / softcap)       */
+  int64_t k_len;         /* live key prefix length, read only when has_k_len    */
+  int32_t has_k_len;     /* 0: every one of the Sk keys is live (a zeroed      *
+                          * struct means this).  Else the kernel-contract      *
+                          * page's k_len parameter of attention_naive: k_len   *
+                          * in 0..Sk, only keys j < k_len exist, and the call  *
+                          * equals one on k[:, :, :k_len] and v[:, :, :k_len]  *
+                          * (queries align bottom-right to the live length,    *
+                          * i' = i + k_len - Sq) while k and v keep their      *
+                          * [B, Hkv, Sk, D] layout; keys j >= k_len are never  *
+                          * read.  The backward entry points require 0.        */
 } attn_fwd_params_t;
 
 /* Host-only validation of an attn_fwd call (no HIP call is made).

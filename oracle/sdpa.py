@@ -33,6 +33,12 @@ design notes of the repository):
 * ALiBi adds ``slope[h] * (j - i')``; slopes are float32 ``[Hq]``.
 * ``softcap=None`` (or 0) disables the softcap; a negative value is an error.
 * KV head of query head ``h`` is ``h // (Hq // Hkv)`` (contiguous groups).
+* ``k_len`` (the kernel-contract page's live-prefix parameter of
+  ``attention_naive``; ``None`` = all ``Sk`` keys): the page says only that
+  it selects a live prefix for decode.  Read here as: the first ``k_len``
+  key/value rows are the whole key sequence and the rest of the ``Sk`` rows
+  do not exist, so positions align to the live length,
+  ``i' = i + k_len - Sq``, as the paged section aligns to the context length.
 
 Every function computes in float64; inputs of any float dtype are upcast.
 """
@@ -115,6 +121,19 @@ def admissible(Sq, Sk, causal, window_left=None, window_right=None, rows=None):
     return ok
 
 
+def live_keys(k, v, k_len):
+    """The live key prefix of the kernel-contract page's ``k_len`` parameter
+    of ``attention_naive`` (``None`` = all ``Sk`` keys): only the first
+    ``k_len`` key/value rows of every head take part; the rows after them are
+    not read.  Returns ``(k, v)`` cut to that prefix."""
+    Sk = k.shape[2]
+    if k_len is None:
+        return k, v
+    if not 0 <= k_len <= Sk:
+        raise ValueError("k_len must lie in [0, Sk]")
+    return k[:, :, :k_len], v[:, :, :k_len]
+
+
 def transform_scores(s, softcap=None, slope=None, rel=None):
     """Score transforms in the order the kernel-contract page fixes for
     ``attention_naive``: the already scaled score first goes through the
@@ -133,14 +152,15 @@ def _scores(qrows, kmat, scale, softcap, slope, rel, ok):
 
 
 def sdpa_naive_f64(q, k, v, *, scale, causal=False, window_left=None,
-                   window_right=None, softcap=None, alibi=None, row_block=512):
+                   window_right=None, softcap=None, alibi=None, row_block=512, k_len=None):
     """Materialised-score attention, the definition itself.
 
     Derivation page section 1 (output row = softmax-weighted convex combination
     of V rows), section 2 (subtract the row max before exponentiating) and the
-    kernel-contract page's ``attention_naive`` (mask, softcap, ALiBi, GQA, and a
-    row with no admissible key gives an all-zero output row).  Score rows are
-    computed ``row_block`` queries at a time only to bound memory.
+    kernel-contract page's ``attention_naive`` (mask, softcap, ALiBi, GQA, the
+    ``k_len`` live key prefix, and a row with no admissible key gives an
+    all-zero output row).  Score rows are computed ``row_block`` queries at a
+    time only to bound memory.
 
     Returns float64 ``[B, Hq, Sq, D]``.
     """
@@ -150,6 +170,8 @@ def sdpa_naive_f64(q, k, v, *, scale, causal=False, window_left=None,
     B, Hq, Hkv, Sq, Sk, D = _check_common(q, k, v, alibi, softcap)
     slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
     out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    k, v = live_keys(k, v, k_len)
+    Sk = k.shape[2]
     if Sq == 0 or Sk == 0:
         return out
     ip_all = query_positions(Sq, Sk)
@@ -180,7 +202,7 @@ def sdpa_naive_f64(q, k, v, *, scale, causal=False, window_left=None,
 
 
 def sdpa_lse_f64(q, k, *, scale, causal=False, window_left=None, window_right=None,
-                 softcap=None, alibi=None, row_block=512):
+                 softcap=None, alibi=None, row_block=512, k_len=None):
     """Natural-log log-sum-exp of each query row's transformed admissible
     scores, ``log(sum_j exp(s_j))``, with ``-inf`` for a row with no
     admissible key.
@@ -198,6 +220,8 @@ def sdpa_lse_f64(q, k, *, scale, causal=False, window_left=None, window_right=No
     B, Hq, Hkv, Sq, Sk, D = _check_common(q, k, k, alibi, softcap)
     slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
     lse = np.full((B, Hq, Sq), -np.inf)
+    k, _ = live_keys(k, k, k_len)
+    Sk = k.shape[2]
     if Sq == 0 or Sk == 0:
         return lse
     ip_all = query_positions(Sq, Sk)
@@ -220,7 +244,7 @@ def sdpa_lse_f64(q, k, *, scale, causal=False, window_left=None, window_right=No
 
 
 def sdpa_online_f64(q, k, v, *, scale, tile=16, causal=False, window_left=None,
-                    window_right=None, softcap=None, alibi=None):
+                    window_right=None, softcap=None, alibi=None, k_len=None):
     """Streaming (online) softmax over key tiles of width ``tile``.
 
     Derivation page section 3: running max ``m``, denominator ``l`` and
@@ -239,6 +263,8 @@ def sdpa_online_f64(q, k, v, *, scale, tile=16, causal=False, window_left=None,
         raise ValueError("tile must be >= 1")
     slopes = None if alibi is None else np.asarray(alibi, dtype=np.float64)
     out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    k, v = live_keys(k, v, k_len)
+    Sk = k.shape[2]
     if Sq == 0 or Sk == 0:
         return out
     ip = query_positions(Sq, Sk)[:, None]

@@ -8,7 +8,7 @@ does not pass them).  There is no fallback: if ``libattn.so`` is missing or
 fails to load, every call raises.
 
     attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
-             window_left=None, window_right=None, softcap=None, stream=None)
+             window_left=None, window_right=None, softcap=None, k_len=None, stream=None)
     attn_fwd_lse(q, k, v, alibi=None, out=None, lse=None, *, ...)  -> (out, lse)
     attn_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q,
                        alibi=None, out=None, *, max_seqlen_q=None, softmax_scale=None,
@@ -67,7 +67,9 @@ class attn_fwd_params_t(ctypes.Structure):
                 ("Sq", ctypes.c_int64), ("Sk", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("window_left", ctypes.c_int64), ("window_right", ctypes.c_int64),
-                ("softmax_scale", ctypes.c_float), ("softcap", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("softcap", ctypes.c_float),
+                ("k_len", ctypes.c_int64),
+                ("has_k_len", ctypes.c_int32)]
 
 
 class attn_paged_params_t(ctypes.Structure):
@@ -172,7 +174,8 @@ def _stream_handle(stream, device):
 
 
 def attn_fwd_params(q_shape, k_shape, dtype, *, softmax_scale=None, causal=False,
-                    window_left=None, window_right=None, softcap=None) -> attn_fwd_params_t:
+                    window_left=None, window_right=None, softcap=None,
+                    k_len=None) -> attn_fwd_params_t:
     B, Hq, Sq, D = q_shape
     _, Hkv, Sk, _ = k_shape
     return attn_fwd_params_t(
@@ -182,7 +185,9 @@ def attn_fwd_params(q_shape, k_shape, dtype, *, softmax_scale=None, causal=False
         window_left=-1 if window_left is None else int(window_left),
         window_right=-1 if window_right is None else int(window_right),
         softmax_scale=(1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale),
-        softcap=0.0 if not softcap else float(softcap))
+        softcap=0.0 if not softcap else float(softcap),
+        k_len=0 if k_len is None else int(k_len),
+        has_k_len=0 if k_len is None else 1)
 
 
 def attn_fwd_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr, params: attn_fwd_params_t) -> int:
@@ -198,7 +203,8 @@ def attn_fwd_lse_check(q_ptr, k_ptr, v_ptr, alibi_ptr, out_ptr, lse_ptr,
                                             None if params is None else ctypes.byref(params)))
 
 
-def _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left, window_right, softcap):
+def _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left, window_right, softcap,
+              k_len=None):
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("alibi", alibi), ("out", out)):
         _need_device(name, t, dev)
@@ -216,16 +222,17 @@ def _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left, window_ri
         raise ValueError("out must match q in shape and dtype")
     p = attn_fwd_params(tuple(q.shape), tuple(k.shape), q.dtype, softmax_scale=softmax_scale,
                         causal=causal, window_left=window_left, window_right=window_right,
-                        softcap=softcap)
+                        softcap=softcap, k_len=k_len)
     return dev, out, p
 
 
 def attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
-             window_left=None, window_right=None, softcap=None, stream=None):
-    """Attention forward over ``[B, H, S, D]`` device tensors (see attn.h)."""
+             window_left=None, window_right=None, softcap=None, k_len=None, stream=None):
+    """Attention forward over ``[B, H, S, D]`` device tensors (see attn.h);
+    ``k_len`` (optional) is the live key prefix: only keys ``j < k_len`` exist."""
     lib = library()
     dev, out, p = _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left,
-                            window_right, softcap)
+                            window_right, softcap, k_len)
     st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alibi), _ptr(out), ctypes.byref(p),
                       _stream_handle(stream, dev))
     if st != 0:
@@ -234,13 +241,13 @@ def attn_fwd(q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
 
 
 def attn_fwd_lse(q, k, v, alibi=None, out=None, lse=None, *, softmax_scale=None, causal=False,
-                 window_left=None, window_right=None, softcap=None, stream=None):
+                 window_left=None, window_right=None, softcap=None, k_len=None, stream=None):
     """As :func:`attn_fwd`, and also the float32 ``[B, Hq, Sq]`` natural-log
     log-sum-exp of every row (``-inf`` for rows with no admissible key).
     Returns ``(out, lse)``."""
     lib = library()
     dev, out, p = _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left,
-                            window_right, softcap)
+                            window_right, softcap, k_len)
     _need_device("lse", lse, dev)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)

@@ -137,6 +137,7 @@ attn_status_t check_fwd(const void* q, const void* k, const void* v, const float
   if (st != ATTN_OK) return st;
   if (bad_scale(p->softmax_scale) || bad_softcap(p->softcap)) return ATTN_ERR_PARAM;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_PARAM;
+  if (p->has_k_len && (p->k_len < 0 || p->k_len > p->Sk)) return ATTN_ERR_PARAM;
   if (qb > 0 && (!q || !out)) return ATTN_ERR_NULL;
   if (qb > 0 && kvb > 0 && (!k || !v)) return ATTN_ERR_NULL;
   const void* ptrs[] = {q, k, v, alibi, out};
@@ -204,11 +205,15 @@ static attn_status_t launch_fwd(const void* q, const void* k, const void* v, con
   fp.Hq = (int)p->Hq;
   fp.Hkv = (int)p->Hkv;
   fp.Sq = (int)p->Sq;
-  fp.Sk = (int)p->Sk;
+  // the live key prefix: masks, alignment and tile counts use its length,
+  // the addressing of k and v their capacity Sk
+  const int64_t live = p->has_k_len ? p->k_len : p->Sk;
+  fp.Sk = (int)live;
+  fp.kv_stride = (int)p->Sk;
   fp.D = (int)p->D;
   fp.causal = p->causal != 0;
   // Windows wider than every possible distance are the same as no window.
-  fp.wl = (p->window_left < 0 || p->window_left >= p->Sk) ? -1 : (int)p->window_left;
+  fp.wl = (p->window_left < 0 || p->window_left >= live) ? -1 : (int)p->window_left;
   fp.wr = (p->window_right < 0 || p->window_right >= p->Sq) ? -1 : (int)p->window_right;
   fp.scale = p->softmax_scale;
   fp.softcap = p->softcap;
@@ -291,6 +296,7 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
   // q, k, v, alibi and the parameters as for the forward, with dq in out's place
   attn_status_t st = check_fwd(q, k, v, alibi, dq, p);
   if (st != ATTN_OK) return st;
+  if (p->has_k_len) return ATTN_ERR_PARAM;  // the backward takes every key live
   const bool valu = p->dtype == ATTN_F32 || p->dtype == ATTN_F64;
   if (!valu && p->D > 128) return ATTN_ERR_HEAD_DIM;  // the matrix-core backward: 64 and 128
   int64_t qb, kvb;

@@ -46,6 +46,7 @@ struct VArgs {
   void* out;
   float* lse;  // per-row log-sum-exp (natural log), or nullptr
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
+  int kv_stride;  // dense: keys between consecutive (sequence, KV head) slices of k and v
   int wl, has_hi, dmax;
   float scale, softcap;
   // paged form
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(VArgs a) {
     Q = static_cast<const T*>(a.q) + ((size_t)q0 * a.Hq + h) * D;
     O = static_cast<T*>(a.out) + ((size_t)q0 * a.Hq + h) * D;
   } else {
-    K += (size_t)(b * a.Hkv + kvh) * Sk * D;
-    V += (size_t)(b * a.Hkv + kvh) * Sk * D;
+    K += (size_t)(b * a.Hkv + kvh) * a.kv_stride * D;
+    V += (size_t)(b * a.Hkv + kvh) * a.kv_stride * D;
   }
   const int off = Sk - Sq;
   const int qi = m0 + row;
@@ -236,6 +237,7 @@ hipError_t launch_fwd_valu(const FwdProblem& p, bool f64, hipStream_t stream) {
   a.lse = p.lse;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
+  a.kv_stride = p.kv_stride > 0 ? p.kv_stride : p.Sk;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.group = p.Hq / p.Hkv;

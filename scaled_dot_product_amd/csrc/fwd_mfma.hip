@@ -77,6 +77,7 @@ struct FwdArgs {
   const void* dout;
   float* stats;
   int Sq, Sk, Hq, Hkv, group, nbh, nqb;
+  int kv_stride;  // dense: keys between consecutive (sequence, KV head) slices of k and v
   int heavy_first;
   // paged, variable-length form (F_PAGED): queries packed [total_q, Hq, D]
   // with a prefix sum, K/V in a [num_blocks, bs, Hkv, D] pool
@@ -376,8 +377,8 @@ void fwd_mfma_kernel(FwdArgs a) {
     V = reinterpret_cast<const T*>(a.v) + (size_t)kvh * D;
   } else {
     Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * Sq * D;
-    K = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * Sk * D;
-    V = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * Sk * D;
+    K = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * a.kv_stride * D;
+    V = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * a.kv_stride * D;
     O = reinterpret_cast<T*>(a.out) + (size_t)bh * Sq * D;
   }
   const int off = Sk - Sq;
@@ -748,6 +749,7 @@ hipError_t ATTN_CAT(launch_fwd_mfma_, ATTN_TAG)(const FwdProblem& p, hipStream_t
   a.stats = p.stats;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
+  a.kv_stride = p.kv_stride > 0 ? p.kv_stride : p.Sk;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.group = p.Hq / p.Hkv;

@@ -19,7 +19,8 @@ struct FwdProblem {
   // [B, Hq, Sq] of float pairs (log2-unit LSE, +inf without keys; dO . O)
   const void* dout = nullptr;
   float* stats = nullptr;
-  int B, Hq, Hkv, Sq, Sk, D;
+  int B, Hq, Hkv, Sq, Sk, D;  // Sk: live keys (the k_len prefix when one is given)
+  int kv_stride = 0;          // keys between consecutive (sequence, KV head) slices of k and v (>= Sk)
   int causal;
   int wl, wr;     // window; -1 = unbounded (already clamped to the useful range)
   float scale;    // softmax scale

@@ -109,9 +109,22 @@ def test_fwd_check_empty_tensors_may_be_null():
     (dict(softmax_scale=float("nan")), PARAM), (dict(softmax_scale=-1.0), PARAM),
     (dict(softcap=-0.5), PARAM), (dict(softcap=float("inf")), PARAM),
     (dict(window_left=-2), PARAM), (dict(window_right=-5), PARAM),
+    (dict(has_k_len=1, k_len=-1), PARAM), (dict(has_k_len=1, k_len=131), PARAM),
 ])
 def test_fwd_check_rejects(kw, code):
     assert check_fwd(fwd(**kw)) == code
+
+
+def test_fwd_check_live_prefix():
+    # k_len is read only with has_k_len; with it, 0 .. Sk (= 130 here)
+    assert check_fwd(fwd(k_len=-7)) == OK
+    for kl in (0, 1, 129, 130):
+        assert check_fwd(fwd(has_k_len=1, k_len=kl)) == OK, kl
+        assert check_fwd(fwd(has_k_len=1, k_len=kl, dtype=sdpa.ATTN_F64, D=64)) == OK, kl
+    p = sdpa.attn_fwd_params((2, 8, 100, 128), (2, 2, 130, 128), sdpa.ATTN_BF16, k_len=5)
+    assert (p.has_k_len, p.k_len) == (1, 5)
+    p = sdpa.attn_fwd_params((2, 8, 100, 128), (2, 2, 130, 128), sdpa.ATTN_BF16)
+    assert p.has_k_len == 0
 
 
 def test_fwd_check_pointers():
@@ -305,7 +318,7 @@ def test_bwd_workspace_size():
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=sdpa.ATTN_F64, D=80), HEAD_DIM),
     (dict(dtype=9), DTYPE), (dict(D=256), HEAD_DIM), (dict(Hkv=3), GQA),
-    (dict(softcap=-1.0), PARAM),
+    (dict(softcap=-1.0), PARAM), (dict(has_k_len=1, k_len=130), PARAM),
 ])
 def test_bwd_check_rejects(kw, code):
     assert check_bwd(fwd(**kw)) == code

@@ -195,6 +195,54 @@ def check_softcap_limits(fn):
                                rtol=0, atol=1e-14)
 
 
+_LIVE_KWS = (dict(scale=0.7, causal=True),
+             dict(scale=0.6, window_left=2, window_right=1),
+             dict(scale=0.8, causal=True, softcap=0.5, alibi=[0.25, 0.75]))
+_LIVE_LENS = (0, 1, 3, 5, 8)
+
+
+def _live_prefix_case():
+    """Keys of capacity 8 whose rows past the live prefix hold NaN: a key
+    read past ``k_len`` poisons its row."""
+    rng = np.random.default_rng(91)
+    q8 = lambda *s: np.round(rng.standard_normal(s) * 8) / 8
+    q, k, v = q8(1, 2, 5, 3), q8(1, 1, 8, 3), q8(1, 1, 8, 3)
+    return q, k, v
+
+
+_LIVE_EXPECTED = {}
+
+
+def _live_expected(kl, ki):
+    """50-digit brute force over the key tensors cut to their first ``kl``
+    rows (the live prefix taken as the whole key sequence), output and lse."""
+    if (kl, ki) not in _LIVE_EXPECTED:
+        from oracle.bruteforce import lse_bruteforce, sdpa_bruteforce
+        q, k, v = _live_prefix_case()
+        kw = _LIVE_KWS[ki]
+        kt, vt = k[:, :, :kl].tolist(), v[:, :, :kl].tolist()
+        out = np.array(sdpa_bruteforce(q.tolist(), kt, vt, **kw), dtype=np.float64)
+        lse = lse_bruteforce(q.tolist(), kt, **kw)
+        lse = np.array([[[-np.inf if x is None else float(x) for x in row] for row in h] for h in lse])
+        _LIVE_EXPECTED[(kl, ki)] = (out, lse)
+    return _LIVE_EXPECTED[(kl, ki)]
+
+
+def check_live_prefix(fn):
+    """Kernel-contract page, ``k_len`` of ``attention_naive``: only the first
+    ``k_len`` key rows exist, the query positions align to that live length,
+    and the rows after it are never read (they hold NaN here)."""
+    q, k, v = _live_prefix_case()
+    for kl in _LIVE_LENS:
+        kd, vd = k.copy(), v.copy()
+        kd[:, :, kl:] = np.nan
+        vd[:, :, kl:] = np.nan
+        for ki, kw in enumerate(_LIVE_KWS):
+            exp, _ = _live_expected(kl, ki)
+            got = fn(q, kd, vd, k_len=kl, **kw)
+            np.testing.assert_allclose(got, exp, rtol=0, atol=1e-13, err_msg=f"k_len={kl} {kw}")
+
+
 # --------------------------------------------------------------------------
 # Tests
 # --------------------------------------------------------------------------
@@ -208,7 +256,8 @@ DENSE_FNS = {
 
 CHECKS = [check_golden_dense, check_zero_query_causal_means, check_zero_query_window_means,
           check_alibi_geometric, check_two_key_ratio, check_single_key_exact,
-          check_shift_invariance, check_gqa_is_repeat_interleave, check_softcap_limits]
+          check_shift_invariance, check_gqa_is_repeat_interleave, check_softcap_limits,
+          check_live_prefix]
 
 
 @pytest.mark.parametrize("fn_name", list(DENSE_FNS))
@@ -397,6 +446,35 @@ def test_lse_matches_decimal_bruteforce(case):
             assert abs(got[idx] - float(r)) <= 1e-12 * max(1.0, abs(float(r)))
     if case == 4:
         assert np.all(got[..., :2] == -np.inf) and np.all(np.isfinite(got[..., 2:]))
+
+
+def test_lse_live_prefix_matches_decimal_bruteforce():
+    """sdpa_lse_f64 with ``k_len``: the 50-digit lse over the cut tensors,
+    with NaN in the rows past the live prefix."""
+    q, k, v = _live_prefix_case()
+    for kl in _LIVE_LENS:
+        kd = k.copy()
+        kd[:, :, kl:] = np.nan
+        for ki, kw in enumerate(_LIVE_KWS):
+            _, exp = _live_expected(kl, ki)
+            got = osd.sdpa_lse_f64(q, kd, k_len=kl, **kw)
+            fin = np.isfinite(exp)
+            assert np.array_equal(np.isfinite(got), fin), (kl, kw)
+            np.testing.assert_allclose(got[fin], exp[fin], rtol=1e-12, atol=1e-12)
+            assert np.all(got[~fin] == -np.inf)
+
+
+def test_live_prefix_full_and_errors():
+    """``k_len = Sk`` is the call without it; ``k_len`` outside [0, Sk] is an
+    error."""
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 1, 2, 4, 3), _rand(rng, 1, 1, 6, 3), _rand(rng, 1, 1, 6, 3)
+    for fn in DENSE_FNS.values():
+        np.testing.assert_array_equal(fn(q, k, v, scale=0.5, causal=True, k_len=6),
+                                      fn(q, k, v, scale=0.5, causal=True))
+        for bad in (-1, 7):
+            with pytest.raises(ValueError):
+                fn(q, k, v, scale=0.5, k_len=bad)
 
 
 def test_lse_closed_forms():

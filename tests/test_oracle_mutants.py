@@ -15,6 +15,7 @@ import test_oracle as pins
 _real_admissible = osd.admissible
 _real_transform = osd.transform_scores
 _real_gather = osd.paged_gather
+_real_live = osd.live_keys
 
 
 def _adm_exclusive(Sq, Sk, causal, window_left=None, window_right=None, rows=None):
@@ -40,6 +41,17 @@ def _adm_strict_causal(Sq, Sk, causal, window_left=None, window_right=None, rows
         ip = (ip if rows is None else ip[rows])[:, None]
         ok &= np.arange(Sk)[None, :] < ip
     return ok
+
+
+def _live_ignored(k, v, k_len):
+    _real_live(k, v, k_len)            # keeps the argument checks
+    return k, v
+
+
+def _live_one_short(k, v, k_len):
+    if k_len is None:
+        return k, v
+    return _real_live(k, v, max(0, k_len - 1))
 
 
 def _tf_alibi_sign(s, softcap=None, slope=None, rel=None):
@@ -119,6 +131,8 @@ MUTANTS = {
     "causal_strict": ("admissible", _adm_strict_causal),
     "window_exclusive": ("admissible", _adm_exclusive),
     "window_sides_swapped": ("admissible", _adm_swapped_window),
+    "live_prefix_ignored": ("live_keys", _live_ignored),
+    "live_prefix_one_short": ("live_keys", _live_one_short),
     "kv_head_modulo": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
     "alibi_sign": ("transform_scores", _tf_alibi_sign),
     "alibi_abs_distance": ("transform_scores", _tf_alibi_abs),
