@@ -119,6 +119,10 @@ template <int DB>
 struct RowState {
   floatx16 o[DB];
   float m_run;
+  // row sum of the weights: D <= 128 sums on the matrix core, and every
+  // element of l_acc holds this lane's row sum; D = 256 (short of registers)
+  // keeps the dot-product form, l_part summing this lane's half of the keys
+  floatx4 l_acc;
   float l_part;
 };
 
@@ -180,6 +184,7 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
   constexpr bool ALIBI = (FLAGS & F_ALIBI) != 0;
   constexpr bool kRaw = !SOFTCAP && !ALIBI;  // max on raw scores, scale folded into exp
   constexpr int DB = D / 32;
+  constexpr bool kMmaSum = D <= 128;         // row sums on the matrix core
   const int rb = n0 + 4 * g - ip;            // j - i' of element offset 0
 
   // With a softcap or ALiBi the scores are turned into log2-unit logits
@@ -247,7 +252,8 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
     if (wave_any(need)) {
       const float alpha = need ? fast_exp2(st.m_run - mt) : 1.f;
       st.m_run = need ? mt : st.m_run;
-      st.l_part *= alpha;
+      if constexpr (D <= 128) st.l_acc = st.l_acc * alpha;
+      else st.l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
     }
@@ -259,7 +265,8 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
       const float alpha = need ? fast_exp2(st.m_run - m_new) : 1.f;
       const float shift = need ? mt : 0.f;  // logits relative to the new reference
       st.m_run = need ? m_new : st.m_run;
-      st.l_part *= alpha;
+      if constexpr (D <= 128) st.l_acc = st.l_acc * alpha;
+      else st.l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
 #pragma unroll
@@ -284,17 +291,28 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
         p0 = fast_exp2(sc[kb][r]);
         p1 = fast_exp2(sc[kb][r + 1]);
       }
-      const uint32_t pk = E::pack2(p0, p1);
-      pp[kb * 8 + r / 2] = pk;
-      st.l_part = E::dot2(pk, E::kOnePair, st.l_part);
+      pp[kb * 8 + r / 2] = E::pack2(p0, p1);
+      if constexpr (!kMmaSum) st.l_part = E::dot2(pp[kb * 8 + r / 2], E::kOnePair, st.l_part);
     }
 
   // O^T += V^T P^T, 16 keys per step; V^T through the LDS transpose read
   const int trow = 4 * g + ((lane & 15) >> 2);                // key row within a 16-key step
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // d within a 32-row block
+  // Row sums of the rounded weights on the matrix core, from the same P^T
+  // operand read as the B operand of the 16x16x32 instruction: lane l's 8
+  // weights (all of query row l % 32) become column l % 16, k-block l / 16.
+  // So column c holds row c in its k-blocks 0 and 2 and row c + 16 in 1 and 3.
+  // The A operand is 0/1: output row m sums the k-blocks of parity (m / 4) & 1.
+  // Lane l receives output rows 4 (l / 16) .. + 3 of column l % 16, which then
+  // all hold the sum of row l % 32, its own row.  This costs no vector-ALU
+  // work; the two-element dot product it replaces stalls behind other waves'
+  // matrix instructions.
+  const uint32_t one = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? E::kOnePair : 0u;
+  const u32x4 sel = {one, one, one, one};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const u32x4 pf = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
+    if constexpr (kMmaSum) st.l_acc = E::mma16(sel, pf, st.l_acc);
     const int r0 = 16 * ks + trow;
     const int sw = swz_v<D>(r0);  // same for r0 + 8
 #pragma unroll
@@ -420,6 +438,7 @@ void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) st.o[db] = floatx16{};
   st.m_run = kNegInf;
+  st.l_acc = floatx4{};
   st.l_part = 0.f;
 
   // ---- asynchronous tile copies global -> LDS.  Chunk c of a tile sits at
@@ -583,7 +602,7 @@ void fwd_mfma_kernel(FwdArgs a) {
   // ---- key groups: group 1 hands (o, m, l) to group 0 through LDS (the tile
   // buffers are free now), one 32-row block of O^T at a time; group 0 rebases
   // both to their common reference max.
-  float l = halves_sum(st.l_part);
+  float l = D <= 128 ? st.l_acc[0] : halves_sum(st.l_part);
   if constexpr (SPLIT) {
     float* xo = reinterpret_cast<float*>(kbuf0);  // [64 lanes x 4 waves][16]
     float* xml = reinterpret_cast<float*>(vbuf0); // [64 x 4][2]
