@@ -83,8 +83,8 @@ typedef struct attn_fwd_params {
   int64_t Sk;            /* key length (0 allowed: output is all zero); one    *
                           * head's K (Sk * D * element size) must be < 2 GiB    */
   int64_t D;             /* head dim: 64, 128 or 256 for F16/BF16 (matrix      *
-                          * cores; the backward 64 or 128); 32, 64, 128 or 256 *
-                          * for F32/F64 (vector ALU)                            */
+                          * cores); 32, 64, 128 or 256 for F32/F64 (vector     *
+                          * ALU); the same for the backward                    */
   int32_t dtype;         /* attn_dtype_t of q, k, v and out                     */
   int32_t causal;        /* nonzero: bottom-right causal mask                   */
   int64_t window_left;   /* -1: unbounded; else keys j >= i' - window_left      */
@@ -301,8 +301,8 @@ attn_status_t attn_paged_prefill(const void* q, const void* k_pool, const void* 
  * P (times 1 - tanh^2(s_pre / softcap) with a softcap), dQ = scale dS K and
  * dK = scale dS^T Q.  dk and dv are [B, Hkv, Sk, D], summed over the query
  * heads of each KV head's group; dq is [B, Hq, Sq, D].  A row with no
- * admissible key contributes nothing.  F16/BF16 with head dims 64/128 run on
- * the matrix cores (float32 accumulation, P and dS rounded to the input dtype
+ * admissible key contributes nothing.  F16/BF16 with head dims 64/128/256 run
+ * on the matrix cores (float32 accumulation, P and dS rounded to the input dtype
  * as matmul operands); F32/F64 with head dims 32 to 256 on the vector ALU,
  * computing in that type throughout.  Deterministic: no atomics, fixed
  * order. */

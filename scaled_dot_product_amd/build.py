@@ -40,7 +40,7 @@ UNITS = [("attn_api.cpp", [], "attn_api.o"),
          ("bwd_valu.hip", KERNEL_FLAGS, "bwd_valu.o")]
 for _elem, _tag in (("__bf16", "bf16"), ("_Float16", "f16")):
     for _d in (128, 64, 256):
-        for _src in ("fwd_mfma", "bwd_mfma") if _d <= 128 else ("fwd_mfma",):
+        for _src in ("fwd_mfma", "bwd_mfma"):
             UNITS.append((f"{_src}.hip",
                           KERNEL_FLAGS + [f"-DATTN_ELEM={_elem}", f"-DATTN_D={_d}",
                                           f"-DATTN_TAG={_tag}_d{_d}"],

@@ -33,24 +33,32 @@ hipError_t launch_bwd_mfma_bf16_d128(const BwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd_mfma_bf16_d64(const BwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd_mfma_f16_d128(const BwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd_mfma_f16_d64(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_mfma_bf16_d256(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_mfma_f16_d256(const BwdProblem& p, hipStream_t stream);
 
 hipError_t launch_bwd_mfma(const BwdProblem& p, int dtype, hipStream_t stream) {
   if (dtype == ATTN_BF16)
-    return p.D == 128 ? launch_bwd_mfma_bf16_d128(p, stream) : launch_bwd_mfma_bf16_d64(p, stream);
-  return p.D == 128 ? launch_bwd_mfma_f16_d128(p, stream) : launch_bwd_mfma_f16_d64(p, stream);
+    return p.D == 256 ? launch_bwd_mfma_bf16_d256(p, stream)
+         : p.D == 128 ? launch_bwd_mfma_bf16_d128(p, stream) : launch_bwd_mfma_bf16_d64(p, stream);
+  return p.D == 256 ? launch_bwd_mfma_f16_d256(p, stream)
+       : p.D == 128 ? launch_bwd_mfma_f16_d128(p, stream) : launch_bwd_mfma_f16_d64(p, stream);
 }
 
 hipError_t launch_bwd_rowstats_bf16_d128(const void*, const void*, const float*, float*, long long, hipStream_t);
 hipError_t launch_bwd_rowstats_bf16_d64(const void*, const void*, const float*, float*, long long, hipStream_t);
 hipError_t launch_bwd_rowstats_f16_d128(const void*, const void*, const float*, float*, long long, hipStream_t);
 hipError_t launch_bwd_rowstats_f16_d64(const void*, const void*, const float*, float*, long long, hipStream_t);
+hipError_t launch_bwd_rowstats_bf16_d256(const void*, const void*, const float*, float*, long long, hipStream_t);
+hipError_t launch_bwd_rowstats_f16_d256(const void*, const void*, const float*, float*, long long, hipStream_t);
 
 hipError_t launch_bwd_rowstats(const void* out, const void* dout, const float* lse, float* stats,
                                long long rows, int D, int dtype, hipStream_t stream) {
   if (dtype == ATTN_BF16)
-    return D == 128 ? launch_bwd_rowstats_bf16_d128(out, dout, lse, stats, rows, stream)
+    return D == 256 ? launch_bwd_rowstats_bf16_d256(out, dout, lse, stats, rows, stream)
+         : D == 128 ? launch_bwd_rowstats_bf16_d128(out, dout, lse, stats, rows, stream)
                     : launch_bwd_rowstats_bf16_d64(out, dout, lse, stats, rows, stream);
-  return D == 128 ? launch_bwd_rowstats_f16_d128(out, dout, lse, stats, rows, stream)
+  return D == 256 ? launch_bwd_rowstats_f16_d256(out, dout, lse, stats, rows, stream)
+       : D == 128 ? launch_bwd_rowstats_f16_d128(out, dout, lse, stats, rows, stream)
                   : launch_bwd_rowstats_f16_d64(out, dout, lse, stats, rows, stream);
 }
 
@@ -297,8 +305,6 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
   attn_status_t st = check_fwd(q, k, v, alibi, dq, p);
   if (st != ATTN_OK) return st;
   if (p->has_k_len) return ATTN_ERR_PARAM;  // the backward takes every key live
-  const bool valu = p->dtype == ATTN_F32 || p->dtype == ATTN_F64;
-  if (!valu && p->D > 128) return ATTN_ERR_HEAD_DIM;  // the matrix-core backward: 64 and 128
   int64_t qb, kvb;
   fwd_shape(p, &qb, &kvb);
   if (qb > 0 && !dout) return ATTN_ERR_NULL;

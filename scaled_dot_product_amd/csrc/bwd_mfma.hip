@@ -1,5 +1,5 @@
 // bwd_mfma.hip -- attention backward on the matrix cores (bf16 / f16, head
-// dim 64 or 128): dQ, dK, dV by recompute.
+// dim 64, 128 or 256): dQ, dK, dV by recompute.
 //
 // Kernel-contract page, attention_flash_backward: with P the stable-softmax
 // weights of the forward (recomputed from Q, K and the forward's per-row
@@ -22,6 +22,10 @@
 //      dP = dO V^T  (dO rows from LDS, V in registers)    8
 //      dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read through the
 //      LDS transpose read and P, dS already in the B-operand layout   8 + 8
+//    At D = 256 the two accumulators would not fit the register file: there
+//    each key block gets two workgroups, each accumulating the dK/dV columns
+//    of one half of the head dimension (both still contract S and dP over all
+//    of it, so S and dP are computed twice).
 //  * bwd_dq_kernel: the forward kernel's shape -- 4 waves x 32 query rows, K
 //    and V tiles of 64 keys through LDS -- with, per tile,
 //      S^T = K Q^T and dP^T = V dO^T (Q and dO in registers)          16 + 16
@@ -32,7 +36,7 @@
 #include "launch.h"
 
 #ifndef ATTN_ELEM
-#error "build with -DATTN_ELEM=<__bf16|_Float16> -DATTN_D=<64|128> -DATTN_TAG=<name>"
+#error "build with -DATTN_ELEM=<__bf16|_Float16> -DATTN_D=<64|128|256> -DATTN_TAG=<name>"
 #endif
 #define ATTN_CAT2(a, b) a##b
 #define ATTN_CAT(a, b) ATTN_CAT2(a, b)
@@ -50,6 +54,10 @@ constexpr int kQW = 32;       // dQ: query rows per wave
 constexpr int kBM = kNW * kQW;  // dQ: query rows per workgroup
 
 enum : int { B_MASK = 1, B_SOFTCAP = 2, B_ALIBI = 4 };
+
+// dK/dV workgroups per key block: one per half of the head dimension at D = 256
+template <int D>
+constexpr int kDHalves = D > 128 ? 2 : 1;
 
 struct BwdArgs {
   const void* q;
@@ -82,7 +90,7 @@ struct BwdArgs {
 // row reads (32 rows, one chunk each) hit distinct banks.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // Transformed score in log2 units (softcap, then ALiBi) of the raw dot
@@ -150,8 +158,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool ALIBI = (FLAGS & B_ALIBI) != 0;
   constexpr int NC = D / 8;
   constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
   constexpr int TC = kBQ * NC;
+  // D = 256: each workgroup accumulates the dK, dV columns of one half of the
+  // head dimension (S and dP are still contracted over all of it), which keeps
+  // the accumulators within the register file
+  constexpr int NH = kDHalves<D>;
+  constexpr int DB = D / 32 / NH;  // 32-column blocks of dK^T, dV^T per workgroup
 
   __shared__ u32x4 qbuf0[TC], qbuf1[TC], obuf0[TC], obuf1[TC];
   __shared__ float2 sbuf0[kBQ], sbuf1[kBQ];
@@ -164,7 +176,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   // ---- work item: chunk ch of key block kblk of (b, kvh); low key blocks
   // see the most queries under a causal mask, so they go first
-  const int id = blockIdx.x;
+  const int dh = NH > 1 ? (int)(blockIdx.x % NH) : 0;  // half of the head dimension
+  const int db0 = dh * DB;                              // its first 32-column block
+  const int id = blockIdx.x / NH;
   const int kc = id / a.nbh_kv;
   const int bkv = id - kc * a.nbh_kv;
   const int kblk = kc / a.nchunk;
@@ -288,8 +302,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
       const u32x4 df = {dsp[4 * ks], dsp[4 * ks + 1], dsp[4 * ks + 2], dsp[4 * ks + 3]};
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dvt[db] = E::mma32(tr_operand<T, D>(Os, ks, db, lane), pf, dvt[db]);
-        dkt[db] = E::mma32(tr_operand<T, D>(Qs, ks, db, lane), df, dkt[db]);
+        dvt[db] = E::mma32(tr_operand<T, D>(Os, ks, db0 + db, lane), pf, dvt[db]);
+        dkt[db] = E::mma32(tr_operand<T, D>(Qs, ks, db0 + db, lane), df, dkt[db]);
       }
     }
   };
@@ -314,7 +328,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // bwd_reduce_kernel); d = 32 db + 8 jj + 4 g .. + 3 of this lane's key
   if (n_ch > 1) {
     float* pk = a.part + ((((size_t)bkv * a.nkb + kblk) * a.nchunk + ch) * 2) * kBK * D +
-                (size_t)(j - k0) * D;
+                (size_t)(j - k0) * D + 32 * db0;
     float* pv = pk + (size_t)kBK * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -329,8 +343,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
   // ---- store: this lane's key row; d = 32 db + 8 jj + 4 g .. + 3
   if (j < Sk) {
-    T* dkr = reinterpret_cast<T*>(a.dk) + kv_off + (size_t)j * D;
-    T* dvr = reinterpret_cast<T*>(a.dv) + kv_off + (size_t)j * D;
+    T* dkr = reinterpret_cast<T*>(a.dk) + kv_off + (size_t)j * D + 32 * db0;
+    T* dvr = reinterpret_cast<T*>(a.dv) + kv_off + (size_t)j * D + 32 * db0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -391,7 +405,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dQ
 
 template <typename T, int D, int FLAGS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   constexpr bool MASK = (FLAGS & B_MASK) != 0;
@@ -646,7 +660,7 @@ hipError_t ATTN_CAT(launch_bwd_mfma_, ATTN_TAG)(const BwdProblem& p, hipStream_t
   a.chunk = p.chunk_items;
   a.nchunk = p.max_chunks;
   a.part = p.partials;
-  const int grid_kv = a.nbh_kv * a.nkb * a.nchunk;
+  const int grid_kv = a.nbh_kv * a.nkb * a.nchunk * kDHalves<ATTN_D>;
   const int grid_q = a.nbh * a.nqb;
   const bool mask = p.causal || p.wl >= 0 || p.wr >= 0 || (p.Sk % kBK) != 0 || (p.Sq % kBM) != 0;
   const int flags = (mask ? B_MASK : 0) | (softcap ? B_SOFTCAP : 0) | (p.alibi ? B_ALIBI : 0);

@@ -302,6 +302,9 @@ def test_bwd_check_accepts_valid_calls():
     # F32 / F64 (vector-ALU backward): head dims 32 to 256
     assert check_bwd(fwd(dtype=sdpa.ATTN_F32)) == OK
     assert check_bwd(fwd(dtype=sdpa.ATTN_F64, D=256)) == OK
+    # F16/BF16 (matrix cores): 64, 128 and 256
+    for dt in (sdpa.ATTN_BF16, sdpa.ATTN_F16):
+        assert check_bwd(fwd(dtype=dt, D=256)) == OK, dt
     assert check_bwd(fwd(dtype=sdpa.ATTN_F64, D=32)) == OK
 
 
@@ -317,7 +320,7 @@ def test_bwd_workspace_size():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=sdpa.ATTN_F64, D=80), HEAD_DIM),
-    (dict(dtype=9), DTYPE), (dict(D=256), HEAD_DIM), (dict(Hkv=3), GQA),
+    (dict(dtype=9), DTYPE), (dict(D=512), HEAD_DIM), (dict(D=32), HEAD_DIM), (dict(Hkv=3), GQA),
     (dict(softcap=-1.0), PARAM), (dict(has_k_len=1, k_len=130), PARAM),
 ])
 def test_bwd_check_rejects(kw, code):

@@ -94,6 +94,23 @@ def test_bwd_parity_other_dims(gpu_lib, dtype, D, case):
     run_bwd(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=800 + case, **kw)
 
 
+# Head dim 256: every dK/dV key block is covered by two workgroups, one per
+# half of the head dimension; the last case has enough query tiles per key
+# block to split them into chunks (float32 partials + their reduction).
+D256_CASES = [0, 1, 2, 4, 5]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", D256_CASES)
+def test_bwd_parity_d256(gpu_lib, dtype, case):
+    B, Hq, Hkv, Sq, Sk, kw = CASES[case]
+    run_bwd(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, 256, seed=850 + case, **kw)
+
+
+def test_bwd_d256_chunked_key_blocks(gpu_lib):
+    run_bwd(gpu_lib, "bf16", 1, 8, 2, 600, 300, 256, causal=True, seed=860)
+
+
 def test_bwd_deterministic(gpu_lib):
     (q, k, v, do, sl, scale), first = run_bwd(gpu_lib, "bf16", 1, 4, 2, 200, 333, 128,
                                               causal=True, seed=900)
@@ -179,6 +196,12 @@ def gpu_fwd_lse(sdpa, q, k, v, alibi, kw):
 def test_bwd_lse_parity(gpu_lib, dtype, D, case):
     B, Hq, Hkv, Sq, Sk, kw = CASES[case]
     run_bwd_lse(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, D, seed=1700 + case, **kw)
+
+
+@pytest.mark.parametrize("dtype,case", [("bf16", 1), ("f16", 5), ("bf16", 2)])
+def test_bwd_lse_parity_d256(gpu_lib, dtype, case):
+    B, Hq, Hkv, Sq, Sk, kw = CASES[case]
+    run_bwd_lse(gpu_lib, dtype, B, Hq, Hkv, Sq, Sk, 256, seed=1750 + case, **kw)
 
 
 def test_bwd_lse_deterministic_and_close_to_recompute(gpu_lib):
