@@ -17,9 +17,12 @@ prefill TFLOP/s; the decode figures ride along under ``decode``.  The CPU
 oracle is timed on a bounded sample of the same prefill workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --mode profile           # fixed launches for rocprofv3
-    python bench.py --summarize DIR          # text summary of rocprofv3 output
-    python bench.py --traffic FETCH WRITE    # HBM bytes per launch from two counter runs
+    python bench.py --mode profile [--launches N]   # the bench's steps, for rocprofv3
+    python bench.py --mode profile_prefill          # launches for the MFMA counter pass
+    python bench.py --mode profile_backward         # backward launches for rocprofv3
+    python bench.py --summarize DIR [--last N]      # kernel-trace summary (last N dispatches)
+    python bench.py --traffic FETCH WRITE           # HBM bytes per launch from two counter runs
+    python bench.py --mfma-util DIR --launches N    # MFMA busy per prefill workload
 """
 from __future__ import annotations
 
@@ -454,9 +457,11 @@ def bench(args):
 
 
 def profile(args):
-    """Fixed launches for rocprofv3: 10 prefills, 10 decodes, and a plain
-    256 MiB float32 copy kernel (read N, write N) that calibrates the HBM
-    byte counters."""
+    """Fixed launches for rocprofv3 in the bench's own order: the same clock
+    warm-up and warm-up steps, then ``--launches`` steps of (prefill, paged
+    decode), then a plain 256 MiB float32 copy kernel (read N, write N) that
+    calibrates the HBM byte counters.  ``--summarize DIR --last N`` averages
+    only the last N dispatches of each kernel, i.e. the timed steps."""
     import torch
     import scaled_dot_product_amd as sdpa
     import workloads as W
@@ -465,18 +470,21 @@ def profile(args):
     stream = torch.cuda.current_stream(dev)
     src = torch.randn(64 * 1024 * 1024, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(2):
+
+    def step():
         run_prefill(sdpa, wp, pre, stream)
         run_decode(sdpa, wd, dec, stream)
+    warm_s, warm_steps = clock_warm(torch, step, args.clock_warm)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     for _ in range(args.launches):
-        run_prefill(sdpa, wp, pre, stream)
-    for _ in range(args.launches):
-        run_decode(sdpa, wd, dec, stream)
+        step()
     for _ in range(args.launches):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_launches": args.launches, "prefill_flops": prefill_flops(wp),
+    print(json.dumps({"profile_launches": args.launches, "clock_warm_steps": warm_steps,
+                      "warmup_steps": args.warmup, "prefill_flops": prefill_flops(wp),
                       "decode_bytes": decode_bytes(wd, lens), "copy_bytes_each_way": src.numel() * 4,
                       "sources_sha256_16": sources_digest()}), flush=True)
 
@@ -509,15 +517,28 @@ PREFILL_CONFIGS = ("GQA_CAUSAL_2K", "LONG_MASKED_8K", "CHUNKED_PREFILL")
 
 
 def profile_prefill(args):
-    """Fixed launches of the three prefill workloads, one after the other
-    (the 2048-token causal GQA one, the long masked 8192-token one, chunked
-    f16 prefill), for the MFMA-utilisation counter pass."""
+    """Fixed launches for the MFMA-utilisation counter pass: the 2048-token
+    causal GQA prefill as the bench times it (clock warm-up, then
+    ``--launches`` steps of prefill + paged decode), then 2 + ``--launches``
+    launches each of the long masked 8192-token prefill and the chunked f16
+    prefill."""
     import torch
     import scaled_dot_product_amd as sdpa
     import workloads as W
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    for name in PREFILL_CONFIGS:
+    wp, wd, pre, dec, lens = setup(torch, sdpa, W, dev)
+
+    def step():
+        run_prefill(sdpa, wp, pre, stream)
+        run_decode(sdpa, wd, dec, stream)
+    clock_warm(torch, step, args.clock_warm)
+    torch.cuda.synchronize()
+    for _ in range(args.launches):
+        step()
+    torch.cuda.synchronize()
+    del pre, dec
+    for name in PREFILL_CONFIGS[1:]:
         w = getattr(W, name)
         q, k, v, alibi = W.dense_inputs(w)
         t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
@@ -530,11 +551,15 @@ def profile_prefill(args):
     print(json.dumps({"profile_launches": args.launches, "workloads": list(PREFILL_CONFIGS)}), flush=True)
 
 
-def mfma_util(path):
+def mfma_util(path, launches):
     """MFMA utilisation of each prefill launch class from a rocprofv3 counter
     run of --mode profile_prefill with SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES
     and GRBM_GUI_ACTIVE: busy cycles per SIMD over the kernel's GPU cycles (per
-    XCD), and the clock the GPU ran at (GPU cycles over the dispatch time)."""
+    XCD), and the clock the GPU ran at (GPU cycles over the dispatch time).
+    Dispatches are taken from the end of the run: the last 2 + L of the
+    chunked prefill, the 2 + L before them of the long masked prefill (the
+    first 2 of each skipped as warm-up), and the L timed bench steps' prefills
+    before those (L = ``launches``)."""
     import workloads as W
     files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -549,21 +574,28 @@ def mfma_util(path):
                                                                   int(r["Start_Timestamp"])) * 1e-9})
                 d[r["Counter_Name"]] = float(r["Counter_Value"])
     ids = sorted(rows)
-    per = len(ids) // len(PREFILL_CONFIGS)
+    L = launches
+    n_other = 2 + L
+    if len(ids) < L + 2 * n_other:
+        sys.exit(f"expected at least {L + 2 * n_other} prefill dispatches, found {len(ids)}")
+    groups = {PREFILL_CONFIGS[2]: ids[-n_other:][2:],
+              PREFILL_CONFIGS[1]: ids[-2 * n_other:-n_other][2:],
+              PREFILL_CONFIGS[0]: ids[-2 * n_other - L:-2 * n_other]}
     simds, xcds = 1024, 8
-    print("# commands (from the repository root, on one MI355X; $REPO is the repository root; "
-          "cd /tmp && export TMPDIR=/tmp first):")
+    print("# commands (from the repository root, on one MI355X; cd /tmp && export TMPDIR=/tmp first, "
+          "then back to the repository root):")
     print(f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
-          f"-d $REPO/{os.path.basename(path.rstrip('/'))} -- python $REPO/bench.py --mode profile_prefill")
-    print(f"#   python bench.py --mfma-util $REPO/{os.path.basename(path.rstrip('/'))} "
-          "> profiles/mfma_util_prefill.txt")
-    print("# MFMA utilisation per prefill workload (rocprofv3 counters, one pass; the first 2 launches of "
-          "each workload are warm-up and skipped)")
+          f"-d {path.rstrip('/')} -- python bench.py --mode profile_prefill --launches {L}")
+    print(f"#   python bench.py --mfma-util {path.rstrip('/')} --launches {L} > profiles/mfma_util_prefill.txt")
+    print("# MFMA utilisation per prefill workload (rocprofv3 counters, one pass).  The 2048-token prefill "
+          "is measured as the bench times it:")
+    print("# after a 1 s clock warm-up, each launch right after a paged decode; the other two run back to "
+          "back, their first 2 launches skipped")
     print("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs); "
           "clock = GPU cycles per XCD / dispatch time")
-    for i, name in enumerate(PREFILL_CONFIGS):
+    for name in PREFILL_CONFIGS:
         w = getattr(W, name)
-        sel = [rows[k] for k in ids[i * per:(i + 1) * per]][2:]
+        sel = [rows[k] for k in groups[name]]
         busy = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) for d in sel) / simds
         gpu = sum(d.get("GRBM_GUI_ACTIVE", 0) for d in sel) / xcds
         t = sum(d["t"] for d in sel)
@@ -572,25 +604,39 @@ def mfma_util(path):
               f"avg_us={t / len(sel) * 1e6:.1f} tflops={flops / t / 1e12:.1f}")
 
 
-def summarize(path):
+def summarize(path, last=None):
     """Print the per-kernel duration table of a rocprofv3 kernel-trace run
-    (its SQLite database, or the CSV stats when it wrote those)."""
+    (its SQLite database, or the CSV stats when it wrote those).  With
+    ``last`` (database only), each kernel's figures cover only its last
+    ``last`` dispatches, i.e. the timed launches after the warm-up."""
     dbs = glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
     csvs = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
     if not dbs and not csvs:
         sys.exit(f"no rocprofv3 output under {path}")
-    print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel")
+    print(f"{'calls':>6} {'avg_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10}  kernel")
     for fn in dbs:
         import sqlite3
         con = sqlite3.connect(fn)
-        rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration) "
-                           "from kernels group by name order by sum(duration) desc").fetchall()
-        for name, n, avg, lo, hi in rows:
-            print(f"{n:>6} {avg / 1e3:>10.2f} {lo / 1e3:>10.2f} {hi / 1e3:>10.2f}  {name[:160]}")
+        cur = con.execute("select * from kernels limit 1")
+        cols = [c[0] for c in cur.description]
+        start = next((c for c in ("start", "start_ns", "begin", "timestamp") if c in cols), None)
+        order = f" order by {start}" if start else ""
+        per = {}
+        for name, dur in con.execute(f"select name, duration from kernels{order}"):
+            per.setdefault(name, []).append(dur)
+        table = []
+        for name, durs in per.items():
+            if last:
+                durs = durs[-last:]
+            table.append((sum(durs), name, durs))
+        for _, name, durs in sorted(table, reverse=True):
+            a = np.asarray(durs, dtype=np.float64) / 1e3
+            print(f"{len(a):>6} {a.mean():>10.2f} {np.median(a):>10.2f} {a.min():>10.2f} {a.max():>10.2f}  "
+                  f"{name[:160]}")
     for fn in csvs:
         with open(fn) as f:
             for r in csv.DictReader(f):
-                print(f"{int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
+                print(f"{int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} {'-':>10} "
                       f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} "
                       f"{float(r.get('MaxNs', 0)) / 1e3:>10.2f}  {r.get('Name', '?')[:160]}")
 
@@ -627,13 +673,12 @@ def traffic(fetch_dir, write_dir, copy_bytes=64 * 1024 * 1024 * 4):
     pre = (fe["prefill"] * f_fac + wr["prefill"] * w_fac) * 1024.0
     dec_f = (fe["decode_main"] + fe["decode_merge"]) * f_fac * 1024.0
     dec_w = (wr["decode_main"] + wr["decode_merge"]) * w_fac * 1024.0
-    print("# commands (from the repository root, on one MI355X; $REPO is the repository root; "
-          "cd /tmp && export TMPDIR=/tmp first):")
+    print("# commands (from the repository root, on one MI355X; cd /tmp && export TMPDIR=/tmp first, "
+          "then back to the repository root):")
     for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        print(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $REPO/{os.path.basename(d.rstrip('/'))} "
-              "-- python $REPO/bench.py --mode profile")
-    names = [os.path.basename(d.rstrip("/")) for d in (fetch_dir, write_dir)]
-    print(f"#   python bench.py --traffic $REPO/{names[0]} $REPO/{names[1]} > profiles/hbm_traffic.txt")
+        print(f"#   rocprofv3 --pmc {ctr} --output-format csv -d {d.rstrip('/')} "
+              "-- python bench.py --mode profile")
+    print(f"#   python bench.py --traffic {fetch_dir.rstrip('/')} {write_dir.rstrip('/')} > profiles/hbm_traffic.txt")
     print("# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),")
     print("# each scaled by the factor that makes the copy kernel (torch.neg over 256 MiB float32,")
     print("# 256 MiB read + 256 MiB written) read its known size.")
@@ -668,15 +713,17 @@ def main():
                     help="seconds of untimed steps before the warm-up steps, so that the GPU "
                          "clocks have ramped to their sustained level")
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--last", type=int, default=None,
+                    help="with --summarize: average only each kernel's last N dispatches")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--mfma-util", metavar="DIR")
     args = ap.parse_args()
     if args.summarize:
-        return summarize(args.summarize)
+        return summarize(args.summarize, args.last)
     if args.traffic:
         return traffic(*args.traffic)
     if args.mfma_util:
-        return mfma_util(args.mfma_util)
+        return mfma_util(args.mfma_util, args.launches)
     if args.gpus != 1:
         sys.exit(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the attention "
                  "kernels here run on one GPU and the library has no multi-GPU path")

@@ -24,12 +24,16 @@ DEV = torch.device("cuda:0")
 # Bar for the gradients (the pages fix none): every gradient element is a sum
 # of products one of whose factors -- P or dS -- enters the matrix cores
 # rounded to the input dtype (unit roundoff u = 2^-8 for bf16, 2^-11 for f16),
-# and the result is rounded once more to the dtype.  The tensor relative L2
-# error is therefore a small multiple of u; 3u leaves room for the accumulated
-# roundings.  Element-wise, cancellation in dS = P (dP - rowsum(P dP)) can make
-# a small element's relative error large, so the element bar is taken relative
-# to the largest element of the tensor: 6u of it.
+# and the result is rounded once more to the dtype, so the tensor relative L2
+# error is of the order of u.  Element-wise, cancellation in
+# dS = P (dP - rowsum(P dP)) can make a small element's relative error large,
+# so the element bar is taken relative to the largest element of the tensor.
+# Measured over every gradient tensor of this file (bf16 and f16, head dims
+# 64, 128 and 256, both entry points): relative L2 at most 0.80u, element
+# error at most 1.53u of the largest element.  The bars, 1.25u and 2.5u, keep
+# about 1.6x of margin over that, so a regression of 2x fails.
 U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+REL_BAR, EL_BAR = 1.25, 2.5
 
 
 def compare_grad(got, ref, dtype, what):
@@ -41,9 +45,9 @@ def compare_grad(got, ref, dtype, what):
     nref = np.linalg.norm(ref)
     rel = np.linalg.norm(g - ref) / nref if nref > 0 else np.linalg.norm(g)
     announce(f"{what}: rel L2 {rel:.3g}, max err {err.max(initial=0):.3g} of max |ref| {scale:.3g}")
-    assert rel <= 3 * U[dtype], f"{what}: relative L2 {rel:.3g} > {3 * U[dtype]:.3g}"
-    assert err.max(initial=0.0) <= 6 * U[dtype] * scale + 1e-6, \
-        f"{what}: max err {err.max():.3g} > {6 * U[dtype]:.3g} * {scale:.3g}"
+    assert rel <= REL_BAR * U[dtype], f"{what}: relative L2 {rel:.3g} > {REL_BAR * U[dtype]:.3g}"
+    assert err.max(initial=0.0) <= EL_BAR * U[dtype] * scale + 1e-6, \
+        f"{what}: max err {err.max():.3g} > {EL_BAR * U[dtype]:.3g} * {scale:.3g}"
 
 
 def run_bwd(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None, softcap=None,
