@@ -290,15 +290,28 @@ def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
     (the binding marshals the arguments and launches, host + kernel) and HIP
     graph replay of the same call (kernel only, no host marshalling), both as
     wall time per call with a synchronisation after each call; and the
-    kernel's own median event time.  For the paged decode workload and the
-    chunked f16 prefill (512 queries, a short prefill)."""
+    kernel's own median event time.  For the paged decode workload, the
+    chunked f16 prefill (512 queries, a short prefill), and a small decode
+    (4 sequences of 1024 tokens, the same heads and pool layout) whose kernel
+    is short enough for the host cost to matter."""
     w = W.CHUNKED_PREFILL
     q, k, v, _ = W.dense_inputs(w)
     t = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
     t["out"] = torch.empty_like(t["q"])
+    ws = W.Paged("paged_decode_bf16_b4_h32x8_d128_ctx1024_bs64", "bf16", 4, 32, 8, 128, 64, 1024, 1024,
+                 8, 16, seed=1006)
+    sq, skp, svp, stab, slens, _ = W.paged_inputs(ws)
+    small = dict(q=sq.to(dev), k_pool=skp.to(dev), v_pool=svp.to(dev), block_table=stab.to(dev),
+                 seq_lens=slens.to(dev))
+    small["out"] = torch.empty_like(small["q"])
+    sp = sdpa.attn_paged_params(tuple(sq.shape), tuple(skp.shape), stab.shape[1], sq.dtype,
+                                num_splits=ws.num_splits)
+    small["workspace"] = torch.empty(max(1, sdpa.attn_paged_decode_workspace_size(sp)), dtype=torch.uint8,
+                                     device=dev)
     cases = {
         W.PAGED_DECODE.name: lambda s: run_decode(sdpa, wd, dec, s),
         w.name: lambda s: run_dense(sdpa, w, t, None, s),
+        ws.name: lambda s: run_decode(sdpa, ws, small, s),
     }
     res = {}
     for name, fn in cases.items():
@@ -336,7 +349,7 @@ def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
                      "graph_us_per_call": modes["graph"],
                      "note": "wall time per call with a synchronisation after each call"}
         del g
-    del t
+    del t, small
     return res
 
 
