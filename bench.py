@@ -286,9 +286,10 @@ def clock_warm(torch, step, seconds):
 
 
 def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
-    """Per-call cost of a launch that the caller waits for, in two modes: eager
-    (the binding marshals the arguments and launches, host + kernel) and HIP
-    graph replay of the same call (kernel only, no host marshalling), both as
+    """Per-call cost of a launch that the caller waits for, in three modes:
+    eager (the binding marshals the arguments and launches, host + kernel),
+    HIP graph replay of the same call (kernel only, no host marshalling) and
+    the binding's prepared plan (one C call), all as
     wall time per call with a synchronisation after each call; and the
     kernel's own median event time.  For the paged decode workload, the
     chunked f16 prefill (512 queries, a short prefill), and a small decode
@@ -308,13 +309,19 @@ def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
                                 num_splits=ws.num_splits)
     small["workspace"] = torch.empty(max(1, sdpa.attn_paged_decode_workspace_size(sp)), dtype=torch.uint8,
                                      device=dev)
+    def decode_plan(wk, d, s):
+        return sdpa.PagedDecodePlan(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                    None, d["out"], softmax_scale=wk.scale, num_splits=wk.num_splits,
+                                    workspace=d["workspace"], stream=s)
     cases = {
-        W.PAGED_DECODE.name: lambda s: run_decode(sdpa, wd, dec, s),
-        w.name: lambda s: run_dense(sdpa, w, t, None, s),
-        ws.name: lambda s: run_decode(sdpa, ws, small, s),
+        W.PAGED_DECODE.name: (lambda s: run_decode(sdpa, wd, dec, s), lambda s: decode_plan(wd, dec, s)),
+        w.name: (lambda s: run_dense(sdpa, w, t, None, s),
+                 lambda s: sdpa.AttnFwdPlan(t["q"], t["k"], t["v"], None, t["out"], softmax_scale=w.scale,
+                                            causal=w.causal, stream=s)),
+        ws.name: (lambda s: run_decode(sdpa, ws, small, s), lambda s: decode_plan(ws, small, s)),
     }
     res = {}
-    for name, fn in cases.items():
+    for name, (fn, make_plan) in cases.items():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -335,8 +342,9 @@ def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
             e1.record(stream)
             torch.cuda.synchronize()
             kern.append(e0.elapsed_time(e1) * 1e3)
+        plan = make_plan(stream)
         modes = {}
-        for mode, call in (("eager", lambda: fn(stream)), ("graph", g.replay)):
+        for mode, call in (("eager", lambda: fn(stream)), ("graph", g.replay), ("plan", plan.run)):
             for _ in range(10):
                 call()
                 torch.cuda.synchronize()
@@ -346,9 +354,10 @@ def host_overhead(torch, sdpa, W, dev, wd, dec, calls=200):
                 torch.cuda.synchronize()
             modes[mode] = (time.perf_counter() - t0) / calls * 1e6
         res[name] = {"kernel_us": float(np.median(kern)), "eager_us_per_call": modes["eager"],
-                     "graph_us_per_call": modes["graph"],
-                     "note": "wall time per call with a synchronisation after each call"}
-        del g
+                     "graph_us_per_call": modes["graph"], "plan_us_per_call": modes["plan"],
+                     "note": "wall time per call with a synchronisation after each call; plan = the "
+                             "binding's prepared call (checks and marshalling done once)"}
+        del g, plan
     del t, small
     return res
 

@@ -20,6 +20,11 @@ fails to load, every call raises.
     attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
                               out=None, *, softmax_scale=None, softcap=None,
                               num_splits=8, error_flag=None, stream=None)
+
+For calls repeated on the same tensors (a serving loop that rewrites q,
+seq_lens and block_table in place each step), ``PagedDecodePlan`` and
+``AttnFwdPlan`` do the checks and the marshalling once; their ``run()`` is one
+call into the library.
 """
 from __future__ import annotations
 
@@ -31,7 +36,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "AttnError", "library", "LIB_PATH",
+    "AttnError", "library", "LIB_PATH", "PagedDecodePlan", "AttnFwdPlan",
     "attn_fwd", "attn_fwd_check", "attn_fwd_params", "attn_fwd_lse", "attn_fwd_lse_check",
     "attn_paged_decode", "attn_paged_decode_check", "attn_paged_decode_workspace_size",
     "attn_paged_decode_noalloc", "DECODE_SCRATCH_BYTES",
@@ -421,6 +426,74 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=
     if st != 0:
         raise AttnError(st, "attn_paged_decode")
     return out
+
+
+class PagedDecodePlan:
+    """``attn_paged_decode`` with its arguments checked and marshalled once.
+
+    Takes the arguments of :func:`attn_paged_decode` and keeps references to
+    its tensors (``out`` and the workspace are allocated here when not given).
+    Between runs the caller may change the tensors' contents in place -- the
+    next token's ``q``, longer ``seq_lens``, new ``block_table`` entries --
+    but never their shapes, dtypes or storage.  ``run()`` makes the one C call
+    (which still validates the arguments host-side) on the stream given here
+    and returns ``out``.  The host cost per step is then that call alone, not
+    the per-call Python checks.
+    """
+
+    def __init__(self, q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
+                 softmax_scale=None, softcap=None, num_splits=8, workspace=None,
+                 error_flag=None, stream=None):
+        lib = library()
+        dev = q.device
+        p, out = _paged_decode_args(q, k_pool, v_pool, block_table, seq_lens, alibi, out,
+                                    workspace, error_flag, softmax_scale, softcap, num_splits)
+        need = attn_paged_decode_workspace_size(p)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        ptrs = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                _ptr(alibi), _ptr(out), _ptr(workspace))
+        st = lib.attn_paged_decode_check(*ptrs, ws_bytes, _ptr(error_flag), ctypes.byref(p))
+        if st != 0:
+            raise AttnError(st, "attn_paged_decode")
+        self.out = out
+        self._keep = (q, k_pool, v_pool, block_table, seq_lens, alibi, workspace, error_flag, p)
+        self._fn = lib.attn_paged_decode
+        self._args = (*ptrs, ws_bytes, _ptr(error_flag), ctypes.byref(p), _stream_handle(stream, dev))
+
+    def run(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise AttnError(st, "attn_paged_decode")
+        return self.out
+
+
+class AttnFwdPlan:
+    """``attn_fwd`` with its arguments checked and marshalled once (the same
+    contract as :class:`PagedDecodePlan`: tensors keep their shapes and
+    storage between runs; ``run()`` is one C call on the stream given here and
+    returns ``out``)."""
+
+    def __init__(self, q, k, v, alibi=None, out=None, *, softmax_scale=None, causal=False,
+                 window_left=None, window_right=None, softcap=None, k_len=None, stream=None):
+        lib = library()
+        dev, out, p = _fwd_args(q, k, v, alibi, out, softmax_scale, causal, window_left,
+                                window_right, softcap, k_len)
+        ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alibi), _ptr(out))
+        st = lib.attn_fwd_check(*ptrs, ctypes.byref(p))
+        if st != 0:
+            raise AttnError(st, "attn_fwd")
+        self.out = out
+        self._keep = (q, k, v, alibi, p)
+        self._fn = lib.attn_fwd
+        self._args = (*ptrs, ctypes.byref(p), _stream_handle(stream, dev))
+
+    def run(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise AttnError(st, "attn_fwd")
+        return self.out
 
 
 DECODE_SCRATCH_BYTES = 32 << 20  # ATTN_DECODE_SCRATCH_BYTES in attn.h
