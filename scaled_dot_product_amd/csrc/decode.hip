@@ -111,9 +111,10 @@ __device__ __forceinline__ int swz_v(int r) {
 // compiler neither counts them nor inserts waits of its own (they have no
 // register result): the loop below keeps a fixed number of copies in flight
 // and waits, with wait_vmem_le, for exactly the ones it is about to read.
+// The K/V pool is read once per decode, so the copies are non-temporal.
 __device__ __forceinline__ void asm_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, int voff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
 }
 // Waits until at most N of this wave's vector-memory operations are in flight.
@@ -559,7 +560,8 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
     const T* Kp = reinterpret_cast<const T*>(a.kp) + (size_t)cur.kvh * D;
     const T* Vp = reinterpret_cast<const T*>(a.vp) + (size_t)cur.kvh * D;
 
-    // Copies of block j (window-relative jw for its page id) into ring slot u;
+    // Copies of block j (window-relative jw for its page id) into ring slot u,
+    // non-temporal (the pool is read once);
     // a block that is not `live` is padding: it keeps every block followed by
     // exactly PF fetches, but reads nothing.
     auto fetch = [&](int u, int j, int jw, bool live) {
@@ -575,12 +577,12 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kr[u][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, (int)((hl * tok_stride + 32 * ks + 8 * g) * sizeof(T)), 0, 0);
+            rk, (int)((hl * tok_stride + 32 * ks + 8 * g) * sizeof(T)), 0, kLoadStream);
       u32x4* vs_ = vslot(u);
 #pragma unroll
       for (int i = 0; i < CPB; ++i) {
         const int r = crow + ROWS * i;
-        dma16(rv, vs_ + i * 64, (int)((r * tok_stride + 8 * (cch ^ swz_v<D>(r))) * sizeof(T)));
+        dma16<kLoadStream>(rv, vs_ + i * 64, (int)((r * tok_stride + 8 * (cch ^ swz_v<D>(r))) * sizeof(T)));
       }
       valid[u] = ok ? (nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u)) : 0u;
     };

@@ -144,10 +144,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes < 0 ? 0 : bytes, 0x00020000);
 }
 
+// Cache-policy operand of the buffer loads: non-temporal (streamed data that
+// is read once; the caches do not keep it at the expense of reused lines).
+constexpr int kLoadStream = 2;
+
 // Asynchronous copy of 16 bytes per lane from a buffer to LDS: lane l's bytes
 // land at lds_base + 16 * l (lds_base must be the same in every lane).
+// POLICY is the cache-policy operand (0: default, kLoadStream: read once).
+template <int POLICY = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_base, int byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)lds_base, 16, byte_off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)lds_base, 16, byte_off, 0, 0, POLICY);
 }
 
 // Waits until this wave's outstanding vector-memory loads (including the
