@@ -120,3 +120,44 @@ def test_random_varlen_prefill(gpu_lib, seed):
     out = gpu_run(gpu_lib, c, **kw)
     ref = oracle_run(c, **kw)
     compare(out, ref, DT[dtype], f"seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_backward(gpu_lib, seed):
+    """attn_bwd (or attn_bwd_lse from a saved forward) on random shapes and
+    options: bf16/f16 on the matrix cores at the relative bars of the backward
+    tests, f32/f64 on the vector ALU at theirs."""
+    from test_bwd_gpu import compare_grad, compare_grad_valu
+    c = dense_config(10_000 + seed)
+    rng = np.random.default_rng(9900 + seed)
+    c["dtype"] = ["bf16", "f16", "f32", "f64"][rng.integers(4)]
+    c["D"] = int(rng.choice({"bf16": (64, 128, 256), "f16": (64, 128, 256), "f32": (32, 64, 128, 256),
+                            "f64": (32, 64, 128)}[c["dtype"]]))
+    c["amp"] = min(c["amp"], 1.0)
+    c["Sq"], c["Sk"] = min(c["Sq"], 300), min(c["Sk"], 300)
+    c["k_len"] = None
+    saved = bool(rng.random() < 0.5)
+    announce(f"random backward seed {seed} (saved forward: {saved}): {c}")
+    q, k, v = W.random_dense(c["dtype"], c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sk"], c["D"], 800 + seed,
+                             c["amp"])
+    do = W.random_dense(c["dtype"], c["B"], c["Hq"], c["Hkv"], c["Sq"], 1, c["D"], 850 + seed, 1.0)[0]
+    sl = torch.from_numpy(W.alibi_slopes(c["Hq"])) if c["alibi"] else None
+    scale = float(np.float32(1.0 / math.sqrt(c["D"])))
+    kw = dict(softmax_scale=scale, causal=c["causal"], window_left=c["wl"], window_right=c["wr"],
+              softcap=c["softcap"])
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    sld = None if sl is None else sl.to(DEV)
+    if saved:
+        out, lse = gpu_lib.attn_fwd_lse(qd, kd, vd, sld, **kw)
+        grads = gpu_lib.attn_bwd_lse(qd, kd, vd, out, lse, dod, sld, **kw)
+    else:
+        grads = gpu_lib.attn_bwd(qd, kd, vd, dod, sld, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward_f64(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), scale=scale,
+                                   causal=c["causal"], window_left=c["wl"], window_right=c["wr"],
+                                   softcap=c["softcap"], alibi=None if sl is None else W.to_f64(sl))
+    for nm, got, r in zip(("dq", "dk", "dv"), grads, ref):
+        if c["dtype"] in ("bf16", "f16"):
+            compare_grad(got, r, c["dtype"], f"seed {seed} {nm}")
+        else:
+            compare_grad_valu(got, r, c["dtype"], f"seed {seed} {nm}")
