@@ -13,19 +13,21 @@
 // Two kernels, each owning what it writes, so no atomics and a fixed order:
 //
 //  * bwd_dkdv_kernel: a workgroup owns 128 keys of one (sequence, KV head),
-//    each of its 4 waves 32 of them.  It walks every query head of the group
-//    and every 32-query tile that can see those keys; the tiles of Q, dO and
-//    the row statistics are copied global -> LDS asynchronously, double
-//    buffered, shared by the 4 waves.  Per tile and wave, with the wave's
-//    keys in the accumulator columns (one key per lane):
+//    each of its 8 waves 16 of them (two waves per SIMD: the state of a
+//    16-key wave fits half the register file).  It walks every query head of
+//    the group and every 32-query tile that can see those keys; the tiles of
+//    Q, dO and the row statistics are copied global -> LDS asynchronously,
+//    double buffered, shared by the 8 waves.  Per tile and wave, on the
+//    16x16x32 instruction with the wave's keys in the accumulator columns
+//    (lane l: key l % 16):
 //      S  = Q K^T   (Q rows from LDS, K in registers)     8 MFMAs at D = 128
 //      dP = dO V^T  (dO rows from LDS, V in registers)    8
 //      dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read through the
 //      LDS transpose read and P, dS already in the B-operand layout   8 + 8
-//    At D = 256 the two accumulators would not fit the register file: there
-//    each key block gets two workgroups, each accumulating the dK/dV columns
-//    of one half of the head dimension (both still contract S and dP over all
-//    of it, so S and dP are computed twice).
+//    At D = 256 the two accumulators would not fit: there each key block gets
+//    two workgroups, each accumulating the dK/dV columns of one half of the
+//    head dimension (both still contract S and dP over all of it, so S and dP
+//    are computed twice).
 //  * bwd_dq_kernel: the forward kernel's shape -- 4 waves x 32 query rows, K
 //    and V tiles of 64 keys through LDS -- with, per tile,
 //      S^T = K Q^T and dP^T = V dO^T (Q and dO in registers)          16 + 16
@@ -44,11 +46,13 @@
 namespace attn {
 namespace {
 
-constexpr int kNW = 4;
+constexpr int kNW = 4;         // dQ: waves per workgroup
 constexpr int kThreads = kNW * 64;
 constexpr int kBQ = 32;       // dK/dV: queries per tile
-constexpr int kKW = 32;       // dK/dV: keys per wave
-constexpr int kBK = kNW * kKW;  // dK/dV: keys per workgroup
+constexpr int kKW = 16;       // dK/dV: keys per wave
+constexpr int kKvW = 8;       // dK/dV: waves per workgroup (two per SIMD)
+constexpr int kKvThreads = kKvW * 64;
+constexpr int kBK = kKvW * kKW;  // dK/dV: keys per workgroup
 constexpr int kBN = 64;       // dQ: keys per tile
 constexpr int kQW = 32;       // dQ: query rows per wave
 constexpr int kBM = kNW * kQW;  // dQ: query rows per workgroup
@@ -149,21 +153,64 @@ __device__ __forceinline__ void copy_tile(const T* base, int rows_left, u32x4* d
 
 // ---------------------------------------------------------------- dK, dV
 
+// A = X^T (16 d rows x the tile's 32 queries) for the 16x16x32 instruction,
+// through the LDS transpose read: lane l (lane group G = l / 16) takes d row
+// 16 db + l % 16, and its 8 k-slots are tile rows 4 G .. 4 G + 3, then
+// 16 + 4 G .. + 3 -- the rows the same lane holds in the 16x16 accumulator
+// layout of S and dP (rows 4 G .. + 3 of each 16-row block), so P and dS are
+// the B operands as they stand.  Tile rows are D elements, chunks swizzled.
+template <typename T, int D>
+__device__ __forceinline__ u32x4 tr16_operand(const T* X, int db, int lane) {
+  const int G = lane >> 4;
+  const int r = (lane & 15) >> 2, p = lane & 3;  // row r, piece p of a 4 x 16 block
+  const int row0 = 4 * G + r, row1 = 16 + 4 * G + r;
+  const int col = 16 * db + 4 * p;
+  const int c0 = ((col >> 3) ^ swz<D>(row0)) * 8 + (col & 7);
+  const int c1 = ((col >> 3) ^ swz<D>(row1)) * 8 + (col & 7);
+  const u32x2 lo = lds_read_tr16(X + row0 * D + c0);
+  const u32x2 hi = lds_read_tr16(X + row1 * D + c1);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Asynchronous copy of the 32 rows of Q and of dO that start at q and dout
+// (rows past `rows_left` read zero) into their swizzled LDS tiles, by all
+// threads of a dK/dV workgroup; each wave copies 64 chunks of one tensor.
+template <typename T, int D>
+__device__ __forceinline__ void copy_q_do(const T* q, const T* dout, int rows_left, u32x4* qd, u32x4* od,
+                                          int tid, int wave) {
+  constexpr int NC = D / 8;
+  constexpr int TC = kBQ * NC;                 // chunks per tensor
+  constexpr int CPT = 2 * TC / kKvThreads;     // chunks per thread
+  static_assert(CPT * kKvThreads == 2 * TC && TC % 64 == 0, "tiles must split evenly over the waves");
+  const int bytes = rows_left * D * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc32(q, bytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc32(dout, bytes);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c0 = i * kKvThreads + wave * 64;   // this wave's first chunk (wave-uniform)
+    const bool is_o = c0 >= TC;
+    const int cc = (is_o ? c0 - TC : c0) + (tid & 63);
+    const int r = cc / NC, pc = cc % NC;
+    const int off = (r * D + (pc ^ swz<D>(r)) * 8) * (int)sizeof(T);
+    dma16(is_o ? ro : rq, (is_o ? od : qd) + (is_o ? c0 - TC : c0), off);
+  }
+}
+
 template <typename T, int D, int FLAGS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   constexpr bool MASK = (FLAGS & B_MASK) != 0;
   constexpr bool SOFTCAP = (FLAGS & B_SOFTCAP) != 0;
   constexpr bool ALIBI = (FLAGS & B_ALIBI) != 0;
   constexpr int NC = D / 8;
-  constexpr int KS = D / 16;
+  constexpr int KS = D / 32;       // 16x16x32 steps of S and dP over d
   constexpr int TC = kBQ * NC;
   // D = 256: each workgroup accumulates the dK, dV columns of one half of the
   // head dimension (S and dP are still contracted over all of it), which keeps
-  // the accumulators within the register file
+  // the accumulators within two waves' share of the register file
   constexpr int NH = kDHalves<D>;
-  constexpr int DB = D / 32 / NH;  // 32-column blocks of dK^T, dV^T per workgroup
+  constexpr int DB = D / 16 / NH;  // 16-column blocks of dK^T, dV^T per workgroup
 
   __shared__ u32x4 qbuf0[TC], qbuf1[TC], obuf0[TC], obuf1[TC];
   __shared__ float2 sbuf0[kBQ], sbuf1[kBQ];
@@ -171,13 +218,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5;
-  const int ln = lane & 31;
+  const int G = lane >> 4;  // lane group: accumulator rows 4 G .. 4 G + 3 of each 16-row block
+  const int n = lane & 15;  // this lane's key within the wave's 16; also its A-operand row
 
   // ---- work item: chunk ch of key block kblk of (b, kvh); low key blocks
   // see the most queries under a causal mask, so they go first
   const int dh = NH > 1 ? (int)(blockIdx.x % NH) : 0;  // half of the head dimension
-  const int db0 = dh * DB;                              // its first 32-column block
+  const int db0 = dh * DB;                              // its first 16-column block
   const int id = blockIdx.x / NH;
   const int kc = id / a.nbh_kv;
   const int bkv = id - kc * a.nbh_kv;
@@ -188,17 +235,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
   const int k0 = kblk * kBK;
   const int j0 = k0 + wave * kKW;  // this wave's first key
-  const int j = j0 + ln;           // this lane's key
+  const int j = j0 + n;            // this lane's key
   const size_t kv_off = (size_t)(b * a.Hkv + kvh) * Sk * D;
   const T* K = reinterpret_cast<const T*>(a.k) + kv_off;
   const T* V = reinterpret_cast<const T*>(a.v) + kv_off;
 
-  // K and V rows of this lane's key as B operands: chunk 2 s + g
+  // K and V rows of this lane's key as B operands: step s is d = 32 s + 8 G .. + 7
   u32x4 kf[KS], vf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    kf[s] = j < Sk ? load16(K + (size_t)j * D + 16 * s + 8 * g) : zero_u32x4();
-    vf[s] = j < Sk ? load16(V + (size_t)j * D + 16 * s + 8 * g) : zero_u32x4();
+    kf[s] = j < Sk ? load16(K + (size_t)j * D + 32 * s + 8 * G) : zero_u32x4();
+    vf[s] = j < Sk ? load16(V + (size_t)j * D + 32 * s + 8 * G) : zero_u32x4();
   }
 
   // admissible iff lo <= j - i' <= hi
@@ -229,11 +276,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     return q0 + kBQ <= Sq && j0 + kKW <= Sk && dlo >= lo && dhi <= hi;
   };
 
-  floatx16 dkt[DB], dvt[DB];
+  floatx4 dkt[DB], dvt[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    dkt[db] = floatx16{};
-    dvt[db] = floatx16{};
+    dkt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dvt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
   // item it of this chunk: flattened index it0 + it over (head, tile)
@@ -242,8 +289,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto copy_item = [&](int it, u32x4* qd, u32x4* od, float2* sd) {
     const int h = item_head(it), q0 = item_q0(it);
     const size_t row0 = (size_t)(b * a.Hq + h) * Sq + q0;
-    copy_tile<T, D, kBQ>(reinterpret_cast<const T*>(a.q) + row0 * D, Sq - q0, qd, tid, wave);
-    copy_tile<T, D, kBQ>(reinterpret_cast<const T*>(a.dout) + row0 * D, Sq - q0, od, tid, wave);
+    copy_q_do<T, D>(reinterpret_cast<const T*>(a.q) + row0 * D, reinterpret_cast<const T*>(a.dout) + row0 * D,
+                    Sq - q0, qd, od, tid, wave);
     if (wave == 0) {
       // 32 (LSE, dO.O) pairs: one dword per lane
       const __amdgpu_buffer_rsrc_t rs = make_rsrc32(a.stats + row0, (Sq - q0) * 8);
@@ -254,57 +301,60 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](int it, const u32x4* qs, const u32x4* os, const float2* ss) {
     const int h = item_head(it), q0 = item_q0(it);
     if (!live(q0)) return;
-    // S = Q K^T, dP = dO V^T: 32 queries (rows) x this wave's 32 keys (lanes)
-    floatx16 s = floatx16{}, dp = floatx16{};
+    // S = Q K^T, dP = dO V^T in two 16-query blocks: block qb holds queries
+    // 16 qb + 4 G .. + 3 (rows) x this wave's 16 keys (lane n)
+    floatx4 s[2], dp[2];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const int c = (2 * st + g) ^ swz<D>(ln);
-      s = E::mma32(qs[ln * NC + c], kf[st], s);
-      dp = E::mma32(os[ln * NC + c], vf[st], dp);
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dp[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const int r = 16 * qb + n;  // A operand: query row 16 qb + l % 16, d = 32 st + 8 G .. + 7
+        const int c = (4 * st + G) ^ swz<D>(r);
+        s[qb] = E::mma16(qs[r * NC + c], kf[st], s[qb]);
+        dp[qb] = E::mma16(os[r * NC + c], vf[st], dp[qb]);
+      }
     }
     float slope_l2 = 0.f;
     if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
     const bool need_mask = MASK && !full(q0);
     const float4* sp = reinterpret_cast<const float4*>(ss);
-    uint32_t pp[8], dsp[8];
+    // P and dS as the B operands of the dV and dK products: k-slots 8 G + 4 qb
+    // + c are query rows 16 qb + 4 G + c
+    u32x4 pf, df;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      // accumulator rows 8 rr + 4 g + 0..3: statistics of 4 consecutive rows
-      const float4 s01 = sp[4 * rr + 2 * g], s23 = sp[4 * rr + 2 * g + 1];
+    for (int qb = 0; qb < 2; ++qb) {
+      // statistics of rows 16 qb + 4 G .. + 3
+      const float4 s01 = sp[8 * qb + 2 * G], s23 = sp[8 * qb + 2 * G + 1];
       const float lse2[4] = {s01.x, s01.z, s23.x, s23.z};
       const float dlt[4] = {s01.y, s01.w, s23.y, s23.w};
       float pv[4], dsv[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int r = 4 * rr + c;
-        const int qrow = q0 + 8 * rr + 4 * g + c;
+        const int qrow = q0 + 16 * qb + 4 * G + c;
         const int rel = j - (qrow + off);
         float t;
-        float x = transform<SOFTCAP, ALIBI>(s[r], a, slope_l2, rel, t);
+        float x = transform<SOFTCAP, ALIBI>(s[qb][c], a, slope_l2, rel, t);
         if (need_mask && (qrow >= Sq || j >= Sk || rel < lo || rel > hi)) x = kNegInf;
         const float p = fast_exp2(x - lse2[c]);
-        float d = p * (dp[r] - dlt[c]);
+        float d = p * (dp[qb][c] - dlt[c]);
         if constexpr (SOFTCAP) d *= 1.f - t * t;
         pv[c] = p;
         dsv[c] = d;
       }
-      pp[2 * rr] = E::pack2(pv[0], pv[1]);
-      pp[2 * rr + 1] = E::pack2(pv[2], pv[3]);
-      dsp[2 * rr] = E::pack2(dsv[0], dsv[1]);
-      dsp[2 * rr + 1] = E::pack2(dsv[2], dsv[3]);
+      pf[2 * qb] = E::pack2(pv[0], pv[1]);
+      pf[2 * qb + 1] = E::pack2(pv[2], pv[3]);
+      df[2 * qb] = E::pack2(dsv[0], dsv[1]);
+      df[2 * qb + 1] = E::pack2(dsv[2], dsv[3]);
     }
     // dV^T += dO^T P, dK^T += Q^T dS over the tile's 32 queries
     const T* Os = reinterpret_cast<const T*>(os);
     const T* Qs = reinterpret_cast<const T*>(qs);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 pf = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
-      const u32x4 df = {dsp[4 * ks], dsp[4 * ks + 1], dsp[4 * ks + 2], dsp[4 * ks + 3]};
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dvt[db] = E::mma32(tr_operand<T, D>(Os, ks, db0 + db, lane), pf, dvt[db]);
-        dkt[db] = E::mma32(tr_operand<T, D>(Qs, ks, db0 + db, lane), df, dkt[db]);
-      }
+    for (int db = 0; db < DB; ++db) {
+      dvt[db] = E::mma16(tr16_operand<T, D>(Os, db0 + db, lane), pf, dvt[db]);
+      dkt[db] = E::mma16(tr16_operand<T, D>(Qs, db0 + db, lane), df, dkt[db]);
     }
   };
 
@@ -325,38 +375,30 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // ---- a block of several chunks: this chunk's float32 partials (summed by
-  // bwd_reduce_kernel); d = 32 db + 8 jj + 4 g .. + 3 of this lane's key
+  // bwd_reduce_kernel); this lane's key row, d = 16 db + 4 G .. + 3
   if (n_ch > 1) {
     float* pk = a.part + ((((size_t)bkv * a.nkb + kblk) * a.nchunk + ch) * 2) * kBK * D +
-                (size_t)(j - k0) * D + 32 * db0;
+                (size_t)(j - k0) * D + 16 * db0;
     float* pv = pk + (size_t)kBK * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        *reinterpret_cast<floatx4*>(pk + 32 * db + 8 * jj + 4 * g) =
-            floatx4{dkt[db][4 * jj], dkt[db][4 * jj + 1], dkt[db][4 * jj + 2], dkt[db][4 * jj + 3]};
-        *reinterpret_cast<floatx4*>(pv + 32 * db + 8 * jj + 4 * g) =
-            floatx4{dvt[db][4 * jj], dvt[db][4 * jj + 1], dvt[db][4 * jj + 2], dvt[db][4 * jj + 3]};
-      }
+    for (int db = 0; db < DB; ++db) {
+      *reinterpret_cast<floatx4*>(pk + 16 * db + 4 * G) = dkt[db];
+      *reinterpret_cast<floatx4*>(pv + 16 * db + 4 * G) = dvt[db];
+    }
     return;
   }
-  // ---- store: this lane's key row; d = 32 db + 8 jj + 4 g .. + 3
+  // ---- store: this lane's key row, d = 16 db + 4 G .. + 3
   if (j < Sk) {
-    T* dkr = reinterpret_cast<T*>(a.dk) + kv_off + (size_t)j * D + 32 * db0;
-    T* dvr = reinterpret_cast<T*>(a.dv) + kv_off + (size_t)j * D + 32 * db0;
+    T* dkr = reinterpret_cast<T*>(a.dk) + kv_off + (size_t)j * D + 16 * db0;
+    T* dvr = reinterpret_cast<T*>(a.dv) + kv_off + (size_t)j * D + 16 * db0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2 wk, wv;
-        wk[0] = E::pack2(dkt[db][4 * jj] * a.scale, dkt[db][4 * jj + 1] * a.scale);
-        wk[1] = E::pack2(dkt[db][4 * jj + 2] * a.scale, dkt[db][4 * jj + 3] * a.scale);
-        wv[0] = E::pack2(dvt[db][4 * jj], dvt[db][4 * jj + 1]);
-        wv[1] = E::pack2(dvt[db][4 * jj + 2], dvt[db][4 * jj + 3]);
-        *reinterpret_cast<u32x2*>(dkr + 32 * db + 8 * jj + 4 * g) = wk;
-        *reinterpret_cast<u32x2*>(dvr + 32 * db + 8 * jj + 4 * g) = wv;
-      }
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 wk = {E::pack2(dkt[db][0] * a.scale, dkt[db][1] * a.scale),
+                        E::pack2(dkt[db][2] * a.scale, dkt[db][3] * a.scale)};
+      const u32x2 wv = {E::pack2(dvt[db][0], dvt[db][1]), E::pack2(dvt[db][2], dvt[db][3])};
+      *reinterpret_cast<u32x2*>(dkr + 16 * db + 4 * G) = wk;
+      *reinterpret_cast<u32x2*>(dvr + 16 * db + 4 * G) = wv;
+    }
   }
 }
 
@@ -570,7 +612,7 @@ void bwd_dq_kernel(BwdArgs a) {
 template <int FLAGS>
 hipError_t launch_pair(const BwdArgs& a, int grid_kv, int grid_q, hipStream_t stream) {
   if (grid_kv > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_kv), dim3(kThreads), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_kv), dim3(kKvThreads), 0,
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
