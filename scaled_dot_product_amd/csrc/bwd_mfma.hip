@@ -283,11 +283,26 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dvt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // item it of this chunk: flattened index it0 + it over (head, tile)
-  auto item_head = [&](int it) { return kvh * a.group + (it0 + it) / nt; };
-  auto item_q0 = [&](int it) { return (t_lo + (it0 + it) % nt) * kBQ; };
-  auto copy_item = [&](int it, u32x4* qd, u32x4* od, float2* sd) {
-    const int h = item_head(it), q0 = item_q0(it);
+  // The items of this chunk are the flattened indices it0 .. over (head,
+  // tile).  A cursor (query head, first query row) walks them in order, one
+  // for the copies and one for the computation a step behind, so that no item
+  // divides by the tile count.
+  struct Cursor {
+    int h, q0;
+  };
+  const int q_end = (t_lo + nt) * kBQ;
+  auto advance = [&](Cursor& c) {
+    c.q0 += kBQ;
+    if (c.q0 == q_end) {
+      c.q0 = t_lo * kBQ;
+      ++c.h;
+    }
+  };
+  Cursor cur_copy = {kvh * a.group + it0 / nt, (t_lo + it0 % nt) * kBQ};
+  Cursor cur_comp = cur_copy;
+  auto copy_item = [&](u32x4* qd, u32x4* od, float2* sd) {
+    const int h = cur_copy.h, q0 = cur_copy.q0;
+    advance(cur_copy);
     const size_t row0 = (size_t)(b * a.Hq + h) * Sq + q0;
     copy_q_do<T, D>(reinterpret_cast<const T*>(a.q) + row0 * D, reinterpret_cast<const T*>(a.dout) + row0 * D,
                     Sq - q0, qd, od, tid, wave);
@@ -298,8 +313,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  auto compute = [&](int it, const u32x4* qs, const u32x4* os, const float2* ss) {
-    const int h = item_head(it), q0 = item_q0(it);
+  auto compute = [&](const u32x4* qs, const u32x4* os, const float2* ss) {
+    const int h = cur_comp.h, q0 = cur_comp.q0;
+    advance(cur_comp);
     if (!live(q0)) return;
     // S = Q K^T, dP = dO V^T in two 16-query blocks: block qb holds queries
     // 16 qb + 4 G .. + 3 (rows) x this wave's 16 keys (lane n)
@@ -318,28 +334,53 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
     float slope_l2 = 0.f;
     if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
-    const bool need_mask = MASK && !full(q0);
+    // statistics of rows 16 qb + 4 G .. + 3: LSE (log2 units) and dO . O
     const float4* sp = reinterpret_cast<const float4*>(ss);
+    float lse2[2][4], dlt[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float4 s01 = sp[8 * qb + 2 * G], s23 = sp[8 * qb + 2 * G + 1];
+      lse2[qb][0] = s01.x, lse2[qb][1] = s01.z, lse2[qb][2] = s23.x, lse2[qb][3] = s23.z;
+      dlt[qb][0] = s01.y, dlt[qb][1] = s01.w, dlt[qb][2] = s23.y, dlt[qb][3] = s23.w;
+    }
+    // exponents of P (transformed score minus the row's LSE), tanh(s / cap)
+    // for the softcap derivative
+    float e[2][4], th[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (!SOFTCAP && !ALIBI) {
+          e[qb][c] = __builtin_fmaf(s[qb][c], a.c_score, -lse2[qb][c]);
+        } else {
+          const int rel = j - (q0 + 16 * qb + 4 * G + c + off);
+          e[qb][c] = transform<SOFTCAP, ALIBI>(s[qb][c], a, slope_l2, rel, th[qb][c]) - lse2[qb][c];
+        }
+      }
+    // the mask, on tiles that straddle a boundary only
+    if (MASK && !full(q0)) {
+      const uint32_t span = (uint32_t)(hi - lo);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int qrow = q0 + 16 * qb + 4 * G + c;
+          const int rel = j - (qrow + off);
+          const bool out = qrow >= Sq || j >= Sk || (uint32_t)(rel - lo) > span;
+          e[qb][c] = out ? kNegInf : e[qb][c];
+        }
+    }
     // P and dS as the B operands of the dV and dK products: k-slots 8 G + 4 qb
     // + c are query rows 16 qb + 4 G + c
     u32x4 pf, df;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // statistics of rows 16 qb + 4 G .. + 3
-      const float4 s01 = sp[8 * qb + 2 * G], s23 = sp[8 * qb + 2 * G + 1];
-      const float lse2[4] = {s01.x, s01.z, s23.x, s23.z};
-      const float dlt[4] = {s01.y, s01.w, s23.y, s23.w};
       float pv[4], dsv[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int qrow = q0 + 16 * qb + 4 * G + c;
-        const int rel = j - (qrow + off);
-        float t;
-        float x = transform<SOFTCAP, ALIBI>(s[qb][c], a, slope_l2, rel, t);
-        if (need_mask && (qrow >= Sq || j >= Sk || rel < lo || rel > hi)) x = kNegInf;
-        const float p = fast_exp2(x - lse2[c]);
-        float d = p * (dp[qb][c] - dlt[c]);
-        if constexpr (SOFTCAP) d *= 1.f - t * t;
+        const float p = fast_exp2(e[qb][c]);
+        float d = p * (dp[qb][c] - dlt[qb][c]);
+        if constexpr (SOFTCAP) d *= 1.f - th[qb][c] * th[qb][c];
         pv[c] = p;
         dsv[c] = d;
       }
@@ -358,17 +399,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  if (n_items > 0) copy_item(0, qbuf0, obuf0, sbuf0);
+  if (n_items > 0) copy_item(qbuf0, obuf0, sbuf0);
   wait_vmem();
   __syncthreads();
   for (int it = 0; it < n_items; it += 2) {
-    if (it + 1 < n_items) copy_item(it + 1, qbuf1, obuf1, sbuf1);
-    compute(it, qbuf0, obuf0, sbuf0);
+    if (it + 1 < n_items) copy_item(qbuf1, obuf1, sbuf1);
+    compute(qbuf0, obuf0, sbuf0);
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_items) {
-      if (it + 2 < n_items) copy_item(it + 2, qbuf0, obuf0, sbuf0);
-      compute(it + 1, qbuf1, obuf1, sbuf1);
+      if (it + 2 < n_items) copy_item(qbuf0, obuf0, sbuf0);
+      compute(qbuf1, obuf1, sbuf1);
       wait_vmem();
       __syncthreads();
     }
