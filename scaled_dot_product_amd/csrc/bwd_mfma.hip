@@ -196,6 +196,10 @@ __device__ __forceinline__ void copy_q_do(const T* q, const T* dout, int rows_le
   }
 }
 
+// dK/dV: transpose-read operands in flight ahead of their product (4 timed
+// best of 2, 4, 6 and 8 on the causal 2K workload)
+constexpr int kTrPF = 4;
+
 template <typename T, int D, int FLAGS>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
@@ -332,6 +336,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
         dp[qb] = E::mma16(os[r * NC + c], vf[st], dp[qb]);
       }
     }
+    // The A operands of the dV and dK products (operand f: dO^T for even f,
+    // Q^T for odd, 16-column block db0 + f / 2) do not depend on P: the first
+    // kTrPF are read before the element-wise work, whose time hides their
+    // latency, and each later one kTrPF products ahead of its use.
+    const T* Os = reinterpret_cast<const T*>(os);
+    const T* Qs = reinterpret_cast<const T*>(qs);
+    // (Not at head dim 256, where the registers are short.)
+    constexpr int NF = 2 * DB;
+    constexpr int PF = D > 128 ? 0 : (kTrPF < NF ? kTrPF : NF);
+    auto tr_op = [&](int f) { return tr16_operand<T, D>((f & 1) ? Qs : Os, db0 + (f >> 1), lane); };
+    u32x4 trf[PF > 0 ? PF : 1];
+#pragma unroll
+    for (int f = 0; f < PF; ++f) trf[f] = tr_op(f);
     float slope_l2 = 0.f;
     if constexpr (ALIBI) slope_l2 = a.alibi[h] * kLog2e;
     // statistics of rows 16 qb + 4 G .. + 3: LSE (log2 units) and dO . O
@@ -390,12 +407,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
       df[2 * qb + 1] = E::pack2(dsv[2], dsv[3]);
     }
     // dV^T += dO^T P, dK^T += Q^T dS over the tile's 32 queries
-    const T* Os = reinterpret_cast<const T*>(os);
-    const T* Qs = reinterpret_cast<const T*>(qs);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dvt[db] = E::mma16(tr16_operand<T, D>(Os, db0 + db, lane), pf, dvt[db]);
-      dkt[db] = E::mma16(tr16_operand<T, D>(Qs, db0 + db, lane), df, dkt[db]);
+    for (int f = 0; f < NF; ++f) {
+      u32x4 op;
+      if constexpr (PF > 0) {
+        op = trf[f % PF];
+        if (f + PF < NF) trf[f % PF] = tr_op(f + PF);
+      } else {
+        op = tr_op(f);
+      }
+      if (f & 1) dkt[f >> 1] = E::mma16(op, df, dkt[f >> 1]);
+      else dvt[f >> 1] = E::mma16(op, pf, dvt[f >> 1]);
     }
   };
 
