@@ -612,25 +612,54 @@ void bwd_dq_kernel(BwdArgs a) {
     }
     const bool need_mask = MASK && !full(t);
     uint32_t dsp[16];
+    if constexpr (!SOFTCAP && !ALIBI) {
+      // exponents of P in place of the scores (scaled score minus the row's
+      // LSE, one FMA), the mask on tiles that straddle a boundary only
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float dv2[2];
+        for (int r = 0; r < 16; ++r) sc[kb][r] = __builtin_fmaf(sc[kb][r], a.c_score, -stt.x);
+      if (need_mask) {
+        const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int key = n0 + 32 * kb + 8 * ((r + c) >> 2) + 4 * g + ((r + c) & 3);
-          const int rel = key - ip;
-          float tt;
-          float x = transform<SOFTCAP, ALIBI>(sc[kb][r + c], a, slope_l2, rel, tt);
-          if (need_mask && (qi >= Sq || key >= Sk || rel < lo || rel > hi)) x = kNegInf;
-          const float p = fast_exp2(x - stt.x);
-          float d = p * (dp[kb][r + c] - stt.y);
-          if constexpr (SOFTCAP) d *= 1.f - tt * tt;
-          dv2[c] = d;
-        }
-        dsp[kb * 8 + r / 2] = E::pack2(dv2[0], dv2[1]);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int rel = key - ip;
+            const bool out = qi >= Sq || key >= Sk || (uint32_t)(rel - lo) > span;
+            sc[kb][r] = out ? kNegInf : sc[kb][r];
+          }
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float d0 = fast_exp2(sc[kb][r]) * (dp[kb][r] - stt.y);
+          const float d1 = fast_exp2(sc[kb][r + 1]) * (dp[kb][r + 1] - stt.y);
+          dsp[kb * 8 + r / 2] = E::pack2(d0, d1);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float dv2[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int key = n0 + 32 * kb + 8 * ((r + c) >> 2) + 4 * g + ((r + c) & 3);
+            const int rel = key - ip;
+            float tt;
+            float x = transform<SOFTCAP, ALIBI>(sc[kb][r + c], a, slope_l2, rel, tt);
+            if (need_mask && (qi >= Sq || key >= Sk || rel < lo || rel > hi)) x = kNegInf;
+            const float p = fast_exp2(x - stt.x);
+            float d = p * (dp[kb][r + c] - stt.y);
+            if constexpr (SOFTCAP) d *= 1.f - tt * tt;
+            dv2[c] = d;
+          }
+          dsp[kb * 8 + r / 2] = E::pack2(dv2[0], dv2[1]);
+        }
+    }
     // dQ^T += K^T dS^T over the tile's 64 keys, 16 per step
     const T* Ks = reinterpret_cast<const T*>(ks_);
 #pragma unroll
