@@ -51,13 +51,14 @@ def compare_grad(got, ref, dtype, what):
 
 
 def run_bwd(sdpa, dtype, B, Hq, Hkv, Sq, Sk, D, *, causal=False, wl=None, wr=None, softcap=None,
-            alibi=False, amp=1.0, seed=0):
+            alibi=False, amp=1.0, seed=0, scale=None):
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
     name = (f"attn_bwd {dtype} B{B} H{Hq}/{Hkv} Sq{Sq} Sk{Sk} D{D} causal={causal} "
-            f"win=({wl},{wr}) cap={softcap} alibi={alibi} seed={seed}")
+            f"win=({wl},{wr}) cap={softcap} alibi={alibi} scale={scale} seed={seed}")
     q, k, v = W.random_dense(dtype, B, Hq, Hkv, Sq, Sk, D, seed, amp)
     do = W.random_dense(dtype, B, Hq, Hkv, Sq, 1, D, seed + 7919, 1.0)[0]
     sl = torch.from_numpy(W.alibi_slopes(Hq)) if alibi else None
-    scale = float(np.float32(1.0 / math.sqrt(D)))
     announce(name)
     dq, dk, dv = sdpa.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV),
                                None if sl is None else sl.to(DEV), softmax_scale=scale,
@@ -113,6 +114,24 @@ def test_bwd_parity_d256(gpu_lib, dtype, case):
 
 def test_bwd_d256_chunked_key_blocks(gpu_lib):
     run_bwd(gpu_lib, "bf16", 1, 8, 2, 600, 300, 256, causal=True, seed=860)
+
+
+def test_bwd_scale_zero_under_masks(gpu_lib):
+    """softmax_scale = 0: uniform weights over each row's admissible keys, so
+    dV averages dO and dQ = dK = 0; the masks must still apply (the exponent
+    is formed before the mask)."""
+    run_bwd(gpu_lib, "bf16", 1, 4, 2, 70, 90, 128, causal=True, wl=20, scale=0.0, seed=870)
+    run_bwd(gpu_lib, "f16", 1, 2, 1, 33, 50, 64, causal=True, scale=0.0, seed=871)
+
+
+@pytest.mark.parametrize("Sk", [2, 5, 16, 17, 37])
+def test_bwd_key_counts_around_a_wave(gpu_lib, Sk):
+    """Key counts below, at and just past the 16 keys a dK/dV wave owns (the
+    other waves of the workgroup have no keys).  (Not a single key: there
+    dS = P (dP - dO . O) is exactly 0 for every row, and the gradients' float32
+    rounding residue has no nonzero reference to be measured against.)"""
+    run_bwd(gpu_lib, "bf16", 1, 4, 2, 40, Sk, 128, causal=True, seed=880 + Sk)
+    run_bwd(gpu_lib, "f16", 2, 2, 2, 24, Sk, 64, seed=890 + Sk)
 
 
 def test_bwd_deterministic(gpu_lib):
