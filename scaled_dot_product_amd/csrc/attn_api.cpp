@@ -276,7 +276,7 @@ static BwdLayout bwd_layout(const attn_fwd_params_t* p) {
     L.chunk_items = 1;
     L.max_chunks = 1;
   } else {
-    attn::bwd_chunking((int)p->B, (int)p->Hkv, (int)p->Hq, (int)p->Sq, (int)p->Sk, p->causal != 0,
+    attn::bwd_chunking((int)p->B, (int)p->Hkv, (int)p->Hq, (int)p->Sq, (int)p->Sk, (int)p->D, p->causal != 0,
                        L.wl, L.wr, &L.chunk_items, &L.max_chunks);
   }
   // per query row: two floats (matrix cores) or two values of the element type

@@ -105,28 +105,69 @@ inline int bwd_kv_items(int kb, int Sq, int Sk, int group, int causal, int wl, i
   return nt * group;
 }
 
-// Chunk size: about 1/512 of all dK/dV items (at least 16): about half a
-// compute unit's share on a 256-CU chip, so that the workgroups pack evenly
-// onto the chip even though the causal key blocks differ in work by up to
-// Sq / 32 tiles (chunks of 1/256 packed worse, 1/1024 doubled the partials for
-// 2 % more); and the most chunks any key block needs.
-constexpr long long kBwdChunkDiv = 512;
-inline void bwd_chunking(int B, int Hkv, int Hq, int Sq, int Sk, int causal, int wl, int wr,
+// Chunk size (items per dK/dV workgroup) and the most chunks any key block
+// needs.  The dK/dV workgroups run one per compute unit, so they go through
+// the chip in rounds of kBwdSlots, and a round lasts about as long as its
+// largest chunk.  For one and for two rounds the smallest chunk size whose
+// workgroups fit is found by bisection (the workgroup count falls as the
+// chunk grows); the smaller (rounds x size) wins, ties going to the larger
+// chunk (fewer float32 partials to sum).  Work that needs more than two
+// rounds of whole key blocks is not split at all.  Chunks hold at least 16
+// items.  More rounds of smaller chunks lose in practice (each workgroup pays
+// its K/V loads and its partial): a sweep of fixed chunk sizes on causal
+// 2048-, 4096- and 8192-token GQA backwards, a non-causal 1024-token one and
+// a D = 64 one put the best size at the one that fills two rounds (or one,
+// for the non-causal shape), and this rule picks it on all five.
+constexpr long long kBwdSlots = 256;   // dK/dV workgroups resident at once (one per CU of the chip)
+constexpr int kBwdMaxRounds = 2;
+inline void bwd_chunking(int B, int Hkv, int Hq, int Sq, int Sk, int D, int causal, int wl, int wr,
                          int* chunk_items, int* max_chunks) {
   const int group = Hkv > 0 ? Hq / Hkv : 0;
   const int nkb = (Sk + 127) / 128;
-  long long total = 0;
+  const long long copies = (long long)B * Hkv * (D > 128 ? 2 : 1);  // workgroups per chunk
   int most = 0;
   for (int kb = 0; kb < nkb; ++kb) {
     const int n = bwd_kv_items(kb, Sq, Sk, group, causal, wl, wr);
-    total += n;
     most = n > most ? n : most;
   }
-  total *= (long long)B * Hkv;
-  long long L = (total + kBwdChunkDiv - 1) / kBwdChunkDiv;
-  if (L < 16) L = 16;
-  *chunk_items = (int)L;
-  *max_chunks = most > 0 ? (int)((most + L - 1) / L) : 1;
+  if (most == 0) {
+    *chunk_items = 16;
+    *max_chunks = 1;
+    return;
+  }
+  auto workgroups = [&](long long L) {
+    long long w = 0;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int n = bwd_kv_items(kb, Sq, Sk, group, causal, wl, wr);
+      w += (n + L - 1) / L;
+    }
+    return w * copies;
+  };
+  long long best_L = most, best_cost = -1;
+  for (int r = 1; r <= kBwdMaxRounds; ++r) {
+    const long long cap = r * kBwdSlots;
+    long long L;
+    if (workgroups(most) > cap) {
+      L = most;  // even whole blocks take more rounds
+    } else {
+      long long lo = 16, hi = most;  // smallest L in [16, most] with workgroups(L) <= cap
+      if (lo > hi) lo = hi;
+      while (lo < hi) {
+        const long long mid = (lo + hi) / 2;
+        if (workgroups(mid) <= cap) hi = mid;
+        else lo = mid + 1;
+      }
+      L = lo;
+    }
+    const long long rounds = (workgroups(L) + kBwdSlots - 1) / kBwdSlots;
+    const long long cost = rounds * L;
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && L > best_L)) {
+      best_cost = cost;
+      best_L = L;
+    }
+  }
+  *chunk_items = (int)best_L;
+  *max_chunks = (int)((most + best_L - 1) / best_L);
 }
 
 // 0 = F32, 1 = F16, 2 = BF16 (attn_dtype_t).
