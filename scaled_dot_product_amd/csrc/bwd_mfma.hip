@@ -32,6 +32,9 @@
 //    and V tiles of 64 keys through LDS -- with, per tile,
 //      S^T = K Q^T and dP^T = V dO^T (Q and dO in registers)          16 + 16
 //      dQ^T += K^T dS^T (K^T through the LDS transpose read)          16
+//    Its launch has extra workgroups after the dQ ones: those sum the float32
+//    partials of the dK/dV key blocks that were split into chunks (in chunk
+//    order), filling the compute units that the dQ tail leaves idle.
 #include <limits.h>
 
 #include "device_common.h"
@@ -438,7 +441,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // ---- a block of several chunks: this chunk's float32 partials (summed by
-  // bwd_reduce_kernel); this lane's key row, d = 16 db + 4 G .. + 3
+  // the dQ launch's extra workgroups); this lane's key row, d = 16 db + 4 G .. + 3
   if (n_ch > 1) {
     float* pk = a.part + ((((size_t)bkv * a.nkb + kblk) * a.nchunk + ch) * 2) * kBK * D +
                 (size_t)(j - k0) * D + 16 * db0;
@@ -468,12 +471,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // Sum of the chunks' partials of every multi-chunk key block, in chunk
 // order: one thread per 4 d of one key row.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+__device__ __forceinline__ void reduce_rows(const BwdArgs& a, int wg) {
   using E = Elem<T>;
   constexpr int TPR = D / 4;              // threads per key row
   constexpr int RPW = 256 / TPR;          // key rows per workgroup
-  const int blk = blockIdx.x / (kBK / RPW);  // (bkv, key block)
-  const int r = (blockIdx.x % (kBK / RPW)) * RPW + threadIdx.x / TPR;
+  const int blk = wg / (kBK / RPW);       // (bkv, key block)
+  const int r = (wg % (kBK / RPW)) * RPW + threadIdx.x / TPR;
   const int d4 = (threadIdx.x % TPR) * 4;
   const int bkv = blk / a.nkb, kblk = blk - bkv * a.nkb;
   const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
@@ -523,6 +526,12 @@ void bwd_dq_kernel(BwdArgs a) {
 
   __shared__ u32x4 kbuf0[TC], kbuf1[TC], vbuf0[TC], vbuf1[TC];
 
+  // workgroups past the dQ grid sum the dK/dV chunk partials (the last ones
+  // dispatched: they fill the compute units the dQ tail leaves idle)
+  if ((int)blockIdx.x >= a.nbh * a.nqb) {
+    reduce_rows<T, D>(a, (int)blockIdx.x - a.nbh * a.nqb);
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -708,15 +717,10 @@ hipError_t launch_pair(const BwdArgs& a, int grid_kv, int grid_q, hipStream_t st
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (grid_kv > 0 && a.nchunk > 1) {
-    constexpr int RPW = 256 / (ATTN_D / 4);
-    hipLaunchKernelGGL((bwd_reduce_kernel<ATTN_ELEM, ATTN_D>), dim3(a.nbh_kv * a.nkb * (kBK / RPW)),
-                       dim3(256), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (grid_q > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_q), dim3(kThreads), 0,
+  constexpr int RPW = 256 / (ATTN_D / 4);
+  const int grid_red = grid_kv > 0 && a.nchunk > 1 ? a.nbh_kv * a.nkb * (kBK / RPW) : 0;
+  if (grid_q + grid_red > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<ATTN_ELEM, ATTN_D, FLAGS>), dim3(grid_q + grid_red), dim3(kThreads), 0,
                        stream, a);
   return hipGetLastError();
 }
