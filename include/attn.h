@@ -158,11 +158,14 @@ typedef struct attn_paged_params {
                                   the matrix cores, F32/F64 on the vector ALU
                                   (one workgroup per (sequence, head); the
                                   workspace is then not touched)                 */
-  int32_t num_splits;          /* key-dimension splits per sequence, 1..256 (a
-                                  tuning value: batches of at least one
+  int32_t num_splits;          /* key-dimension splits per sequence, 1..256,
+                                  or 0: chosen by the library from the shape
+                                  (about 1024 work items, at least 256
+                                  tokens of block-table capacity per split).
+                                  A tuning value: batches of at least one
                                   (sequence, KV head, 16-query-head chunk)
                                   group per compute unit split each group
-                                  over the waves of one workgroup instead)  */
+                                  over the waves of one workgroup instead    */
   float softmax_scale;         /* finite, >= 0                                   */
   float softcap;               /* 0: off; > 0: softcap * tanh(s / softcap)       */
 } attn_paged_params_t;

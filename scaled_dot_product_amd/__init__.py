@@ -16,10 +16,13 @@ fails to load, every call raises.
                        softcap=None, error_flag=None, stream=None)
     attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
                       out=None, *, softmax_scale=None, softcap=None,
-                      num_splits=8, workspace=None, error_flag=None, stream=None)
+                      num_splits=0, workspace=None, error_flag=None, stream=None)
     attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, alibi=None,
                               out=None, *, softmax_scale=None, softcap=None,
-                              num_splits=8, error_flag=None, stream=None)
+                              num_splits=0, error_flag=None, stream=None)
+
+``num_splits=0`` (the default) lets the library choose the decode's split
+count from the shape; a positive value (1..256) is used as given.
 
 For calls repeated on the same tensors (a serving loop that rewrites q,
 seq_lens and block_table in place each step), ``PagedDecodePlan`` and
@@ -350,7 +353,7 @@ def attn_bwd_lse(q, k, v, out, lse, dout, alibi=None, *, softmax_scale=None, cau
 
 
 def attn_paged_params(q_shape, pool_shape, max_blocks_per_seq, dtype, *, softmax_scale=None,
-                      softcap=None, num_splits=8) -> attn_paged_params_t:
+                      softcap=None, num_splits=0) -> attn_paged_params_t:
     B, Hq, _, D = q_shape
     num_blocks, block_size, Hkv, _ = pool_shape
     return attn_paged_params_t(
@@ -409,7 +412,7 @@ def _paged_decode_args(q, k_pool, v_pool, block_table, seq_lens, alibi, out, wor
 
 
 def attn_paged_decode(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
-                      softmax_scale=None, softcap=None, num_splits=8, workspace=None,
+                      softmax_scale=None, softcap=None, num_splits=0, workspace=None,
                       error_flag=None, stream=None):
     """Paged split-KV decode, one query per sequence (see attn.h)."""
     lib = library()
@@ -442,7 +445,7 @@ class PagedDecodePlan:
     """
 
     def __init__(self, q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
-                 softmax_scale=None, softcap=None, num_splits=8, workspace=None,
+                 softmax_scale=None, softcap=None, num_splits=0, workspace=None,
                  error_flag=None, stream=None):
         lib = library()
         dev = q.device
@@ -500,7 +503,7 @@ DECODE_SCRATCH_BYTES = 32 << 20  # ATTN_DECODE_SCRATCH_BYTES in attn.h
 
 
 def attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, alibi=None, out=None, *,
-                              softmax_scale=None, softcap=None, num_splits=8, error_flag=None,
+                              softmax_scale=None, softcap=None, num_splits=0, error_flag=None,
                               stream=None):
     """attn_paged_decode without a workspace argument: the library's
     device-resident scratch array (DECODE_SCRATCH_BYTES per GPU) serves as it,

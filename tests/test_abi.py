@@ -193,8 +193,26 @@ def test_workspace_size():
     o_bytes = 4 * 32 * 8 * 128 * 4
     lse_off = (o_bytes + 255) // 256 * 256
     assert sdpa.attn_paged_decode_workspace_size(p) == lse_off + 4 * 32 * 8 * 4
-    assert sdpa.attn_paged_decode_workspace_size(paged(num_splits=0)) == 0
+    assert sdpa.attn_paged_decode_workspace_size(paged(num_splits=-1)) == 0
     assert sdpa.attn_paged_decode_workspace_size(paged(D=100)) == 0
+
+
+def test_automatic_split_count():
+    """num_splits = 0: about 1024 (sequence, KV head, head chunk, split) items,
+    at least 256 tokens of block-table capacity per split, within 1..256; the
+    workspace is that of the explicit count it picks."""
+    ws = sdpa.attn_paged_decode_workspace_size
+    # 4 sequences x 8 KV heads = 32 groups -> 32 splits (capacity 512 x 64 tokens)
+    assert ws(paged(num_splits=0, max_blocks_per_seq=512)) == ws(paged(num_splits=32, max_blocks_per_seq=512))
+    # one sequence: 8 groups -> 128 splits
+    assert ws(paged(B=1, num_splits=0, max_blocks_per_seq=2048)) == \
+        ws(paged(B=1, num_splits=128, max_blocks_per_seq=2048))
+    # short capacity: 10 x 64 tokens -> 2 splits of at least 256 tokens
+    assert ws(paged(num_splits=0)) == ws(paged(num_splits=2))
+    # many groups: one split
+    assert ws(paged(B=256, num_splits=0, num_blocks=5000)) == ws(paged(B=256, num_splits=1, num_blocks=5000))
+    # capacity below 256 tokens: one split
+    assert ws(paged(num_splits=0, max_blocks_per_seq=3)) == ws(paged(num_splits=1, max_blocks_per_seq=3))
 
 
 def test_paged_check_accepts_valid_calls():
@@ -202,6 +220,7 @@ def test_paged_check_accepts_valid_calls():
     assert check_paged(paged(D=64, dtype=sdpa.ATTN_F16, block_size=16, num_splits=1,
                              softcap=20.0), al=AL, err=ERR) == OK
     assert check_paged(paged(Hkv=32, num_splits=256)) == OK
+    assert check_paged(paged(num_splits=0)) == OK  # chosen by the library
     assert check_paged(paged(B=0), q=None, out=None, tab=None, lens=None, ws=None) == OK
     # F32 / F64 (vector-ALU path): any block size, head dims 32 to 256
     assert check_paged(paged(dtype=sdpa.ATTN_F32)) == OK
@@ -213,7 +232,7 @@ def test_paged_check_accepts_valid_calls():
     (dict(B=-1), SHAPE), (dict(block_size=0), SHAPE), (dict(B=70000), SHAPE),
     (dict(max_blocks_per_seq=1 << 30), SHAPE),
     (dict(Hkv=5), GQA), (dict(D=32), HEAD_DIM),
-    (dict(num_splits=0), PARAM), (dict(num_splits=257), PARAM),
+    (dict(num_splits=-1), PARAM), (dict(num_splits=257), PARAM),
     (dict(softmax_scale=float("inf")), PARAM), (dict(softcap=-1.0), PARAM),
 ])
 def test_paged_check_rejects(kw, code):

@@ -67,6 +67,32 @@ def test_paged_parity(gpu_lib, case):
             assert torch.count_nonzero(out[b]).item() == 0
 
 
+AUTO_SPLIT_CASES = [
+    # dtype, B, Hq, Hkv, D, block_size, lens  (num_splits = 0: chosen by the library)
+    ("bf16", 1, 32, 8, 128, 64, [20000]),            # 8 groups: many splits
+    ("bf16", 2, 32, 8, 128, 16, [6000, 1]),
+    ("f16", 3, 8, 2, 64, 32, [3000, 0, 700]),
+    ("bf16", 1, 16, 4, 256, 64, [5000]),
+    ("bf16", 2, 4, 4, 128, 16, [100, 255]),          # short capacity: few splits
+]
+
+
+@pytest.mark.parametrize("case", range(len(AUTO_SPLIT_CASES)))
+def test_paged_parity_automatic_splits(gpu_lib, case):
+    dtype, B, Hq, Hkv, D, bs, lens = AUTO_SPLIT_CASES[case]
+    maxb = max((max(lens) + bs - 1) // bs, 1)
+    w = W.Paged("t", dtype, B, Hq, Hkv, D, bs, 0, 0, 0, maxb, seed=260 + case)
+    q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
+    scale = D ** -0.5
+    announce(f"paged decode with automatic splits, case {case}: {AUTO_SPLIT_CASES[case]}")
+    out = gpu_decode(gpu_lib, q, kp, vp, table, sl, None, softmax_scale=scale, num_splits=0)
+    ref = oracle_decode(q, kp, vp, table, sl, None, scale=scale)
+    compare(out, ref, DT[dtype], f"automatic splits case {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
 def wide_lens(B, hi, seed):
     """Lengths for the wide batches: empty, single-token, block-edge and long
     sequences mixed, the rest uniform on [0, hi]."""

@@ -87,4 +87,4 @@ def test_plans_reject_bad_arguments_when_built(gpu_lib):
         gpu_lib.AttnFwdPlan(q, k, v)  # Hq % Hkv != 0
     w, qp, kp, vp, table, sl = _decode_inputs(33, [5, 6, 7, 8])
     with pytest.raises(gpu_lib.AttnError):
-        gpu_lib.PagedDecodePlan(qp.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), sl.to(DEV), num_splits=0)
+        gpu_lib.PagedDecodePlan(qp.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), sl.to(DEV), num_splits=-1)
