@@ -433,7 +433,8 @@ __device__ __forceinline__ void lds_tr4(u32x2 (&v)[4], const uint32_t (&a)[4]) {
 // slots and the workgroup writes the output itself (the same re-basing to a
 // common max as the merge kernel), so there is neither a workspace round trip
 // nor a second launch.
-constexpr int kOrdMax = 256;   // batches up to this size are ordered longest-first
+constexpr int kOrdMax = 256;         // split form: batches up to this size are ordered longest-first
+constexpr int kOrdMaxFused = 4096;   // fused form: the same up to this size (12-bit sequence index)
 constexpr int kStreamWaves = 4;
 template <bool FUSED, int D>
 constexpr int stream_waves() { return FUSED ? (D <= 128 ? 8 : 4) : kStreamWaves; }
@@ -452,26 +453,57 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
   constexpr int SLOT = kTB * NCH;
   static_assert(NS == 3 && kPageWindow % NS == 0 && DB % 4 == 0, "ring and read batches");
   __shared__ u32x4 vring0[NW][SLOT], vring1[NW][SLOT], vring2[NW][SLOT];
-  __shared__ int ord[kOrdMax], lens_lds[kOrdMax];
+  constexpr int ORD = FUSED ? kOrdMaxFused : kOrdMax;
+  __shared__ int ord[ORD], lens_lds[ORD];
   __shared__ float2 ml_x[FUSED ? NW : 1][16];  // fused: per wave and head, (max, sum)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, hl = lane & 15;
 
-  // ---- ord[r] = the r-th longest sequence (the launcher guarantees
-  // B <= kOrdMax); the lengths stay in LDS so that no item start waits on a
-  // global load
-  for (int i = tid; i < a.B; i += 64 * NW) lens_lds[i] = a.lens[i];
+  // ---- ord[r] = the r-th longest sequence, ties by index (the launcher
+  // guarantees B <= ORD); the lengths stay in LDS so that no item start waits
+  // on a global load.  Up to kOrdMax sequences each thread counts the longer
+  // ones (B^2 / threads steps); above that a bitonic sort of packed keys in
+  // ord (log2(n) (log2(n) + 1) / 2 passes over n = B rounded up to a power of
+  // two).  Either way every workgroup derives the same order.
+  const bool big = FUSED && a.B > kOrdMax;
+  int npow = 1;
+  while (big && npow < a.B) npow <<= 1;
+  unsigned* key = reinterpret_cast<unsigned*>(ord);
+  for (int i = tid; i < (big ? npow : a.B); i += 64 * NW) {
+    const int l = i < a.B ? a.lens[i] : 0;
+    if (i < a.B) lens_lds[i] = l;
+    // length (clamped to 20 bits) descending, then index ascending, as one
+    // ascending unsigned key; padding sorts last
+    if (big)
+      key[i] = i < a.B ? ((0xFFFFFu - (unsigned)min(max(l, 0), 0xFFFFF)) << 12) | (unsigned)i : 0xFFFFFFFFu;
+  }
   __syncthreads();
-  for (int i = tid; i < a.B; i += 64 * NW) {
-    const int li = lens_lds[i];
-    int r = 0;
-    for (int j = 0; j < a.B; ++j) {
-      const int lj = lens_lds[j];
-      r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+  if (!big) {
+    for (int i = tid; i < a.B; i += 64 * NW) {
+      const int li = lens_lds[i];
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int lj = lens_lds[j];
+        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      ord[r] = i;
     }
-    ord[r] = i;
+  } else {
+    for (int k = 2; k <= npow; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int p = tid; p < npow / 2; p += 64 * NW) {
+          const int lo = ((p & ~(j - 1)) << 1) | (p & (j - 1));   // bit j clear; partner lo + j
+          const unsigned x = key[lo], y = key[lo + j];
+          if ((x > y) == ((lo & k) == 0)) {
+            key[lo] = y;
+            key[lo + j] = x;
+          }
+        }
+        __syncthreads();
+      }
+    for (int r = tid; r < a.B; r += 64 * NW) ord[r] = (int)(key[r] & 0xFFFu);
   }
   __syncthreads();
 
@@ -817,7 +849,7 @@ hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t st
   const dim3 grid(p.splits, p.Hkv * a.hchunks, p.B);
   const long long groups = (long long)p.B * p.Hkv * a.hchunks;
   const int cus = device_cus();
-  if (p.block_size % kTB == 0 && p.B <= kOrdMax && groups >= cus) {
+  if (p.block_size % kTB == 0 && p.B <= kOrdMaxFused && groups >= cus) {
     // fused persistent form: one workgroup per compute unit (it fills the
     // unit's registers), the output written directly
     constexpr int FW = stream_waves<true, D>();

@@ -135,13 +135,10 @@ def test_paged_parity_wide_batch(gpu_lib, case):
             assert torch.count_nonzero(out[b]).item() == 0
 
 
-# Batches above 256 sequences with block sizes that are multiples of 16: the
-# partial kernel over uniform 16-token blocks (one 2-wave workgroup per split
-# and group, the longest sequences first) plus the merge kernel.  The last two
-# cases exceed the batch size up to which each workgroup ranks the lengths in
-# LDS (2048 at head dim 128, 1024 at 64), so those take sequences in index
-# order.
-PARTIAL_CASES = [
+# Batches above 256 sequences with block sizes that are multiples of 16: still
+# the fused form, with the lengths ordered by a bitonic sort in LDS (up to 4096
+# sequences).
+LARGE_BATCH_CASES = [
     # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
     ("bf16", 300, 8, 4, 128, 16, 300, 3, None, False),
     ("bf16", 512, 8, 8, 128, 64, 260, 8, None, False),
@@ -151,67 +148,90 @@ PARTIAL_CASES = [
     ("bf16", 400, 32, 8, 128, 32, 200, 5, None, False),
     ("bf16", 2100, 2, 1, 128, 16, 40, 2, None, False),
     ("f16", 1100, 4, 2, 64, 32, 70, 3, 25.0, True),
+    ("bf16", 4096, 2, 1, 128, 16, 24, 1, None, False),     # the largest batch the fused form orders
 ]
 
 
-@pytest.mark.parametrize("case", range(len(PARTIAL_CASES)))
-def test_paged_parity_partial_kernel(gpu_lib, case):
-    dtype, B, Hq, Hkv, D, bs, hi, splits, cap, use_alibi = PARTIAL_CASES[case]
-    lens = wide_lens(B, hi, 400 + case)
+@pytest.mark.parametrize("case", range(len(LARGE_BATCH_CASES)))
+def test_paged_parity_large_batch(gpu_lib, case):
+    run_batch_case(gpu_lib, LARGE_BATCH_CASES[case], 400 + case, f"paged decode large-batch case {case}")
+
+
+# Above 4096 sequences: the partial kernel over uniform 16-token blocks (one
+# 2-wave workgroup per split and group) plus the merge kernel.  The workgroups
+# rank the lengths in LDS up to 2048 sequences at head dim 128 (1024 at 64) and
+# take them in index order beyond that, so these batches use index order.
+PARTIAL_CASES = [
+    # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
+    ("bf16", 4097, 2, 1, 128, 16, 20, 2, None, False),
+    ("f16", 4500, 4, 2, 64, 32, 24, 3, 25.0, True),
+    ("bf16", 4200, 8, 2, 256, 16, 17, 1, None, True),
+]
+
+
+def run_batch_case(gpu_lib, case, seed, name):
+    dtype, B, Hq, Hkv, D, bs, hi, splits, cap, use_alibi = case
+    lens = wide_lens(B, hi, seed)
     maxb = (max(lens) + bs - 1) // bs + 1
-    w = W.Paged("t", dtype, B, Hq, Hkv, D, bs, 0, 0, splits, maxb, seed=410 + case)
+    w = W.Paged("t", dtype, B, Hq, Hkv, D, bs, 0, 0, splits, maxb, seed=seed + 10)
     q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
     alibi = torch.from_numpy(W.alibi_slopes(Hq)) if use_alibi else None
     scale = D ** -0.5
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
-    announce(f"paged decode partial-kernel case {case}: {PARTIAL_CASES[case]}")
+    announce(f"{name}: {case}")
     out = gpu_decode(gpu_lib, q, kp, vp, table, sl, alibi, softmax_scale=scale, softcap=cap,
                      num_splits=splits, error_flag=flag)
     assert flag.item() == 0
     ref = oracle_decode(q, kp, vp, table, sl, alibi, scale=scale, softcap=cap)
-    compare(out, ref, DT[dtype], f"paged partial-kernel case {case}")
+    compare(out, ref, DT[dtype], name)
     for b, n in enumerate(lens):
         if n == 0:
             assert torch.count_nonzero(out[b]).item() == 0
 
 
-def test_partial_kernel_error_flag_and_determinism(gpu_lib):
-    """The partial kernel (B = 300, 16-token blocks): a block id outside the
-    pool masks its keys and sets the flag, a length beyond the table's
-    capacity is clamped and sets it, the other sequences are unaffected, and
-    reruns are bitwise equal."""
-    B, Hq, Hkv, D, bs, maxb = 300, 8, 2, 128, 16, 20
+@pytest.mark.parametrize("case", range(len(PARTIAL_CASES)))
+def test_paged_parity_partial_kernel(gpu_lib, case):
+    run_batch_case(gpu_lib, PARTIAL_CASES[case], 450 + case, f"paged decode partial-kernel case {case}")
+
+
+@pytest.mark.parametrize("B", [300, 4200])
+def test_large_batch_error_flag_and_determinism(gpu_lib, B):
+    """16-token blocks at B = 300 (the fused form over sorted lengths) and
+    B = 4200 (the partial kernel): a block id outside the pool masks its keys
+    and sets the flag, a length beyond the table's capacity is clamped and
+    sets it, the other sequences are unaffected, and reruns are bitwise equal."""
+    Hq, Hkv, D, bs, maxb = 8, 2, 128, 16, 20
     w = W.Paged("ep", "bf16", B, Hq, Hkv, D, bs, 0, 0, 4, maxb, seed=91)
     lens = wide_lens(B, 300, 92)
     q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
-    announce("partial kernel: valid call, rerun")
+    announce(f"B={B}: valid call, rerun")
     a = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
     b = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
     assert flag.item() == 0
     assert torch.equal(a, b)
     ref = oracle_decode(q, kp, vp, table, sl, scale=D ** -0.5)
-    compare(a, ref, torch.bfloat16, "partial kernel")
+    compare(a, ref, torch.bfloat16, f"B={B}")
     victim = int(np.argmax(np.array(lens) > 2 * bs))
     bad = table.clone()
     bad[victim, 1] = 10 ** 6                                # keys 16..31 of that sequence are masked
-    announce("partial kernel: block id out of range")
+    announce(f"B={B}: block id out of range")
     out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag, num_splits=4)
     assert flag.item() == 1
     assert torch.isfinite(out.float()).all()
     others = [i for i in range(B) if i != victim]
-    compare(out[others], ref[others], torch.bfloat16, "partial kernel, unaffected sequences")
+    compare(out[others], ref[others], torch.bfloat16, f"B={B}, unaffected sequences")
     n = lens[victim]
     keep = [t for t in range(n) if not bs <= t < 2 * bs]
     kb = oracle.paged_gather(W.to_f64(kp), table.numpy(), n, victim, bs)[keep]
     vb = oracle.paged_gather(W.to_f64(vp), table.numpy(), n, victim, bs)[keep]
     r1 = oracle.sdpa_naive_f64(W.to_f64(q[victim:victim + 1]), kb.transpose(1, 0, 2)[None],
                                vb.transpose(1, 0, 2)[None], scale=D ** -0.5)
-    compare(out[victim:victim + 1], r1, torch.bfloat16, "partial kernel, masked keys")
+    compare(out[victim:victim + 1], r1, torch.bfloat16, f"B={B}, masked keys")
     flag.zero_()
     long = sl.clone()
     long[3] = maxb * bs + 5
-    announce("partial kernel: seq_len beyond capacity")
+    announce(f"B={B}: seq_len beyond capacity")
     gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag, num_splits=4)
     assert flag.item() == 1
 
@@ -228,16 +248,18 @@ def test_paged_decode_workload(gpu_lib):
 
 @pytest.mark.parametrize("bs,splits,B,Hkv", [(64, 8, 4, 2), (16, 3, 4, 2), (5, 1, 4, 2),
                                              (16, 8, 64, 4), (32, 2, 128, 2),
-                                             (16, 3, 300, 2), (64, 8, 300, 1)])
+                                             (16, 3, 300, 2), (64, 8, 300, 1), (16, 3, 4200, 1)])
 def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
     """One-hot scores: q = 1024 e0 in every head and a single key row equal to
     8 e0 give that key a score of 1024 * 8 / sqrt(128) ~ 724 and every other
     key 0, so exp underflows to exactly 0 elsewhere and the output is exactly
-    the V row of that logical token.  V rows hold (sequence, position % 128,
-    position // 128, kv head) as bf16-exact integers; slots no table entry
-    points at hold a finite sentinel so that a stray read is visible.  The
-    cases with B = 64 and 128 have 256 (sequence, KV head) groups (the fused
-    form); those with B = 300 run the partial kernel over 16-token blocks."""
+    the V row of that logical token.  V rows hold (sequence % 128, position
+    % 128, position // 128, kv head, sequence // 128) as bf16-exact integers;
+    slots no table entry points at hold a finite sentinel so that a stray
+    read is visible.  The
+    cases with B = 64, 128 and 300 have at least 256 (sequence, KV head)
+    groups (the fused form); B = 4200 runs the partial kernel over 16-token
+    blocks."""
     Hq, D = 8, 128
     lens = [130, 64, 7, 200] if B == 4 else np.random.default_rng(6).integers(1, 260, size=B).tolist()
     rng = np.random.default_rng(5)
@@ -250,10 +272,11 @@ def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
         t = np.arange(n)
         blk, slot = table_np[b, t // bs], t % bs
         row = np.zeros((n, Hkv, D), dtype=np.float32)
-        row[:, :, 0] = b
+        row[:, :, 0] = b % 128
         row[:, :, 1] = (t % 128)[:, None]
         row[:, :, 2] = (t // 128)[:, None]
         row[:, :, 3] = np.arange(Hkv)[None, :]
+        row[:, :, 4] = b // 128
         vp_np[blk, slot] = row
     vp = torch.from_numpy(vp_np).to(torch.bfloat16)
     q = torch.zeros(B, Hq, 1, D, dtype=torch.bfloat16)
@@ -273,11 +296,16 @@ def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
         out = gpu_lib.attn_paged_decode(dq, kp.to(DEV), dvp, dt, dsl, num_splits=splits)
         torch.cuda.synchronize()
         out = out.cpu()
-        for b, t in enumerate(targets):
-            for h in range(Hq):
-                g = h // (Hq // Hkv)
-                want = torch.tensor([b, t % 128, t // 128, g] + [0] * (D - 4), dtype=torch.bfloat16)
-                assert torch.equal(out[b, h, 0], want), (b, h, t)
+        want = torch.zeros(B, Hq, 1, D, dtype=torch.bfloat16)
+        tt = torch.tensor(targets, dtype=torch.float32)
+        want[:, :, 0, 0] = (torch.arange(B) % 128).float()[:, None]
+        want[:, :, 0, 4] = torch.div(torch.arange(B), 128, rounding_mode="floor").float()[:, None]
+        want[:, :, 0, 1] = (tt % 128)[:, None]
+        want[:, :, 0, 2] = torch.div(tt, 128, rounding_mode="floor")[:, None]
+        want[:, :, 0, 3] = (torch.arange(Hq) // (Hq // Hkv)).float()[None, :]
+        if not torch.equal(out, want):
+            b, h = (out != want).any(dim=-1)[..., 0].nonzero()[0].tolist()
+            raise AssertionError(f"sequence {b} head {h} target {targets[b]}: {out[b, h, 0, :5]}")
 
 
 def test_error_flag_and_masking(gpu_lib):

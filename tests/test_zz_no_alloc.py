@@ -6,7 +6,7 @@ Both run the same kernels on the same inputs, so the outputs must be
 bitwise equal; they are also checked against the float64 oracle.  Two calls
 in a row, the second with a smaller input, for each decode form that uses a
 workspace: the split persistent kernel (fewer (sequence, KV head) groups than
-compute units) and the partial kernel (B > 256)."""
+compute units) and the partial kernel (B > 4096)."""
 import numpy as np
 import pytest
 import torch
@@ -23,8 +23,8 @@ DEV = torch.device("cuda:0")
 FORMS = {
     "split persistent": [("bf16", 8, 32, 8, 128, 64, 900, 8, None, False),
                          ("bf16", 3, 16, 4, 128, 16, 300, 4, 20.0, True)],
-    "partial kernel": [("f16", 300, 8, 2, 128, 16, 200, 4, None, True),
-                       ("f16", 260, 4, 2, 64, 32, 100, 3, None, False)],
+    "partial kernel": [("f16", 4200, 4, 2, 128, 16, 40, 2, None, True),
+                       ("f16", 4100, 2, 2, 64, 32, 30, 3, None, False)],
 }
 
 
