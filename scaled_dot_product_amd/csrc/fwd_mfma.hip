@@ -173,11 +173,13 @@ __device__ __forceinline__ void qk_tile_pf(const u32x4* Ks, const u32x4* qf, int
   }
 }
 
-// Transform + mask + online update of one tile's scores, then O += P V.
+// Transform + mask + online update of one tile's scores: the weights P,
+// rounded and packed as the B operand of O^T += V^T P^T, and O rescaled when
+// the reference max rises.
 template <typename T, int D, int FLAGS>
-__device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowState<D / 32>& st,
-                                           const FwdArgs& a, int Sk, int n0, int ip, int ipa_w,
-                                           int ipb_w, float slope_l2, int lane, int g) {
+__device__ __forceinline__ void softmax_p(floatx16 (&sc)[2], uint32_t (&pp)[16], RowState<D / 32>& st,
+                                          const FwdArgs& a, int Sk, int n0, int ip, int ipa_w,
+                                          int ipb_w, float slope_l2, int g) {
   using E = Elem<T>;
   constexpr bool MASK = (FLAGS & F_MASK) != 0;
   constexpr bool SOFTCAP = (FLAGS & F_SOFTCAP) != 0;
@@ -278,7 +280,6 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
   const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
 
   // weights, rounded to the input type, packed as the PV B operand
-  uint32_t pp[16];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -294,7 +295,15 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
       pp[kb * 8 + r / 2] = E::pack2(p0, p1);
       if constexpr (!kMmaSum) st.l_part = E::dot2(pp[kb * 8 + r / 2], E::kOnePair, st.l_part);
     }
+}
 
+// O^T += V^T P^T for the 64 keys of one tile (weights pp from softmax_p).
+template <typename T, int D>
+__device__ __forceinline__ void pv_tile(const uint32_t (&pp)[16], const T* Vs, RowState<D / 32>& st,
+                                        int lane, int g) {
+  using E = Elem<T>;
+  constexpr int DB = D / 32;
+  constexpr bool kMmaSum = D <= 128;
   // O^T += V^T P^T, 16 keys per step; V^T through the LDS transpose read
   const int trow = 4 * g + ((lane & 15) >> 2);                // key row within a 16-key step
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // d within a 32-row block
@@ -325,6 +334,16 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowSt
       st.o[db] = E::mma32(va, pf, st.o[db]);
     }
   }
+}
+
+// One tile's softmax, then O += P V.
+template <typename T, int D, int FLAGS>
+__device__ __forceinline__ void softmax_pv(floatx16 (&sc)[2], const T* Vs, RowState<D / 32>& st,
+                                           const FwdArgs& a, int Sk, int n0, int ip, int ipa_w,
+                                           int ipb_w, float slope_l2, int lane, int g) {
+  uint32_t pp[16];
+  softmax_p<T, D, FLAGS>(sc, pp, st, a, Sk, n0, ip, ipa_w, ipb_w, slope_l2, g);
+  pv_tile<T, D>(pp, Vs, st, lane, g);
 }
 
 // Key-split mode (F_SPLIT, for grids too small to fill the chip): the
@@ -514,9 +533,19 @@ void fwd_mfma_kernel(FwdArgs a) {
   // the softmax of a tile that does not sees a key bound at its first key, so
   // all of its keys are masked.
   const int n = t_end - t_begin;
+  // Group 1 of a split workgroup runs the pipeline rotated by half a step:
+  // step i does the matrix work first (O += P(i-1) V(i-1), then S(i)) and the
+  // softmax of tile i after it, so that on each SIMD (one wave of each group)
+  // one wave's vector phase meets the other's matrix phase between two
+  // barriers.  The operations on O keep their order, so the result is the
+  // same bit for bit.  Its copies run one tile later: K(i+1) and V(i) in step i.
+  // (head dim 64 only: at 128 the rotated loop does not fit the registers)
+  const bool rot = SPLIT && D == 64 && grp == 1;
   // steps every wave of the workgroup runs (barriers must match): group 0 of a
-  // split workgroup has at least as many tiles as group 1
-  const int n_steps = SPLIT ? half : n;
+  // split workgroup has at least as many tiles as group 1, which needs one
+  // step more than it has tiles
+  const int n_steps = !SPLIT ? n : D != 64 ? half
+                      : (t_last > t_first ? max(half, t_last - t_first - half + 1) : 0);
   u32x4* const kb0 = kbuf0 + grp * TC;
   u32x4* const kb1 = kbuf1 + grp * TC;
   u32x4* const vb0 = vbuf0 + grp * TC;
@@ -532,30 +561,34 @@ void fwd_mfma_kernel(FwdArgs a) {
   }
   bool ok_unused;
   if (n_steps > 0) {
-    // descriptors first, copies after: the page ids may still be in flight,
-    // and a wait for them placed between copies would wait for the copies too
+    // K(0), V(0) and K(1); rotated: K(0) only.  Descriptors first, copies
+    // after: the page ids may still be in flight, and a wait for them placed
+    // between copies would wait for the copies too
     if constexpr (PAGED) {
       const __amdgpu_buffer_rsrc_t rk0 = n > 0 ? tile_rsrc(K, t_begin, kc, kok0) : make_rsrc32(K, 0);
-      const __amdgpu_buffer_rsrc_t rv0 = n > 0 ? tile_rsrc(V, t_begin, vc, ok_unused) : make_rsrc32(V, 0);
+      __amdgpu_buffer_rsrc_t rv0 = make_rsrc32(V, 0), rk1 = make_rsrc32(K, 0);
       advance(kc);
-      advance(vc);
-      const __amdgpu_buffer_rsrc_t rk1 = n > 1 ? tile_rsrc(K, t_begin + 1, kc, kok1) : make_rsrc32(K, 0);
-      advance(kc);
+      if (!rot) {
+        rv0 = n > 0 ? tile_rsrc(V, t_begin, vc, ok_unused) : make_rsrc32(V, 0);
+        advance(vc);
+        rk1 = n > 1 ? tile_rsrc(K, t_begin + 1, kc, kok1) : make_rsrc32(K, 0);
+        advance(kc);
+      }
       if (n > 0) {
         dma_k(kb0, rk0);
-        dma_v(vb0, rv0);
+        if (!rot) dma_v(vb0, rv0);
       }
-      if (n > 1) dma_k(kb1, rk1);
+      if (!rot && n > 1) dma_k(kb1, rk1);
     } else {
       if (n > 0) {
         dma_k(kb0, tile_rsrc(K, t_begin, kc, kok0));
-        dma_v(vb0, tile_rsrc(V, t_begin, vc, ok_unused));
+        if (!rot) dma_v(vb0, tile_rsrc(V, t_begin, vc, ok_unused));
       }
-      if (n > 1) dma_k(kb1, tile_rsrc(K, t_begin + 1, kc, kok1));
+      if (!rot && n > 1) dma_k(kb1, tile_rsrc(K, t_begin + 1, kc, kok1));
     }
     wait_vmem();
     __syncthreads();
-    if (n > 0 && live(t_begin)) qk_tile<T, D>(kb0, qf, ln, g, sc);
+    if (!rot && n > 0 && live(t_begin)) qk_tile<T, D>(kb0, qf, ln, g, sc);
   }
   auto step = [&](int i, const u32x4* kread, const u32x4* vread, u32x4* kload, u32x4* vload,
                   bool& ok_load) {
@@ -593,9 +626,51 @@ void fwd_mfma_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
-  for (int i = 0; i < n_steps; i += 2) {
-    step(i, kb1, vb0, kb0, vb1, kok0);
-    if (i + 1 < n_steps) step(i + 1, kb0, vb1, kb1, vb0, kok1);
+  // the rotated step of group 1: K(i) is in kcur, V(i-1) in vprev; pp
+  // carries tile i-1's weights from its softmax into this step
+  uint32_t pp[16];
+  auto step_rot = [&](int i, const u32x4* kcur, const u32x4* vprev, u32x4* kload, u32x4* vload,
+                      bool& ok_cur, bool& ok_load) {
+    const int t = t_begin + i;
+    wait_vmem();
+    __syncthreads();  // K(i), V(i-1) landed; everyone is done with step i-1's buffers
+    if constexpr (PAGED) {
+      // the copies below read tiles t + 1 (K, at kc) and t (V, at vc)
+      if (i + 1 < n && kc.lb - pbase >= 64) load_pages(vc.lb);
+      const __amdgpu_buffer_rsrc_t rk = i + 1 < n ? tile_rsrc(K, t + 1, kc, ok_load) : make_rsrc32(K, 0);
+      const __amdgpu_buffer_rsrc_t rv = i < n ? tile_rsrc(V, t, vc, ok_unused) : make_rsrc32(V, 0);
+      advance(kc);
+      advance(vc);
+      if (i + 1 < n) dma_k(kload, rk);
+      if (i < n) dma_v(vload, rv);
+    } else {
+      if (i + 1 < n) dma_k(kload, tile_rsrc(K, t + 1, kc, ok_load));
+      if (i < n) dma_v(vload, tile_rsrc(V, t, vc, ok_unused));
+    }
+    u32x4 kf[kKPF];
+#pragma unroll
+    for (int p = 0; p < kKPF; ++p) kf[p] = kfrag<T, D>(kcur, p, ln, g);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    if (i >= 1 && live(t - 1)) pv_tile<T, D>(pp, reinterpret_cast<const T*>(vprev), st, lane, g);
+    if (i < n && live(t)) qk_tile_pf<T, D>(kcur, qf, ln, g, kf, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    if (i < n && live(t))
+      softmax_p<T, D, FLAGS>(sc, pp, st, a, PAGED && !ok_cur ? t * kBN : Sk, t * kBN, ip, ipa_w, ipb_w,
+                             slope_l2, g);
+  };
+  // (two loops, so that each carries only its own state across its steps)
+  if (rot) {
+    for (int i = 0; i < n_steps; i += 2) {
+      step_rot(i, kb0, vb1, kb1, vb0, kok0, kok1);
+      if (i + 1 < n_steps) step_rot(i + 1, kb1, vb0, kb0, vb1, kok1, kok0);
+    }
+  } else {
+    for (int i = 0; i < n_steps; i += 2) {
+      step(i, kb1, vb0, kb0, vb1, kok0);
+      if (i + 1 < n_steps) step(i + 1, kb0, vb1, kb1, vb0, kok1);
+    }
   }
   if (PAGED && bad_page && a.err && lane == 0) *a.err = 1;
 
