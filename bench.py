@@ -6,9 +6,10 @@ One step = one pass of the whole path over one batch of synthetic input:
     scale 1/sqrt(128) -- causal-effective TFLOP/s (4 * D * admissible pairs);
   * decode: attn_paged_decode, bf16, B=64, Hq=32, Hkv=8, D=128, context
     lengths uniform on [512, 8192], 64-token blocks randomly permuted in one
-    pool, num_splits 8 (the fused form splits each (sequence, KV head) over
-    the 8 waves of a workgroup) -- HBM GB/s over the live K/V bytes plus Q,
-    out and the block-table entries read.
+    pool, num_splits 8 (the split form: 512 (sequence, KV head) groups x 8
+    key ranges = 4096 items over persistent per-wave workers, then the merge
+    kernel) -- HBM GB/s over the live K/V bytes plus Q, out and the
+    block-table entries read.
 
 Inputs are generated (seeded) and resident in device memory before the timed
 region.  Kernel durations come from HIP events recorded on the stream the
@@ -265,8 +266,8 @@ def run_decode(sdpa, wd, dec, stream):
                            num_splits=wd.num_splits, workspace=dec["workspace"], stream=stream)
 
 
-DECODE_SPLIT_USED = ("fused form: each (sequence, KV head) group is split over the 8 waves of "
-                     "one workgroup and merged in LDS; num_splits does not apply to this form")
+DECODE_SPLIT_USED = ("split form: each (sequence, KV head) group in 8 key ranges, the 4096 items "
+                     "streamed by persistent per-wave workers, the partials combined by the merge kernel")
 
 
 def clock_warm(torch, step, seconds):
@@ -446,7 +447,8 @@ def bench(args):
                 "work_per_launch": flops, "ms_per_launch": t_pre * 1e3}
     roof_dec = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": traffic.get("decode_bytes"),
-                "kernel": "decode_stream_kernel<bf16, D=128, fused> (one launch: 512 groups >= 256 CUs)",
+                "kernel": "decode_stream_kernel<bf16, D=128, split form> + decode_merge_kernel "
+                          "(4096 items: 512 groups x 8 splits)",
                 "work_per_launch": nbytes, "ms_per_launch": t_dec * 1e3}
     dominant = roof_pre if t_pre >= t_dec else roof_dec
     result = {

@@ -160,12 +160,14 @@ typedef struct attn_paged_params {
                                   workspace is then not touched)                 */
   int32_t num_splits;          /* key-dimension splits per sequence, 1..256,
                                   or 0: chosen by the library from the shape
-                                  (about 1024 work items, at least 256
+                                  (about 1024 work items of (sequence, KV
+                                  head, 16-query-head chunk, split), 4096
+                                  from 256 groups up, with at least 256
                                   tokens of block-table capacity per split).
-                                  A tuning value: batches of at least one
-                                  (sequence, KV head, 16-query-head chunk)
-                                  group per compute unit split each group
-                                  over the waves of one workgroup instead    */
+                                  A tuning value: with at least one group
+                                  per compute unit but fewer than 4 items
+                                  per compute unit, each group is split over
+                                  the waves of one workgroup instead         */
   float softmax_scale;         /* finite, >= 0                                   */
   float softcap;               /* 0: off; > 0: softcap * tanh(s / softcap)       */
 } attn_paged_params_t;

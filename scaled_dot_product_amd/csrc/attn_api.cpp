@@ -161,18 +161,24 @@ attn_status_t check_fwd(const void* q, const void* k, const void* v, const float
 // The split count of a paged decode: the caller's, or with num_splits = 0
 // one chosen from the shape.  The split form runs persistent workers over
 // (sequence, KV head, head chunk, split) items, two 4-wave workgroups per
-// compute unit; it streams at close to the HBM ceiling once there are about
-// 1024 items (measured at B = 4 x 32768 tokens: 2.2 TB/s with 8 splits, 5.4
-// with 32, 5.2 with 64; B = 16 x 8192: 8 splits best), so the automatic
-// count asks for that many, keeps each split of the longest sequence the
-// block table can hold at 256 tokens or more, and stays within 1..256.
+// compute unit.  With fewer (sequence, KV head, head chunk) groups than
+// compute units it streams at close to the HBM ceiling from about 1024 items
+// (measured at B = 4 x 32768 tokens: 2.2 TB/s with 8 splits, 5.4 with 32, 5.2
+// with 64; B = 16 x 8192: 8 splits best); with more groups, about 4096 items
+// balance the workers better (B = 32 x 512..8192 tokens: 5.5 TB/s with 16
+// splits; B = 256 x 512..4096: 6.4 TB/s with 2).  The automatic count asks
+// for that many, keeps each split of the longest sequence the block table
+// can hold at 256 tokens or more, and stays within 1..256.
 constexpr int64_t kAutoSplitItems = 1024;
+constexpr int64_t kAutoSplitItemsWide = 4096;
+constexpr int64_t kAutoSplitWideGroups = 256;
 constexpr int64_t kAutoSplitMinTokens = 256;
 int64_t paged_splits(const attn_paged_params_t* p) {
   if (p->num_splits != 0) return p->num_splits;
   const int64_t hchunks = (p->Hq / p->Hkv + 15) / 16;
   const int64_t groups = p->B * p->Hkv * hchunks;
-  int64_t s = groups > 0 ? (kAutoSplitItems + groups - 1) / groups : 1;
+  const int64_t target = groups >= kAutoSplitWideGroups ? kAutoSplitItemsWide : kAutoSplitItems;
+  int64_t s = groups > 0 ? (target + groups - 1) / groups : 1;
   const int64_t by_len = p->max_blocks_per_seq * p->block_size / kAutoSplitMinTokens;
   if (s > by_len) s = by_len;
   return s < 1 ? 1 : (s > 256 ? 256 : s);

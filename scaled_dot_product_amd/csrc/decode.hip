@@ -433,8 +433,12 @@ __device__ __forceinline__ void lds_tr4(u32x2 (&v)[4], const uint32_t (&a)[4]) {
 // slots and the workgroup writes the output itself (the same re-basing to a
 // common max as the merge kernel), so there is neither a workspace round trip
 // nor a second launch.
-constexpr int kOrdMax = 256;         // split form: batches up to this size are ordered longest-first
-constexpr int kOrdMaxFused = 4096;   // fused form: the same up to this size (12-bit sequence index)
+// Batches are ordered longest-first: up to kOrdMax sequences by counting, above
+// that by a sort, up to kOrdMaxSplit (split form) or kOrdMaxFused (fused form:
+// one workgroup per compute unit, so more LDS) sequences.
+constexpr int kOrdMax = 256;
+constexpr int kOrdMaxSplit = 2048;
+constexpr int kOrdMaxFused = 4096;   // (a 12-bit sequence index in the sort key)
 constexpr int kStreamWaves = 4;
 template <bool FUSED, int D>
 constexpr int stream_waves() { return FUSED ? (D <= 128 ? 8 : 4) : kStreamWaves; }
@@ -453,7 +457,7 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
   constexpr int SLOT = kTB * NCH;
   static_assert(NS == 3 && kPageWindow % NS == 0 && DB % 4 == 0, "ring and read batches");
   __shared__ u32x4 vring0[NW][SLOT], vring1[NW][SLOT], vring2[NW][SLOT];
-  constexpr int ORD = FUSED ? kOrdMaxFused : kOrdMax;
+  constexpr int ORD = FUSED ? kOrdMaxFused : kOrdMaxSplit;
   __shared__ int ord[ORD], lens_lds[ORD];
   __shared__ float2 ml_x[FUSED ? NW : 1][16];  // fused: per wave and head, (max, sum)
 
@@ -467,7 +471,7 @@ __global__ __launch_bounds__((64 * stream_waves<FUSED, D>())) void decode_stream
   // ones (B^2 / threads steps); above that a bitonic sort of packed keys in
   // ord (log2(n) (log2(n) + 1) / 2 passes over n = B rounded up to a power of
   // two).  Either way every workgroup derives the same order.
-  const bool big = FUSED && a.B > kOrdMax;
+  const bool big = a.B > kOrdMax;
   int npow = 1;
   while (big && npow < a.B) npow <<= 1;
   unsigned* key = reinterpret_cast<unsigned*>(ord);
@@ -849,14 +853,26 @@ hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t st
   const dim3 grid(p.splits, p.Hkv * a.hchunks, p.B);
   const long long groups = (long long)p.B * p.Hkv * a.hchunks;
   const int cus = device_cus();
-  if (p.block_size % kTB == 0 && p.B <= kOrdMaxFused && groups >= cus) {
+  const long long items = groups * p.splits;
+  const long long cap = (long long)p.max_blocks * p.block_size;
+  const bool uniform = p.block_size % kTB == 0;
+  // The split form's independent per-wave workers stream best once there
+  // are at least 4 items per compute unit; with fewer, a group is better
+  // spread over the waves of a workgroup (the fused form).  Above the split
+  // form's ordering limit the fused form serves long contexts; short ones
+  // (capacity of at most 1024 tokens) go to the partial kernel, whose many
+  // small workgroups hide the latency of items this short.
+  const bool split_form = uniform && p.B <= kOrdMaxSplit && !(groups >= cus && items < 4LL * cus);
+  const bool fused_form = uniform && !split_form && groups >= cus && p.B <= kOrdMaxFused &&
+                          (p.B <= kOrdMaxSplit || cap > 1024);
+  if (fused_form) {
     // fused persistent form: one workgroup per compute unit (it fills the
     // unit's registers), the output written directly
     constexpr int FW = stream_waves<true, D>();
     hipLaunchKernelGGL((decode_stream_kernel<T, D, true>), dim3((unsigned)cus), dim3(64 * FW), 0, stream, a);
     return hipGetLastError();
   }
-  if (p.block_size % kTB == 0 && p.B <= kOrdMax) {
+  if (split_form) {
     // persistent: as many 4-wave workgroups as are resident at once (two per
     // compute unit, one at head dim 256), never more than there are items
     const long long items = groups * p.splits;
@@ -864,7 +880,7 @@ hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t st
     const long long wgs = std::min<long long>((items + kStreamWaves - 1) / kStreamWaves, per_cu * cus);
     hipLaunchKernelGGL((decode_stream_kernel<T, D, false>), dim3((unsigned)wgs), dim3(64 * kStreamWaves), 0,
                        stream, a);
-  } else if (p.block_size % kTB == 0)
+  } else if (uniform)
     hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, true, NW>), grid, dim3(64 * NW), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_partial_kernel<T, D, 2, false, NW>), grid, dim3(64 * NW), 0, stream, a);

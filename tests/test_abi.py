@@ -198,9 +198,10 @@ def test_workspace_size():
 
 
 def test_automatic_split_count():
-    """num_splits = 0: about 1024 (sequence, KV head, head chunk, split) items,
-    at least 256 tokens of block-table capacity per split, within 1..256; the
-    workspace is that of the explicit count it picks."""
+    """num_splits = 0: about 1024 (sequence, KV head, head chunk, split) items
+    (4096 from 256 groups up), at least 256 tokens of block-table capacity
+    per split, within 1..256; the workspace is that of the explicit count it
+    picks."""
     ws = sdpa.attn_paged_decode_workspace_size
     # 4 sequences x 8 KV heads = 32 groups -> 32 splits (capacity 512 x 64 tokens)
     assert ws(paged(num_splits=0, max_blocks_per_seq=512)) == ws(paged(num_splits=32, max_blocks_per_seq=512))
@@ -209,8 +210,14 @@ def test_automatic_split_count():
         ws(paged(B=1, num_splits=128, max_blocks_per_seq=2048))
     # short capacity: 10 x 64 tokens -> 2 splits of at least 256 tokens
     assert ws(paged(num_splits=0)) == ws(paged(num_splits=2))
-    # many groups: one split
-    assert ws(paged(B=256, num_splits=0, num_blocks=5000)) == ws(paged(B=256, num_splits=1, num_blocks=5000))
+    # 256 groups and more: about 4096 items; 32 x 8 = 256 groups -> 16 splits
+    assert ws(paged(B=32, num_splits=0, max_blocks_per_seq=512)) == \
+        ws(paged(B=32, num_splits=16, max_blocks_per_seq=512))
+    # 2048 groups -> 2 splits (capacity 10 x 64 tokens allows 2)
+    assert ws(paged(B=256, num_splits=0, num_blocks=5000)) == ws(paged(B=256, num_splits=2, num_blocks=5000))
+    # 8192 groups -> one split
+    assert ws(paged(B=1024, num_splits=0, num_blocks=20000)) == \
+        ws(paged(B=1024, num_splits=1, num_blocks=20000))
     # capacity below 256 tokens: one split
     assert ws(paged(num_splits=0, max_blocks_per_seq=3)) == ws(paged(num_splits=1, max_blocks_per_seq=3))
 

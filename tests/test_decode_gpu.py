@@ -74,6 +74,8 @@ AUTO_SPLIT_CASES = [
     ("f16", 3, 8, 2, 64, 32, [3000, 0, 700]),
     ("bf16", 1, 16, 4, 256, 64, [5000]),
     ("bf16", 2, 4, 4, 128, 16, [100, 255]),          # short capacity: few splits
+    # 40 x 8 = 320 groups: about 4096 items (13 splits), the split form
+    ("bf16", 40, 32, 8, 128, 64, [int(x) for x in np.random.default_rng(3).integers(300, 2000, 40)]),
 ]
 
 
@@ -103,16 +105,21 @@ def wide_lens(B, hi, seed):
     return rng.permutation(lens).astype(np.int32).tolist()
 
 
-# Batches of at least 256 (sequence, KV head, 16-head chunk) groups: one per
-# compute unit of a 256-CU chip or more, so that every group is a whole
-# workgroup's item and the workgroup merges its chunks itself.
+# Batches of at least 256 (sequence, KV head, 16-head chunk) groups, one per
+# compute unit of a 256-CU chip or more.  With fewer than 1024 (group, split)
+# items (4 per compute unit) every group is a whole workgroup's item and the
+# workgroup merges its chunks itself (the fused form); with more, per-wave
+# workers stream the items and the merge kernel combines them (the split form).
 WIDE_CASES = [
     # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
-    ("bf16", 64, 8, 4, 128, 16, 700, 8, None, False),
-    ("f16", 128, 4, 2, 64, 32, 300, 4, 15.0, True),
-    ("bf16", 64, 40, 2, 128, 64, 400, 8, None, True),     # 20 heads per KV head: 2 chunks
-    ("bf16", 64, 16, 4, 256, 16, 500, 8, None, False),
-    ("f16", 256, 2, 1, 128, 48, 200, 2, 30.0, False),
+    ("bf16", 64, 8, 4, 128, 16, 700, 2, None, False),      # fused: 256 groups x 2 splits
+    ("f16", 128, 4, 2, 64, 32, 300, 3, 15.0, True),        # fused
+    ("bf16", 64, 40, 2, 128, 64, 400, 1, None, True),      # fused; 20 heads per KV head: 2 chunks
+    ("bf16", 64, 16, 4, 256, 16, 500, 2, None, False),     # fused
+    ("f16", 256, 2, 1, 128, 48, 200, 2, 30.0, False),      # fused
+    ("bf16", 64, 8, 4, 128, 16, 700, 8, None, False),      # split form: 2048 items
+    ("f16", 128, 4, 2, 64, 32, 300, 4, 15.0, True),        # split form
+    ("bf16", 64, 16, 4, 256, 16, 500, 8, None, True),      # split form at head dim 256
 ]
 
 
@@ -135,20 +142,23 @@ def test_paged_parity_wide_batch(gpu_lib, case):
             assert torch.count_nonzero(out[b]).item() == 0
 
 
-# Batches above 256 sequences with block sizes that are multiples of 16: still
-# the fused form, with the lengths ordered by a bitonic sort in LDS (up to 4096
-# sequences).
+# Batches above 256 sequences with block sizes that are multiples of 16: the
+# lengths ordered by a bitonic sort in LDS; the split form up to 2048
+# sequences, the fused form below 4 items per compute unit and, up to 4096
+# sequences, for block tables of more than 1024 tokens.
 LARGE_BATCH_CASES = [
     # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
-    ("bf16", 300, 8, 4, 128, 16, 300, 3, None, False),
-    ("bf16", 512, 8, 8, 128, 64, 260, 8, None, False),
-    ("f16", 300, 4, 2, 64, 64, 400, 1, 20.0, True),
-    ("bf16", 320, 16, 4, 256, 16, 150, 8, 30.0, True),
-    ("f16", 512, 8, 2, 128, 16, 250, 8, None, True),
-    ("bf16", 400, 32, 8, 128, 32, 200, 5, None, False),
-    ("bf16", 2100, 2, 1, 128, 16, 40, 2, None, False),
-    ("f16", 1100, 4, 2, 64, 32, 70, 3, 25.0, True),
-    ("bf16", 4096, 2, 1, 128, 16, 24, 1, None, False),     # the largest batch the fused form orders
+    ("bf16", 300, 8, 4, 128, 16, 300, 3, None, False),     # split form
+    ("bf16", 512, 8, 8, 128, 64, 260, 8, None, False),     # split form
+    ("f16", 300, 4, 2, 64, 64, 400, 1, 20.0, True),        # fused: 600 items
+    ("bf16", 320, 16, 4, 256, 16, 150, 8, 30.0, True),     # split form, head dim 256
+    ("f16", 512, 8, 2, 128, 16, 250, 8, None, True),       # split form
+    ("bf16", 400, 32, 8, 128, 32, 200, 5, None, False),    # split form
+    ("f16", 1100, 4, 2, 64, 32, 70, 3, 25.0, True),        # split form
+    ("bf16", 2048, 2, 1, 128, 16, 40, 2, None, False),     # split form, its largest batch
+    ("bf16", 700, 4, 1, 128, 32, 300, 1, None, True),      # fused: 700 items
+    ("bf16", 2500, 2, 1, 128, 16, 1100, 1, None, False),   # fused: capacity 1120 tokens
+    ("f16", 4096, 2, 1, 64, 32, 1100, 2, 15.0, False),     # fused, its largest batch
 ]
 
 
@@ -157,15 +167,18 @@ def test_paged_parity_large_batch(gpu_lib, case):
     run_batch_case(gpu_lib, LARGE_BATCH_CASES[case], 400 + case, f"paged decode large-batch case {case}")
 
 
-# Above 4096 sequences: the partial kernel over uniform 16-token blocks (one
-# 2-wave workgroup per split and group) plus the merge kernel.  The workgroups
-# rank the lengths in LDS up to 2048 sequences at head dim 128 (1024 at 64) and
-# take them in index order beyond that, so these batches use index order.
+# Above 2048 sequences with block tables of at most 1024 tokens, and above
+# 4096 sequences: the partial kernel over uniform 16-token blocks (one 2-wave
+# workgroup per split and group) plus the merge kernel.  The workgroups rank
+# the lengths in LDS up to 2048 sequences at head dim 128 (1024 at 64) and
+# take them in index order beyond that.
 PARTIAL_CASES = [
     # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
     ("bf16", 4097, 2, 1, 128, 16, 20, 2, None, False),
     ("f16", 4500, 4, 2, 64, 32, 24, 3, 25.0, True),
     ("bf16", 4200, 8, 2, 256, 16, 17, 1, None, True),
+    ("bf16", 2100, 2, 1, 128, 16, 40, 2, None, False),
+    ("f16", 3000, 4, 1, 128, 64, 200, 1, None, True),
 ]
 
 
@@ -194,20 +207,21 @@ def test_paged_parity_partial_kernel(gpu_lib, case):
     run_batch_case(gpu_lib, PARTIAL_CASES[case], 450 + case, f"paged decode partial-kernel case {case}")
 
 
-@pytest.mark.parametrize("B", [300, 4200])
-def test_large_batch_error_flag_and_determinism(gpu_lib, B):
-    """16-token blocks at B = 300 (the fused form over sorted lengths) and
-    B = 4200 (the partial kernel): a block id outside the pool masks its keys
-    and sets the flag, a length beyond the table's capacity is clamped and
-    sets it, the other sequences are unaffected, and reruns are bitwise equal."""
+@pytest.mark.parametrize("B,splits", [(300, 4), (300, 1), (4200, 4)])
+def test_large_batch_error_flag_and_determinism(gpu_lib, B, splits):
+    """16-token blocks at B = 300 (over sorted lengths: the split form with 4
+    splits, the fused form with 1) and B = 4200 (the partial kernel): a block
+    id outside the pool masks its keys and sets the flag, a length beyond the
+    table's capacity is clamped and sets it, the other sequences are
+    unaffected, and reruns are bitwise equal."""
     Hq, Hkv, D, bs, maxb = 8, 2, 128, 16, 20
     w = W.Paged("ep", "bf16", B, Hq, Hkv, D, bs, 0, 0, 4, maxb, seed=91)
     lens = wide_lens(B, 300, 92)
     q, kp, vp, table, sl, _ = W.paged_inputs(w, seq_lens=lens)
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     announce(f"B={B}: valid call, rerun")
-    a = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
-    b = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=4)
+    a = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=splits)
+    b = gpu_decode(gpu_lib, q, kp, vp, table, sl, error_flag=flag, num_splits=splits)
     assert flag.item() == 0
     assert torch.equal(a, b)
     ref = oracle_decode(q, kp, vp, table, sl, scale=D ** -0.5)
@@ -216,7 +230,7 @@ def test_large_batch_error_flag_and_determinism(gpu_lib, B):
     bad = table.clone()
     bad[victim, 1] = 10 ** 6                                # keys 16..31 of that sequence are masked
     announce(f"B={B}: block id out of range")
-    out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag, num_splits=4)
+    out = gpu_decode(gpu_lib, q, kp, vp, bad, sl, error_flag=flag, num_splits=splits)
     assert flag.item() == 1
     assert torch.isfinite(out.float()).all()
     others = [i for i in range(B) if i != victim]
@@ -232,7 +246,7 @@ def test_large_batch_error_flag_and_determinism(gpu_lib, B):
     long = sl.clone()
     long[3] = maxb * bs + 5
     announce(f"B={B}: seq_len beyond capacity")
-    gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag, num_splits=4)
+    gpu_decode(gpu_lib, q, kp, vp, table, long, error_flag=flag, num_splits=splits)
     assert flag.item() == 1
 
 
@@ -248,7 +262,8 @@ def test_paged_decode_workload(gpu_lib):
 
 @pytest.mark.parametrize("bs,splits,B,Hkv", [(64, 8, 4, 2), (16, 3, 4, 2), (5, 1, 4, 2),
                                              (16, 8, 64, 4), (32, 2, 128, 2),
-                                             (16, 3, 300, 2), (64, 8, 300, 1), (16, 3, 4200, 1)])
+                                             (16, 3, 300, 2), (64, 8, 300, 1), (16, 1, 300, 2),
+                                             (16, 3, 4200, 1)])
 def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
     """One-hot scores: q = 1024 e0 in every head and a single key row equal to
     8 e0 give that key a score of 1024 * 8 / sqrt(128) ~ 724 and every other
@@ -256,10 +271,11 @@ def test_paging_is_bit_exact(gpu_lib, bs, splits, B, Hkv):
     the V row of that logical token.  V rows hold (sequence % 128, position
     % 128, position // 128, kv head, sequence // 128) as bf16-exact integers;
     slots no table entry points at hold a finite sentinel so that a stray
-    read is visible.  The
-    cases with B = 64, 128 and 300 have at least 256 (sequence, KV head)
-    groups (the fused form); B = 4200 runs the partial kernel over 16-token
-    blocks."""
+    read is visible.  B = 4 runs the split form (and the partial kernel at
+    block size 5); B = 128 with 2 splits and B = 300 with 1 the fused form
+    (at least 256 groups, fewer than 1024 items); B = 64 with 8 splits and
+    B = 300 with 3 or 8 the split form; B = 4200 the partial kernel over
+    16-token blocks."""
     Hq, D = 8, 128
     lens = [130, 64, 7, 200] if B == 4 else np.random.default_rng(6).integers(1, 260, size=B).tolist()
     rng = np.random.default_rng(5)

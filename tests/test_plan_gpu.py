@@ -52,15 +52,15 @@ def test_paged_decode_plan_matches_entry_point_and_oracle(gpu_lib):
 
 
 def test_paged_decode_plan_fused_form(gpu_lib):
-    # enough (sequence, KV head) groups for the fused form
+    # 512 (sequence, KV head) groups, one split each: the fused form
     lens = list(np.random.default_rng(5).integers(64, 600, size=64))
     w, q, kp, vp, table, sl = _decode_inputs(32, lens, B=64, Hq=32, Hkv=8, bs=64, max_blocks=10)
     args = [t.to(DEV) for t in (q, kp, vp, table, sl)]
     announce("PagedDecodePlan fused form")
-    plan = gpu_lib.PagedDecodePlan(*args)
+    plan = gpu_lib.PagedDecodePlan(*args, num_splits=1)
     for _ in range(3):
         got = plan.run()
-    ref = gpu_lib.attn_paged_decode(*args)
+    ref = gpu_lib.attn_paged_decode(*args, num_splits=1)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
 

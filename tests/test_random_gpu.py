@@ -73,7 +73,7 @@ def test_random_paged_decode(gpu_lib, seed):
     D = int(rng.choice([64, 128, 256]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
     Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
-    # batch and longest context together (B = 300: the fused form over a bitonic sort of the lengths)
+    # batch and longest context together (B = 300: lengths ordered by a bitonic sort)
     B, hi = [(1, 1500), (3, 1500), (17, 300), (70, 300), (300, 40)][rng.integers(5)]
     bs = int(rng.choice([1, 5, 16, 32, 64, 128]))
     lens = rng.integers(0, hi + 1, size=B).astype(np.int32)
