@@ -159,6 +159,8 @@ LARGE_BATCH_CASES = [
     ("bf16", 700, 4, 1, 128, 32, 300, 1, None, True),      # fused: 700 items
     ("bf16", 2500, 2, 1, 128, 16, 1100, 1, None, False),   # fused: capacity 1120 tokens
     ("f16", 4096, 2, 1, 64, 32, 1100, 2, 15.0, False),     # fused, its largest batch
+    ("bf16", 2049, 8, 2, 128, 64, 1100, 4, None, True),    # fused: one past the split form's limit
+    ("bf16", 2300, 4, 1, 256, 16, 1050, 1, 30.0, False),   # fused at head dim 256
 ]
 
 
