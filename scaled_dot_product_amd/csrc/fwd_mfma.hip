@@ -539,12 +539,14 @@ void fwd_mfma_kernel(FwdArgs a) {
   // one wave's vector phase meets the other's matrix phase between two
   // barriers.  The operations on O keep their order, so the result is the
   // same bit for bit.  Its copies run one tile later: K(i+1) and V(i) in step i.
-  // (head dim 64 only: at 128 the rotated loop does not fit the registers)
-  const bool rot = SPLIT && D == 64 && grp == 1;
+  // (head dim 64 only: at 128 the rotated loop does not fit the registers;
+  // and not over the paged pool, where the longer loop's scalar spills cost
+  // more than the overlap gains: 61.3 vs 59.8 us on the chunked workload)
+  const bool rot = SPLIT && !PAGED && D == 64 && grp == 1;
   // steps every wave of the workgroup runs (barriers must match): group 0 of a
   // split workgroup has at least as many tiles as group 1, which needs one
   // step more than it has tiles
-  const int n_steps = !SPLIT ? n : D != 64 ? half
+  const int n_steps = !SPLIT ? n : (D != 64 || PAGED) ? half
                       : (t_last > t_first ? max(half, t_last - t_first - half + 1) : 0);
   u32x4* const kb0 = kbuf0 + grp * TC;
   u32x4* const kb1 = kbuf1 + grp * TC;
