@@ -539,14 +539,15 @@ void fwd_mfma_kernel(FwdArgs a) {
   // one wave's vector phase meets the other's matrix phase between two
   // barriers.  The operations on O keep their order, so the result is the
   // same bit for bit.  Its copies run one tile later: K(i+1) and V(i) in step i.
-  // (head dim 64 only: at 128 the rotated loop does not fit the registers;
-  // and not over the paged pool, where the longer loop's scalar spills cost
-  // more than the overlap gains: 61.3 vs 59.8 us on the chunked workload)
-  const bool rot = SPLIT && !PAGED && D == 64 && grp == 1;
+  // (not over the paged pool, where the longer loop's scalar spills cost more
+  // than the overlap gains: 61.3 vs 59.8 us on the chunked workload; the
+  // rotated step reads its K fragments as it goes, without the prefetch of
+  // the other order, which does not fit the registers at head dim 128)
+  const bool rot = SPLIT && !PAGED && D <= 128 && grp == 1;
   // steps every wave of the workgroup runs (barriers must match): group 0 of a
   // split workgroup has at least as many tiles as group 1, which needs one
   // step more than it has tiles
-  const int n_steps = !SPLIT ? n : (D != 64 || PAGED) ? half
+  const int n_steps = !SPLIT ? n : (D > 128 || PAGED) ? half
                       : (t_last > t_first ? max(half, t_last - t_first - half + 1) : 0);
   u32x4* const kb0 = kbuf0 + grp * TC;
   u32x4* const kb1 = kbuf1 + grp * TC;
@@ -649,13 +650,10 @@ void fwd_mfma_kernel(FwdArgs a) {
       if (i + 1 < n) dma_k(kload, tile_rsrc(K, t + 1, kc, ok_load));
       if (i < n) dma_v(vload, tile_rsrc(V, t, vc, ok_unused));
     }
-    u32x4 kf[kKPF];
-#pragma unroll
-    for (int p = 0; p < kKPF; ++p) kf[p] = kfrag<T, D>(kcur, p, ln, g);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     if (i >= 1 && live(t - 1)) pv_tile<T, D>(pp, reinterpret_cast<const T*>(vprev), st, lane, g);
-    if (i < n && live(t)) qk_tile_pf<T, D>(kcur, qf, ln, g, kf, sc);
+    if (i < n && live(t)) qk_tile<T, D>(kcur, qf, ln, g, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     if (i < n && live(t))
