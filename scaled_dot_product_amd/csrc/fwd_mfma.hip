@@ -543,11 +543,16 @@ void fwd_mfma_kernel(FwdArgs a) {
   // than the overlap gains: 61.3 vs 59.8 us on the chunked workload; the
   // rotated step reads its K fragments as it goes, without the prefetch of
   // the other order, which does not fit the registers at head dim 128)
-  const bool rot = SPLIT && !PAGED && D <= 128 && grp == 1;
+  // Without the key split, every other workgroup runs rotated at head dim 64,
+  // so that the two workgroups sharing a compute unit less often meet in the
+  // same phase (B = 8 x 16 heads x 512 queries over 4096 keys, f16: 83.0 ->
+  // 81.0 us; at head dim 128 the two loops together spill registers and the
+  // 2048-token workload went from 73.8 to 81.1 us).
+  const bool rot = !PAGED && (SPLIT ? D <= 128 && grp == 1 : D == 64 && (blockIdx.x & 1) != 0);
   // steps every wave of the workgroup runs (barriers must match): group 0 of a
   // split workgroup has at least as many tiles as group 1, which needs one
   // step more than it has tiles
-  const int n_steps = !SPLIT ? n : (D > 128 || PAGED) ? half
+  const int n_steps = !SPLIT ? (rot && n > 0 ? n + 1 : n) : (D > 128 || PAGED) ? half
                       : (t_last > t_first ? max(half, t_last - t_first - half + 1) : 0);
   u32x4* const kb0 = kbuf0 + grp * TC;
   u32x4* const kb1 = kbuf1 + grp * TC;
