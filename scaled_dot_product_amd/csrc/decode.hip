@@ -426,13 +426,14 @@ __device__ __forceinline__ void lds_tr4(u32x2 (&v)[4], const uint32_t (&a)[4]) {
 // waits are exact; only the V transpose reads are inline asm, after an
 // explicit wait for that block's copies.
 //
-// Fused form (FUSED, when there are at least as many (sequence, KV head, head
-// chunk) groups as compute units): the worker is the whole workgroup and the
-// item is a group; wave w streams the w-th of NW equal token chunks of the
-// group, and at the group's end the NW partial states meet in the waves' ring
-// slots and the workgroup writes the output itself (the same re-basing to a
-// common max as the merge kernel), so there is neither a workspace round trip
-// nor a second launch.
+// Fused form (FUSED; the launcher picks it when there are at least as many
+// (sequence, KV head, head chunk) groups as compute units but few items per
+// compute unit, or for long contexts above the split form's batch limit): the
+// worker is the whole workgroup and the item is a group; wave w streams the
+// w-th of NW equal token chunks of the group, and at the group's end the NW
+// partial states meet in the waves' ring slots and the workgroup writes the
+// output itself (the same re-basing to a common max as the merge kernel), so
+// there is neither a workspace round trip nor a second launch.
 // Batches are ordered longest-first: up to kOrdMax sequences by counting, above
 // that by a sort, up to kOrdMaxSplit (split form) or kOrdMaxFused (fused form:
 // one workgroup per compute unit, so more LDS) sequences.
@@ -875,7 +876,6 @@ hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t st
   if (split_form) {
     // persistent: as many 4-wave workgroups as are resident at once (two per
     // compute unit, one at head dim 256), never more than there are items
-    const long long items = groups * p.splits;
     const long long per_cu = D <= 128 ? 2 : 1;  // head dim 256: one wave per SIMD
     const long long wgs = std::min<long long>((items + kStreamWaves - 1) / kStreamWaves, per_cu * cus);
     hipLaunchKernelGGL((decode_stream_kernel<T, D, false>), dim3((unsigned)wgs), dim3(64 * kStreamWaves), 0,
