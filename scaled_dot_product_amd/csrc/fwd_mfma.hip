@@ -158,17 +158,17 @@ __device__ __forceinline__ u32x4 kfrag(const u32x4* Ks, int f, int ln, int g) {
 // before the softmax of the previous tile, so that their LDS latency hides
 // behind it (8 is 32 VGPRs; it fits the two-waves-per-SIMD budget at D = 128)
 constexpr int kKPF = ATTN_KPF;
-template <typename T, int D>
+template <typename T, int D, int KPF>
 __device__ __forceinline__ void qk_tile_pf(const u32x4* Ks, const u32x4* qf, int ln, int g,
-                                           u32x4 (&kf)[kKPF], floatx16 (&sc)[2]) {
+                                           u32x4 (&kf)[KPF], floatx16 (&sc)[2]) {
   using E = Elem<T>;
   constexpr int NF = 2 * (D / 16);
   sc[0] = floatx16{};
   sc[1] = floatx16{};
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const u32x4 a = kf[f % kKPF];
-    if (f + kKPF < NF) kf[f % kKPF] = kfrag<T, D>(Ks, f + kKPF, ln, g);
+    const u32x4 a = kf[f % KPF];
+    if (f + KPF < NF) kf[f % KPF] = kfrag<T, D>(Ks, f + KPF, ln, g);
     sc[f & 1] = E::mma32(a, qf[f >> 1], sc[f & 1]);
   }
 }
@@ -363,6 +363,10 @@ void fwd_mfma_kernel(FwdArgs a) {
   constexpr int CPT = TC / kThreads;     // chunks per thread per tile and tensor
   constexpr int KS = D / 16;             // contraction steps of K Q^T
   constexpr int DB = D / 32;             // 32-row blocks of O^T
+  // K fragments read ahead in the plain step order (4 where the rotated order
+  // also runs at head dim 128, so that both loops fit the registers)
+  constexpr int KPF =
+      ((FLAGS & F_SOFTCAP) != 0 && D == 128 && (FLAGS & (F_PAGED | F_SPLIT)) == 0) ? 4 : kKPF;
   static_assert(CPT * kThreads == TC, "tile must split evenly over the workgroup");
 
   // Four separate LDS objects so that the compiler can tell the buffer being
@@ -548,7 +552,13 @@ void fwd_mfma_kernel(FwdArgs a) {
   // same phase (B = 8 x 16 heads x 512 queries over 4096 keys, f16: 83.0 ->
   // 81.0 us; at head dim 128 the two loops together spill registers and the
   // 2048-token workload went from 73.8 to 81.1 us).
-  const bool rot = !PAGED && (SPLIT ? D <= 128 && grp == 1 : D == 64 && (blockIdx.x & 1) != 0);
+  // With a softcap (vector-bound: three transcendentals per score) the same
+  // holds at head dim 128, given a shorter K prefetch so that both loops fit
+  // (the long masked 8192-token workload: 555 -> 543 us); without one, the
+  // rotated step's K reads without prefetch slow the matrix-bound loop.
+  constexpr bool SOFTCAP = (FLAGS & F_SOFTCAP) != 0;
+  const bool rot = !PAGED && (SPLIT ? D <= 128 && grp == 1
+                                    : (D == 64 || (SOFTCAP && D <= 128)) && (blockIdx.x & 1) != 0);
   // steps every wave of the workgroup runs (barriers must match): group 0 of a
   // split workgroup has at least as many tiles as group 1, which needs one
   // step more than it has tiles
@@ -617,9 +627,9 @@ void fwd_mfma_kernel(FwdArgs a) {
       if (i + 2 < n) dma_k(kload, tile_rsrc(K, t + 2, kc, ok_load));
       if (i + 1 < n) dma_v(vload, tile_rsrc(V, t + 1, vc, ok_unused));
     }
-    u32x4 kf[kKPF];
+    u32x4 kf[KPF];
 #pragma unroll
-    for (int p = 0; p < kKPF; ++p) kf[p] = kfrag<T, D>(kread, p, ln, g);
+    for (int p = 0; p < KPF; ++p) kf[p] = kfrag<T, D>(kread, p, ln, g);
     if (live(t))
       softmax_pv<T, D, FLAGS>(sc, reinterpret_cast<const T*>(vread), st, a,
                               PAGED && !ok_t ? t * kBN : Sk, t * kBN, ip, ipa_w, ipb_w, slope_l2,
@@ -630,7 +640,7 @@ void fwd_mfma_kernel(FwdArgs a) {
     // over the one in its softmax (vector) phase.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
-    if (i + 1 < n && live(t + 1)) qk_tile_pf<T, D>(kread, qf, ln, g, kf, sc);
+    if (i + 1 < n && live(t + 1)) qk_tile_pf<T, D, KPF>(kread, qf, ln, g, kf, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
