@@ -200,11 +200,12 @@ attn_status_t attn_paged_decode_check(const void* q, const void* k_pool, const v
  * the kernels on `stream` and returns.  For block sizes that are multiples of
  * 16: a persistent kernel whose per-wave workers write per-split partials for
  * the merge kernel (B <= 2048, unless there are at least as many (sequence,
- * KV head, 16-query-head chunk) groups as compute units but fewer than 4
- * group-split items per compute unit); or a persistent kernel with one
- * workgroup per compute unit that spreads each group over its waves, merges
- * them in LDS and writes out directly, the workspace untouched (that case, and
- * 2048 < B <= 4096 with max_blocks_per_seq * block_size > 1024).  Otherwise,
+ * KV head, 16-query-head chunk) groups as compute units and either D = 256
+ * or fewer than 4 group-split items per compute unit); or a persistent kernel
+ * with one workgroup per compute unit that spreads each group over its waves,
+ * merges them in LDS and writes out directly, the workspace untouched (that
+ * case, and 2048 < B <= 4096 with max_blocks_per_seq * block_size > 1024).
+ * Otherwise,
  * and for other block sizes, a partial kernel (one workgroup per sequence, KV
  * head and split) and the merge kernel.  The result is the same up to
  * rounding order in every form.

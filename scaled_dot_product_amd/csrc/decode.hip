@@ -859,11 +859,15 @@ hipError_t launch_typed(const DecodeProblem& p, const DecArgs& a, hipStream_t st
   const bool uniform = p.block_size % kTB == 0;
   // The split form's independent per-wave workers stream best once there
   // are at least 4 items per compute unit; with fewer, a group is better
-  // spread over the waves of a workgroup (the fused form).  Above the split
-  // form's ordering limit the fused form serves long contexts; short ones
-  // (capacity of at most 1024 tokens) go to the partial kernel, whose many
-  // small workgroups hide the latency of items this short.
-  const bool split_form = uniform && p.B <= kOrdMaxSplit && !(groups >= cus && items < 4LL * cus);
+  // spread over the waves of a workgroup (the fused form).  At head dim 256
+  // the split form runs one 4-wave workgroup per compute unit and the fused
+  // form is the faster whenever it has a group per compute unit (B = 64 x
+  // 512..8192 tokens: 352 vs 364 us; 128..1024: 60.5 vs 77.4 us).  Above the
+  // split form's ordering limit the fused form serves long contexts; short
+  // ones (capacity of at most 1024 tokens) go to the partial kernel, whose
+  // many small workgroups hide the latency of items this short.
+  const bool split_form =
+      uniform && p.B <= kOrdMaxSplit && (groups < cus || (D <= 128 && items >= 4LL * cus));
   const bool fused_form = uniform && !split_form && groups >= cus && p.B <= kOrdMaxFused &&
                           (p.B <= kOrdMaxSplit || cap > 1024);
   if (fused_form) {

@@ -107,9 +107,10 @@ def wide_lens(B, hi, seed):
 
 # Batches of at least 256 (sequence, KV head, 16-head chunk) groups, one per
 # compute unit of a 256-CU chip or more.  With fewer than 1024 (group, split)
-# items (4 per compute unit) every group is a whole workgroup's item and the
-# workgroup merges its chunks itself (the fused form); with more, per-wave
-# workers stream the items and the merge kernel combines them (the split form).
+# items (4 per compute unit), and always at head dim 256, every group is a
+# whole workgroup's item and the workgroup merges its chunks itself (the fused
+# form); otherwise per-wave workers stream the items and the merge kernel
+# combines them (the split form).
 WIDE_CASES = [
     # dtype, B, Hq, Hkv, D, block_size, max len, splits, softcap, alibi
     ("bf16", 64, 8, 4, 128, 16, 700, 2, None, False),      # fused: 256 groups x 2 splits
@@ -119,7 +120,7 @@ WIDE_CASES = [
     ("f16", 256, 2, 1, 128, 48, 200, 2, 30.0, False),      # fused
     ("bf16", 64, 8, 4, 128, 16, 700, 8, None, False),      # split form: 2048 items
     ("f16", 128, 4, 2, 64, 32, 300, 4, 15.0, True),        # split form
-    ("bf16", 64, 16, 4, 256, 16, 500, 8, None, True),      # split form at head dim 256
+    ("bf16", 64, 16, 4, 256, 16, 500, 8, None, True),      # fused: head dim 256 keeps it with many items
 ]
 
 
@@ -151,7 +152,7 @@ LARGE_BATCH_CASES = [
     ("bf16", 300, 8, 4, 128, 16, 300, 3, None, False),     # split form
     ("bf16", 512, 8, 8, 128, 64, 260, 8, None, False),     # split form
     ("f16", 300, 4, 2, 64, 64, 400, 1, 20.0, True),        # fused: 600 items
-    ("bf16", 320, 16, 4, 256, 16, 150, 8, 30.0, True),     # split form, head dim 256
+    ("bf16", 320, 16, 4, 256, 16, 150, 8, 30.0, True),     # fused at head dim 256 (1280 groups)
     ("f16", 512, 8, 2, 128, 16, 250, 8, None, True),       # split form
     ("bf16", 400, 32, 8, 128, 32, 200, 5, None, False),    # split form
     ("f16", 1100, 4, 2, 64, 32, 70, 3, 25.0, True),        # split form
